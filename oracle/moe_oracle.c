@@ -1,0 +1,527 @@
+/*
+ * moe_oracle.c -- plain, slow, scalar CPU oracle for the MoE token
+ * permute / unpermute path and the fused chunk sort-and-pad / restore pair.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the
+ * entry module and the CPU-baseline leg of the benchmark may load it.  The
+ * product library never links, calls or includes anything from here, and
+ * this file includes nothing from the product sources.
+ *
+ * Every function is the plain definition of its step, written as loops in
+ * the order the pages describe, with no blocking, fusion or reordering:
+ *
+ *   oracle_row_id_map*      -- stable counting sort: per-expert counts, an
+ *                              exclusive scan, then a cursor walk over the
+ *                              (token, expert) pairs in token order.
+ *   oracle_permute          -- bitwise row copies token -> destination rows.
+ *   oracle_unpermute        -- fp32 fused multiply-adds of prob x row, in
+ *                              top-k slot order, starting from +0, rounded
+ *                              once to bf16.
+ *   oracle_unpermute_bwd    -- act-grad scatter (fp32 product, then bf16)
+ *                              and prob-grad row dot products (exact
+ *                              products summed in fp64, rounded once).
+ *   oracle_permute_bwd      -- slot-order fp32 sum of the k gradient rows.
+ *   oracle_chunk_map        -- padded destination -> source row map.
+ *   oracle_sort_chunks_and_pad / oracle_unpad_and_restore_chunks
+ *                           -- the two copies driven by that map.
+ *
+ * bf16 values travel as their 16-bit patterns (uint16_t).  The conversions
+ * below are written from the IEEE 754 definitions: widening is exact, and
+ * narrowing is round-to-nearest, ties-to-even on the 16 discarded bits.
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -shared -fPIC.
+ * -ffp-contract=off keeps every a*b+c that is not an explicit fmaf() as
+ * two roundings.
+ *
+ * Return codes (all functions): 0 ok, otherwise one of the ORC_* values.
+ * Outputs are unspecified after an error.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_BAD_EXPERT 1   /* an expert index outside [0, E)               */
+#define ORC_DUP_EXPERT 2   /* one expert twice in a token's routing        */
+#define ORC_BAD_ARG 3      /* a size or shape argument out of range        */
+#define ORC_BAD_ROW 4      /* a map entry pointing outside its buffer      */
+#define ORC_BAD_CHUNKS 5   /* negative split size / order not a permutation */
+#define ORC_OVERFLOW 6     /* tokens exceed the input capacity, or padded
+                              groups exceed the output capacity            */
+#define ORC_NO_MEM 7
+#define ORC_BAD_ORDER 8    /* pair list not in non-decreasing token order  */
+
+/* ---- bf16 <-> fp32, from the bfloat16 / IEEE 754 binary32 layouts ----- */
+
+static float bf16_to_f32(uint16_t b)
+{
+    /* bf16 is the top half of a binary32: widening appends 16 zero bits. */
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t exponent = (u >> 23) & 0xffu;
+    uint32_t mantissa = u & 0x7fffffu;
+    if (exponent == 0xffu && mantissa != 0u) {
+        /* NaN: keep sign and the upper payload bits, force the quiet bit. */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    }
+    uint32_t kept = u >> 16;          /* sign, exponent, 7 mantissa bits */
+    uint32_t dropped = u & 0xffffu;   /* the 16 bits rounded away        */
+    if (dropped > 0x8000u) {
+        kept += 1u;                   /* above the halfway point: up     */
+    } else if (dropped == 0x8000u) {
+        if (kept & 1u) kept += 1u;    /* exactly halfway: to even        */
+    }
+    /* A carry out of the mantissa increments the exponent, which is the
+       correct next representable value (up to +-Inf on overflow). */
+    return (uint16_t)kept;
+}
+
+uint16_t oracle_f32_to_bf16(float f) { return f32_to_bf16_rne(f); }
+float oracle_bf16_to_f32(uint16_t b) { return bf16_to_f32(b); }
+float oracle_fmaf(float a, float b, float c) { return fmaf(a, b, c); }
+
+/* ---- (1) row map: stable counting sort --------------------------------- */
+
+/*
+ * Core of the row map, over an explicit list of routed (token, expert)
+ * pairs given in non-decreasing token order.
+ *
+ * d9d 0.1.0, permute_with_probs.py, make_row_id_map: the worked example in
+ * its comments shows that after the second pass the destination rows run
+ * expert-major (all rows of expert 0 first) and, inside one expert, in
+ * ascending token order.  moe-ops README, "Why this library": the permute
+ * is a counting sort (histogram + exclusive prefix sum).  That is exactly:
+ *   count[e]   = number of pairs with expert e
+ *   offset[e]  = count[0] + ... + count[e-1]         (exclusive scan)
+ *   walking the pairs in token order, the next pair of expert e takes
+ *   row offset[e] + (pairs of e already placed).
+ * Output: row_id_map[e * T + t] = row, or -1 when t is not routed to e;
+ *         expert_offsets[0..E] = the exclusive scan, expert_offsets[E] =
+ *         number of pairs.
+ */
+int oracle_row_id_map_pairs(const int32_t *pair_token, const int32_t *pair_expert,
+                            int64_t npairs, int T, int E,
+                            int32_t *row_id_map, int32_t *expert_offsets)
+{
+    if (T < 0 || E < 1 || npairs < 0) return ORC_BAD_ARG;
+    for (int64_t i = 0; i < npairs; i++) {
+        if (pair_token[i] < 0 || pair_token[i] >= T) return ORC_BAD_ARG;
+        if (pair_expert[i] < 0 || pair_expert[i] >= E) return ORC_BAD_EXPERT;
+        if (i > 0 && pair_token[i] < pair_token[i - 1]) return ORC_BAD_ORDER;
+    }
+    int64_t *count = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    int64_t *cursor = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    if (!count || !cursor) { free(count); free(cursor); return ORC_NO_MEM; }
+
+    for (int64_t i = 0; i < npairs; i++) count[pair_expert[i]] += 1;
+
+    int64_t running = 0;
+    for (int e = 0; e < E; e++) {
+        expert_offsets[e] = (int32_t)running;
+        cursor[e] = running;
+        running += count[e];
+    }
+    expert_offsets[E] = (int32_t)running;
+
+    for (int64_t i = 0; i < (int64_t)E * T; i++) row_id_map[i] = -1;
+
+    int status = ORC_OK;
+    for (int64_t i = 0; i < npairs; i++) {
+        int t = pair_token[i];
+        int e = pair_expert[i];
+        int64_t slot = (int64_t)e * T + t;
+        if (row_id_map[slot] != -1) { status = ORC_DUP_EXPERT; break; }
+        row_id_map[slot] = (int32_t)cursor[e];
+        cursor[e] += 1;
+    }
+    free(count);
+    free(cursor);
+    return status;
+}
+
+/*
+ * Row map from top-k routing: topk_idx[t * k + j] is token t's j-th expert.
+ * The pairs are (t, topk_idx[t][j]) for t ascending, then j ascending; with
+ * the experts of one token distinct this is the same map as a stable argsort
+ * of the flattened top-k index array (xtuner issue "permute different with
+ * torch version", maintainer's reply).
+ */
+int oracle_row_id_map(const int32_t *topk_idx, int T, int k, int E,
+                      int32_t *row_id_map, int32_t *expert_offsets)
+{
+    if (T < 0 || k < 1 || E < 1) return ORC_BAD_ARG;
+    int64_t n = (int64_t)T * k;
+    int32_t *pt = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    int32_t *pe = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    if (!pt || !pe) { free(pt); free(pe); return ORC_NO_MEM; }
+    for (int t = 0; t < T; t++) {
+        for (int j = 0; j < k; j++) {
+            pt[(int64_t)t * k + j] = t;
+            pe[(int64_t)t * k + j] = topk_idx[(int64_t)t * k + j];
+        }
+    }
+    int status = oracle_row_id_map_pairs(pt, pe, n, T, E, row_id_map, expert_offsets);
+    free(pt);
+    free(pe);
+    return status;
+}
+
+/* Destination row of token t's slot j, with bounds checks. */
+static int slot_row(const int32_t *topk_idx, const int32_t *row_id_map,
+                    int T, int k, int E, int64_t n_rows, int t, int j, int64_t *row)
+{
+    int e = topk_idx[(int64_t)t * k + j];
+    if (e < 0 || e >= E) return ORC_BAD_EXPERT;
+    int32_t r = row_id_map[(int64_t)e * T + t];
+    if (r < 0 || (int64_t)r >= n_rows) return ORC_BAD_ROW;
+    *row = r;
+    return ORC_OK;
+}
+
+/* ---- (2) permute -------------------------------------------------------- */
+
+/*
+ * d9d permute_with_probs.py, _permute_kernel: each token's hidden row is
+ * stored unchanged to every destination row it is routed to, and with
+ * probabilities the token's probability for that expert is stored at the
+ * same destination index.  (The kernel's zero-row rule for a probability of
+ * exactly 0.0 serves mask-map padding and is not part of this path.)
+ * out is [T*k][H] bf16 bits; out_probs [T*k] (may be NULL).
+ */
+int oracle_permute(const uint16_t *x, const float *probs, const int32_t *topk_idx,
+                   const int32_t *row_id_map, int T, int H, int k, int E,
+                   uint16_t *out, float *out_probs)
+{
+    if (T < 0 || H < 1 || k < 1 || E < 1) return ORC_BAD_ARG;
+    int64_t n_rows = (int64_t)T * k;
+    for (int t = 0; t < T; t++) {
+        for (int j = 0; j < k; j++) {
+            int64_t r;
+            int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
+            if (s) return s;
+            for (int h = 0; h < H; h++) out[r * H + h] = x[(int64_t)t * H + h];
+            if (probs && out_probs) out_probs[r] = probs[(int64_t)t * k + j];
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- (4) unpermute combine ---------------------------------------------- */
+
+/*
+ * Megatron-core core.transformer.moe.batch_invariant,
+ * unpermute_with_bf16_rank_partials (and _rank_tree_unpermute_kernel with
+ * BF16_RANK_PARTIALS): the token's routes are added in the order of its
+ * route rows ([tokens, topk], i.e. top-k slot order), as fp32 fused
+ * multiply-adds of probability and row starting from zero, and the sum is
+ * rounded to bf16.  With one EP rank that is the whole combine.
+ *   acc = +0.0f
+ *   for j = 0 .. k-1:  acc = fmaf(p[t][j], float(in[r_j][h]), acc)
+ *   out[t][h] = bf16_rne(acc)
+ * probs == NULL means unit weights; fmaf(1, x, acc) is then exactly acc + x.
+ * in is [n_rows][H] bf16 bits (n_rows = T*k normally).
+ */
+int oracle_unpermute(const uint16_t *in, const float *probs, const int32_t *topk_idx,
+                     const int32_t *row_id_map, int T, int H, int k, int E,
+                     int64_t n_rows, uint16_t *out)
+{
+    if (T < 0 || H < 1 || k < 1 || E < 1) return ORC_BAD_ARG;
+    for (int t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++) {
+            float acc = +0.0f;
+            for (int j = 0; j < k; j++) {
+                int64_t r;
+                int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
+                if (s) return s;
+                float p = probs ? probs[(int64_t)t * k + j] : 1.0f;
+                acc = fmaf(p, bf16_to_f32(in[r * H + h]), acc);
+            }
+            out[(int64_t)t * H + h] = f32_to_bf16_rne(acc);
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- unpermute backward ------------------------------------------------- */
+
+/*
+ * d9d permute_with_probs.py, _unpermute_bwd_with_merging_probs_kernel:
+ *   act grad:  d_in[r_j][h] = bf16(fp32(d_out[t][h]) * p[t][j])
+ *              (an fp32 product rounded to fp32, then cast to bf16; there is
+ *              no addition, so no fused operation),
+ *   prob grad: d_probs[t][j] = sum_h float(fwd_in[r_j][h]) * float(d_out[t][h]).
+ * Megatron batch_invariant, _rank_tree_unpermute_bwd_kernel: each permuted
+ * row belongs to one (token, slot), so the scatter has one writer per row.
+ * The pages leave the order of the prob-grad sum open; here each product of
+ * two bf16 values is exact in fp64 and the products are summed in fp64, with
+ * one final rounding to fp32 (a tolerance covers any fp32 order).
+ * probs == NULL: d_in[r_j] = d_out[t] bitwise and d_probs is not written.
+ */
+int oracle_unpermute_bwd(const uint16_t *d_out, const uint16_t *fwd_in, const float *probs,
+                         const int32_t *topk_idx, const int32_t *row_id_map,
+                         int T, int H, int k, int E, int64_t n_rows,
+                         uint16_t *d_in, float *d_probs)
+{
+    if (T < 0 || H < 1 || k < 1 || E < 1) return ORC_BAD_ARG;
+    for (int t = 0; t < T; t++) {
+        for (int j = 0; j < k; j++) {
+            int64_t r;
+            int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
+            if (s) return s;
+            if (probs) {
+                float p = probs[(int64_t)t * k + j];
+                for (int h = 0; h < H; h++) {
+                    float g = bf16_to_f32(d_out[(int64_t)t * H + h]);
+                    float prod = g * p;          /* one fp32 rounding */
+                    d_in[r * H + h] = f32_to_bf16_rne(prod);
+                }
+                if (d_probs && fwd_in) {
+                    double dot = 0.0;
+                    for (int h = 0; h < H; h++) {
+                        double a = (double)bf16_to_f32(fwd_in[r * H + h]);
+                        double b = (double)bf16_to_f32(d_out[(int64_t)t * H + h]);
+                        dot += a * b;
+                    }
+                    d_probs[(int64_t)t * k + j] = (float)dot;
+                }
+            } else {
+                for (int h = 0; h < H; h++) d_in[r * H + h] = d_out[(int64_t)t * H + h];
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- permute backward --------------------------------------------------- */
+
+/*
+ * d9d permute_with_probs.py, _moe_permute_mask_map.backward: the permute's
+ * gradient is the unweighted unpermute of the permuted gradient, and the
+ * permuted-probability gradient is gathered back to each token's slots.
+ *   d_x[t][h]        = bf16_rne(((+0 + g_0) + g_1) + ... + g_{k-1}),
+ *                      g_j = float(d_out[r_j][h]), fp32, slot order
+ *   d_probs[t][j]    = d_out_probs[r_j]
+ */
+int oracle_permute_bwd(const uint16_t *d_out, const float *d_out_probs, const int32_t *topk_idx,
+                       const int32_t *row_id_map, int T, int H, int k, int E, int64_t n_rows,
+                       uint16_t *d_x, float *d_probs)
+{
+    if (T < 0 || H < 1 || k < 1 || E < 1) return ORC_BAD_ARG;
+    for (int t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++) {
+            float acc = +0.0f;
+            for (int j = 0; j < k; j++) {
+                int64_t r;
+                int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
+                if (s) return s;
+                acc = acc + bf16_to_f32(d_out[r * H + h]);
+            }
+            d_x[(int64_t)t * H + h] = f32_to_bf16_rne(acc);
+        }
+        if (d_out_probs && d_probs) {
+            for (int j = 0; j < k; j++) {
+                int64_t r;
+                int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
+                if (s) return s;
+                d_probs[(int64_t)t * k + j] = d_out_probs[r];
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- (3) fused chunk sort-and-pad / unpad-and-restore -------------------- */
+
+/*
+ * TransformerEngine PR "Fuse MoE chunk sorting and padding", Description,
+ * Changes and Diagram.  Rank chunks arrive back to back in input order
+ * (chunk c holds split_sizes[c] rows).  The explicit chunk order lists, for
+ * each sorted position q, the input chunk sorted_idx[q]; R consecutive sorted
+ * positions form one expert group g = q / R.  Inside a group the chunks are
+ * laid back to back; the group is then zero-padded to a multiple of the
+ * alignment A (an empty group takes no rows).  The map from padded
+ * destination rows to source rows is kept for the restore and the
+ * backward; destination rows with no source hold -1, including every row
+ * past the last group up to the fixed output capacity.
+ *   src_off[c]  = split_sizes[0] + ... + split_sizes[c-1]   (input order)
+ *   n_g         = sum of split_sizes[sorted_idx[q]] over q in group g
+ *   padded_g    = ceil(n_g / A) * A
+ *   pad_off[g]  = padded_0 + ... + padded_{g-1};  padded_offsets = pad_off
+ * Errors: order not a permutation of [0, C), a negative size, C % R != 0,
+ * sum of sizes > N_cap, pad_off[G] > out_cap.
+ */
+int oracle_chunk_map(const int32_t *split_sizes, const int32_t *sorted_idx, int C, int R, int A,
+                     int N_cap, int out_cap, int32_t *row_map, int32_t *padded_offsets)
+{
+    if (C < 1 || R < 1 || A < 1 || N_cap < 0 || out_cap < 0 || C % R != 0) return ORC_BAD_ARG;
+    int G = C / R;
+    int status = ORC_OK;
+    int64_t *src_off = (int64_t *)calloc((size_t)C, sizeof(int64_t));
+    int *seen = (int *)calloc((size_t)C, sizeof(int));
+    if (!src_off || !seen) { free(src_off); free(seen); return ORC_NO_MEM; }
+
+    int64_t total = 0;
+    for (int c = 0; c < C; c++) {
+        if (split_sizes[c] < 0) { status = ORC_BAD_CHUNKS; goto done; }
+        src_off[c] = total;
+        total += split_sizes[c];
+    }
+    for (int q = 0; q < C; q++) {
+        int c = sorted_idx[q];
+        if (c < 0 || c >= C || seen[c]) { status = ORC_BAD_CHUNKS; goto done; }
+        seen[c] = 1;
+    }
+    if (total > N_cap) { status = ORC_OVERFLOW; goto done; }
+
+    for (int d = 0; d < out_cap; d++) row_map[d] = -1;
+
+    int64_t group_start = 0;
+    for (int g = 0; g < G; g++) {
+        padded_offsets[g] = (int32_t)group_start;
+        int64_t d = group_start;          /* next destination row in group */
+        for (int q = g * R; q < (g + 1) * R; q++) {
+            int c = sorted_idx[q];
+            for (int i = 0; i < split_sizes[c]; i++) {
+                if (d >= out_cap) { status = ORC_OVERFLOW; goto done; }
+                row_map[d] = (int32_t)(src_off[c] + i);
+                d += 1;
+            }
+        }
+        int64_t n_g = d - group_start;
+        int64_t padded = ((n_g + A - 1) / A) * A;
+        group_start += padded;
+        if (group_start > out_cap) { status = ORC_OVERFLOW; goto done; }
+    }
+    padded_offsets[G] = (int32_t)group_start;
+
+done:
+    free(src_off);
+    free(seen);
+    return status;
+}
+
+/*
+ * Sort-and-pad copy (same PR): out[d] = in[row_map[d]] for mapped rows and
+ * all-zero bits for padding rows; the probabilities move with the tokens.
+ * elem_bytes / prob_bytes give the element sizes (copies are bitwise).
+ */
+static int pad_copy(const uint8_t *in, const uint8_t *probs, int elem_bytes, int prob_bytes,
+                    int N_cap, int H, const int32_t *row_map, int out_cap,
+                    uint8_t *out, uint8_t *out_probs)
+{
+    int64_t row_bytes = (int64_t)H * elem_bytes;
+    for (int d = 0; d < out_cap; d++) {
+        int32_t s = row_map[d];
+        if (s >= N_cap) return ORC_BAD_ROW;
+        if (s >= 0) {
+            memcpy(out + d * row_bytes, in + (int64_t)s * row_bytes, (size_t)row_bytes);
+            if (probs && out_probs)
+                memcpy(out_probs + (int64_t)d * prob_bytes, probs + (int64_t)s * prob_bytes,
+                       (size_t)prob_bytes);
+        } else {
+            memset(out + d * row_bytes, 0, (size_t)row_bytes);
+            if (probs && out_probs) memset(out_probs + (int64_t)d * prob_bytes, 0, (size_t)prob_bytes);
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Unpad-and-restore copy (same PR): every mapped padded row goes back to its
+ * source row; padding rows are dropped.  Rows of the restored buffer that no
+ * chunk covers (from the token total up to N_cap) are all-zero bits.
+ */
+static int restore_copy(const uint8_t *in, const uint8_t *probs, int elem_bytes, int prob_bytes,
+                        const int32_t *row_map, int64_t n_act, int out_cap, int H, int N_cap,
+                        uint8_t *out, uint8_t *out_probs)
+{
+    int64_t row_bytes = (int64_t)H * elem_bytes;
+    for (int64_t s = n_act; s < N_cap; s++) {
+        memset(out + s * row_bytes, 0, (size_t)row_bytes);
+        if (probs && out_probs) memset(out_probs + s * prob_bytes, 0, (size_t)prob_bytes);
+    }
+    for (int d = 0; d < out_cap; d++) {
+        int32_t s = row_map[d];
+        if (s >= N_cap) return ORC_BAD_ROW;
+        if (s < 0) continue;
+        memcpy(out + (int64_t)s * row_bytes, in + (int64_t)d * row_bytes, (size_t)row_bytes);
+        if (probs && out_probs)
+            memcpy(out_probs + (int64_t)s * prob_bytes, probs + (int64_t)d * prob_bytes,
+                   (size_t)prob_bytes);
+    }
+    return ORC_OK;
+}
+
+static int check_elem(int elem_bytes, int prob_bytes)
+{
+    if (elem_bytes != 2 && elem_bytes != 4) return ORC_BAD_ARG;
+    if (prob_bytes != 2 && prob_bytes != 4) return ORC_BAD_ARG;
+    return ORC_OK;
+}
+
+int oracle_sort_chunks_and_pad(const void *in, const void *probs, int elem_bytes, int prob_bytes,
+                               int N_cap, int H, const int32_t *split_sizes,
+                               const int32_t *sorted_idx, int C, int R, int A, int out_cap,
+                               void *out, void *out_probs, int32_t *row_map,
+                               int32_t *padded_offsets)
+{
+    int s = check_elem(elem_bytes, prob_bytes);
+    if (s || H < 1) return s ? s : ORC_BAD_ARG;
+    s = oracle_chunk_map(split_sizes, sorted_idx, C, R, A, N_cap, out_cap, row_map, padded_offsets);
+    if (s) return s;
+    return pad_copy((const uint8_t *)in, (const uint8_t *)probs, elem_bytes, prob_bytes, N_cap, H,
+                    row_map, out_cap, (uint8_t *)out, (uint8_t *)out_probs);
+}
+
+int oracle_unpad_and_restore_chunks(const void *in, const void *probs, int elem_bytes,
+                                    int prob_bytes, const int32_t *row_map,
+                                    const int32_t *split_sizes, int C, int out_cap, int H,
+                                    int N_cap, void *out, void *out_probs)
+{
+    int s = check_elem(elem_bytes, prob_bytes);
+    if (s || H < 1 || C < 1) return s ? s : ORC_BAD_ARG;
+    int64_t n_act = 0;
+    for (int c = 0; c < C; c++) {
+        if (split_sizes[c] < 0) return ORC_BAD_CHUNKS;
+        n_act += split_sizes[c];
+    }
+    if (n_act > N_cap) return ORC_OVERFLOW;
+    return restore_copy((const uint8_t *)in, (const uint8_t *)probs, elem_bytes, prob_bytes,
+                        row_map, n_act, out_cap, H, N_cap, (uint8_t *)out, (uint8_t *)out_probs);
+}
+
+/*
+ * Backwards (same PR, Changes: padding is zero-filled and contributes zero
+ * gradient).  The sort-and-pad copy is a row permutation plus zero rows, so
+ * its gradient is the restore applied to the padded gradient (padding-row
+ * gradients are dropped); the restore's gradient is the pad copy applied to
+ * the restored gradient (padding rows get zero gradient).
+ */
+int oracle_sort_chunks_and_pad_bwd(const void *d_out, const void *d_out_probs, int elem_bytes,
+                                   int prob_bytes, const int32_t *row_map,
+                                   const int32_t *split_sizes, int C, int out_cap, int H,
+                                   int N_cap, void *d_in, void *d_in_probs)
+{
+    return oracle_unpad_and_restore_chunks(d_out, d_out_probs, elem_bytes, prob_bytes, row_map,
+                                           split_sizes, C, out_cap, H, N_cap, d_in, d_in_probs);
+}
+
+int oracle_unpad_and_restore_chunks_bwd(const void *d_out, const void *d_out_probs,
+                                        int elem_bytes, int prob_bytes, const int32_t *row_map,
+                                        int out_cap, int H, int N_cap, void *d_in,
+                                        void *d_in_probs)
+{
+    int s = check_elem(elem_bytes, prob_bytes);
+    if (s || H < 1) return s ? s : ORC_BAD_ARG;
+    return pad_copy((const uint8_t *)d_out, (const uint8_t *)d_out_probs, elem_bytes, prob_bytes,
+                    N_cap, H, row_map, out_cap, (uint8_t *)d_in, (uint8_t *)d_in_probs);
+}

@@ -1,0 +1,488 @@
+"""Pins for the CPU oracle: each test checks the oracle against something
+other than itself -- values printed on the pages, brute force on tiny inputs,
+exact rational arithmetic, closed forms, invariants, or an independent
+library routine (torch CPU casts, numpy sorts and dots).
+
+No test here needs a GPU.
+"""
+import itertools
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers ---
+
+def _read_golden(name):
+    blocks, cur = {}, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.replace("_", "").isalnum() and not any(c.isdigit() for c in line[:1]) \
+                    and " " not in line:
+                cur = line
+                blocks[cur] = []
+                continue
+            blocks[cur].append(line.split())
+    return blocks
+
+
+def _bits(t):
+    return workloads.bf16_bits(t)
+
+
+def _to_bf16_torch(f32: np.ndarray) -> np.ndarray:
+    """Reference fp32 -> bf16 RNE by torch's CPU cast (bit patterns)."""
+    return _bits(torch.from_numpy(np.ascontiguousarray(f32, np.float32)).to(torch.bfloat16))
+
+
+def _bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _rn_f32(q: Fraction) -> Fraction:
+    """Round an exact rational to the nearest binary32 value, ties to even
+    (independent of the oracle; overflow is not exercised here)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                      # subnormal range: fixed quantum
+    quantum = Fraction(2) ** (e - 23)
+    m = a / quantum
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * n * quantum
+
+
+def _brute_rows(topk_idx: np.ndarray, E: int):
+    """Row of every (t, j) by sorting the (expert, token) pairs: the rows
+    are expert-major with ascending tokens inside an expert."""
+    T, k = topk_idx.shape
+    pairs = sorted((int(topk_idx[t, j]), t, j) for t in range(T) for j in range(k))
+    rows = np.empty((T, k), np.int64)
+    for pos, (_, t, j) in enumerate(pairs):
+        rows[t, j] = pos
+    ref = np.full((E, T), -1, np.int32)
+    for t in range(T):
+        for j in range(k):
+            ref[topk_idx[t, j], t] = rows[t, j]
+    counts = np.bincount(topk_idx.ravel(), minlength=E)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return ref, offs, rows
+
+
+# ---------------------------------------------------- (1) the row map ------
+
+def test_worked_example_second_pass():
+    g = _read_golden("p2_worked_example.txt")
+    mask = np.array(g["routing_map"], dtype=np.int32)          # [T][E]
+    pass2 = np.array(g["pass2"], dtype=np.int32)               # [T][E]
+    T, E = mask.shape
+    pt, pe = np.nonzero(mask)          # row-major: token order, then expert
+    m, off = oracle.row_id_map_pairs(pt, pe, T, E)
+    np.testing.assert_array_equal(m, pass2.T)   # our layout is [E][T]
+    np.testing.assert_array_equal(off, [0, 3, 5, 7])
+
+
+def test_worked_example_third_pass():
+    g = _read_golden("p2_worked_example.txt")
+    mask = np.array(g["routing_map"], dtype=np.int32)
+    T, E = mask.shape
+    pt, pe = np.nonzero(mask)
+    m, _ = oracle.row_id_map_pairs(pt, pe, T, E)
+    for t, row in enumerate(g["pass3"]):
+        n = int(row[2 * E])
+        rows = sorted((int(m[e, t]), e) for e in range(E) if m[e, t] >= 0)[::-1]
+        assert n == len(rows)
+        assert [int(v) for v in row[:n]] == [r for r, _ in rows]
+        assert [int(v) for v in row[E:E + n]] == [e for _, e in rows]
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (2, 3, 1), (3, 3, 2), (2, 4, 3), (3, 4, 2),
+                                   (4, 3, 1), (2, 3, 3)])
+def test_row_map_brute_force_all_routings(T, E, k):
+    """Every routing with k distinct experts per token, in every slot order."""
+    choices = list(itertools.permutations(range(E), k))
+    for routing in itertools.product(choices, repeat=T):
+        idx = np.array(routing, dtype=np.int32).reshape(T, k)
+        m, off = oracle.row_id_map(idx, E)
+        ref, ref_off, _ = _brute_rows(idx, E)
+        np.testing.assert_array_equal(m, ref)
+        np.testing.assert_array_equal(off, ref_off)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_row_map_equals_stable_argsort(seed):
+    """A stable argsort of the flattened top-k indices gives the same rows."""
+    rng = np.random.default_rng(seed)
+    T, E, k = int(rng.integers(1, 300)), int(rng.integers(1, 70)), 0
+    k = int(rng.integers(1, min(E, 9) + 1))
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    m, off = oracle.row_id_map(idx, E)
+    order = np.argsort(idx.ravel(), kind="stable")
+    row_of_flat = np.empty_like(order)
+    row_of_flat[order] = np.arange(order.size)
+    t = np.repeat(np.arange(T), k)
+    np.testing.assert_array_equal(m[idx.ravel(), t], row_of_flat)
+    assert (m >= 0).sum() == T * k
+
+
+def test_row_map_invariants_skewed():
+    w = workloads.random_routed(2000, 8, 96, 7, seed=11, with_dy=False, zipf_s=1.1)
+    idx = w.topk_idx.numpy()
+    m, off = oracle.row_id_map(idx, 96)
+    counts = np.bincount(idx.ravel(), minlength=96)
+    assert counts.sum() == 2000 * 7 == off[-1]
+    np.testing.assert_array_equal(np.diff(off), counts)
+    rows = m[m >= 0]
+    np.testing.assert_array_equal(np.sort(rows), np.arange(2000 * 7))   # bijection
+    for e in range(96):
+        r = m[e][m[e] >= 0]
+        assert np.all(np.diff(r) == 1)                  # ascending tokens, dense
+        if r.size:
+            assert r[0] == off[e] and r[-1] == off[e + 1] - 1
+
+
+def test_row_map_errors():
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.row_id_map(np.array([[0, 3]], np.int32), 3)
+    assert ei.value.code == 1
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.row_id_map(np.array([[1, 1]], np.int32), 3)
+    assert ei.value.code == 2
+    with pytest.raises(oracle.OracleError):
+        oracle.row_id_map(np.array([[-1]], np.int32), 3)
+
+
+def test_row_map_empty_tokens():
+    m, off = oracle.row_id_map(np.zeros((0, 2), np.int32), 5)
+    assert m.shape == (5, 0)
+    np.testing.assert_array_equal(off, np.zeros(6))
+
+
+# ------------------------------------------------------- (2) permute -------
+
+def _routed(T, H, E, k, seed):
+    return workloads.random_routed(T, H, E, k, seed=seed)
+
+
+@pytest.mark.parametrize("T,H,E,k", [(16, 64, 32, 4), (37, 24, 9, 3), (5, 7, 2, 2)])
+def test_permute_is_row_copy(T, H, E, k):
+    w = _routed(T, H, E, k, seed=T)
+    idx = w.topk_idx.numpy()
+    x = _bits(w.x)
+    m, _ = oracle.row_id_map(idx, E)
+    out, op = oracle.permute(x, w.probs.numpy(), idx, m)
+    _, _, rows = _brute_rows(idx, E)
+    exp = np.empty((T * k, H), np.uint16)
+    exp_p = np.empty(T * k, np.float32)
+    exp[rows.ravel()] = np.repeat(x, k, axis=0)
+    exp_p[rows.ravel()] = w.probs.numpy().ravel()
+    np.testing.assert_array_equal(out, exp)
+    np.testing.assert_array_equal(op, exp_p)
+
+
+# ----------------------------------------------------- (4) unpermute -------
+
+def test_libm_fmaf_is_fused():
+    a = 1.0 + 2.0 ** -12
+    c = -(1.0 + 2.0 ** -11)
+    assert oracle.fmaf(a, a, c) == 2.0 ** -24           # one rounding
+    assert np.float32(np.float32(a) * np.float32(a)) + np.float32(c) == 0.0
+
+
+def test_bf16_rounding_matches_torch_cast():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.standard_normal(3000).astype(np.float32),
+        (rng.standard_normal(500) * 1e-39).astype(np.float32),          # subnormals
+        np.clip(rng.standard_normal(500) * 1e38, -3.3e38, 3.3e38).astype(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 1.0, -1.0, 3.4028235e38], np.float32),
+    ])
+    # exact ties: low 16 bits == 0x8000, with even and odd kept parts
+    u = rng.integers(0, 2 ** 31, 1000, dtype=np.uint32)
+    ties = ((u & 0xFFFF0000) | 0x8000).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    vals = np.concatenate([vals, ties])
+    got = np.array([oracle.f32_to_bf16(float(v)) for v in vals], np.uint16)
+    np.testing.assert_array_equal(got, _to_bf16_torch(vals))
+    # NaN: stays NaN, quiet bit set, sign kept
+    for pattern in (0x7FA00001, 0xFFC12345, 0x7F800001):
+        f = np.array([pattern], np.uint32).view(np.float32)[0]
+        b = oracle.f32_to_bf16(float(f))
+        assert (b & 0x7F80) == 0x7F80 and (b & 0x0040) and (b >> 15) == (pattern >> 31)
+
+
+def test_unpermute_k1_is_single_rounded_product():
+    """k = 1: out = bf16(RN32(p * x)); torch's fp32 multiply and bf16 cast."""
+    w = _routed(64, 40, 8, 1, seed=3)
+    idx = w.topk_idx.numpy()
+    m, _ = oracle.row_id_map(idx, 8)
+    x = _bits(w.x)
+    P, _ = oracle.permute(x, None, idx, m)
+    p = (w.probs * 0.0 + torch.rand(64, 1, generator=torch.Generator().manual_seed(9)))
+    y = oracle.unpermute(P, p.numpy(), idx, m)
+    exp = _bits((w.x.float() * p).to(torch.bfloat16))
+    np.testing.assert_array_equal(y, exp)
+    # unit weight (probs omitted): permute then unpermute is the identity
+    y1 = oracle.unpermute(P, None, idx, m)
+    np.testing.assert_array_equal(y1, x)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 6, 8])
+def test_unpermute_unit_probs_k_copies(k):
+    """Unit weights over k identical copies: j*x is exact in fp32 for bf16 x,
+    so the result is bf16(k*x) (torch cast of the exact product)."""
+    E = 12
+    w = _routed(50, 33, E, k, seed=k)
+    idx = w.topk_idx.numpy()
+    m, _ = oracle.row_id_map(idx, E)
+    P, _ = oracle.permute(_bits(w.x), None, idx, m)
+    y = oracle.unpermute(P, None, idx, m)
+    ones = np.ones((50, k), np.float32)
+    y2 = oracle.unpermute(P, ones, idx, m)
+    exp = _bits((w.x.float() * k).to(torch.bfloat16))
+    np.testing.assert_array_equal(y, exp)
+    np.testing.assert_array_equal(y2, exp)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_unpermute_exact_rational_fma_chain(seed):
+    """Each step acc = RN32(p_j * x_j + acc) computed with exact rationals,
+    in slot order from zero, then bf16 by torch's cast.  Catches a dropped
+    fusion (mul-then-add), a reversed slot order or a wrong start value."""
+    T, H, E, k = 6, 12, 10, 5
+    w = _routed(T, H, E, k, seed=100 + seed)
+    idx = w.topk_idx.numpy()
+    probs = w.probs.numpy()
+    m, _ = oracle.row_id_map(idx, E)
+    rng = np.random.default_rng(seed)
+    P = _bits(torch.from_numpy(rng.standard_normal((T * k, H)).astype(np.float32))
+              .to(torch.bfloat16))
+    y = oracle.unpermute(P, probs, idx, m)
+    Pf = _bf16_to_f32(P)
+    acc_f = np.zeros((T, H), np.float32)
+    for t in range(T):
+        for h in range(H):
+            acc = Fraction(0)
+            for j in range(k):
+                r = m[idx[t, j], t]
+                acc = _rn_f32(Fraction(float(probs[t, j])) * Fraction(float(Pf[r, h])) + acc)
+            acc_f[t, h] = float(acc)
+    np.testing.assert_array_equal(y, _to_bf16_torch(acc_f))
+
+
+# -------------------------------------------------- unpermute backward -----
+
+def test_unpermute_bwd_act_grad_and_prob_grad():
+    T, H, E, k = 40, 72, 16, 4
+    w = _routed(T, H, E, k, seed=21)
+    idx = w.topk_idx.numpy()
+    m, _ = oracle.row_id_map(idx, E)
+    _, _, rows = _brute_rows(idx, E)
+    rng = np.random.default_rng(1)
+    fwd_in = _bits(torch.from_numpy(rng.standard_normal((T * k, H)).astype(np.float32))
+                   .to(torch.bfloat16))
+    dy = _bits(w.dy)
+    d_in, d_p = oracle.unpermute_bwd(dy, fwd_in, w.probs.numpy(), idx, m)
+    # act grad: torch fp32 multiply, then torch bf16 cast, scattered to rows
+    prod = (w.dy.float()[:, None, :] * w.probs[:, :, None]).to(torch.bfloat16)
+    exp = np.empty((T * k, H), np.uint16)
+    exp[rows.ravel()] = _bits(prod.reshape(T * k, H))
+    np.testing.assert_array_equal(d_in, exp)
+    # prob grad: numpy float64 dot of the widened rows
+    fi = _bf16_to_f32(fwd_in).astype(np.float64)
+    g = _bf16_to_f32(dy).astype(np.float64)
+    ref = np.einsum("tjh,th->tj", fi[rows], g)
+    scale = np.einsum("tjh,th->tj", np.abs(fi[rows]), np.abs(g))
+    assert np.all(np.abs(d_p.astype(np.float64) - ref) <= 1e-6 * scale + 1e-30)
+    # without probs the scatter is a bitwise copy
+    d_in0, d_p0 = oracle.unpermute_bwd(dy, None, None, idx, m)
+    exp0 = np.empty_like(exp)
+    exp0[rows.ravel()] = np.repeat(dy, k, axis=0)
+    np.testing.assert_array_equal(d_in0, exp0)
+    assert d_p0 is None
+
+
+# ---------------------------------------------------- permute backward -----
+
+def test_permute_bwd_slot_order_sum():
+    T, H, E, k = 30, 20, 11, 6
+    w = _routed(T, H, E, k, seed=31)
+    idx = w.topk_idx.numpy()
+    m, _ = oracle.row_id_map(idx, E)
+    _, _, rows = _brute_rows(idx, E)
+    rng = np.random.default_rng(2)
+    dP_t = torch.from_numpy(rng.standard_normal((T * k, H)).astype(np.float32)).to(torch.bfloat16)
+    dpp = rng.standard_normal(T * k).astype(np.float32)
+    dx, dprob = oracle.permute_bwd(_bits(dP_t), dpp, idx, m)
+    acc = torch.zeros(T, H, dtype=torch.float32)
+    rr = torch.from_numpy(rows)
+    for j in range(k):                        # torch fp32 adds, slot order
+        acc = acc + dP_t.float()[rr[:, j]]
+    np.testing.assert_array_equal(dx, _bits(acc.to(torch.bfloat16)))
+    np.testing.assert_array_equal(dprob, dpp[rows])
+    # closed form: gradient rows that are k copies of dY sum to bf16(k*dY)
+    dP_copy, _ = oracle.permute(_bits(w.dy), None, idx, m)
+    dx2, _ = oracle.permute_bwd(dP_copy, None, idx, m)
+    np.testing.assert_array_equal(dx2, _bits((w.dy.float() * k).to(torch.bfloat16)))
+
+
+# ------------------------------------- (3) chunk sort-and-pad / restore ----
+
+def _brute_chunk_rows(sizes, order, R, A, out_cap):
+    """Padded destination rows by list concatenation, group by group."""
+    src_off = np.concatenate([[0], np.cumsum(sizes)])[:-1]
+    rows, offs = [], []
+    for g in range(len(order) // R):
+        offs.append(len(rows))
+        grp = []
+        for q in range(g * R, (g + 1) * R):
+            c = order[q]
+            grp += list(range(src_off[c], src_off[c] + sizes[c]))
+        while len(grp) % A:
+            grp.append(-1)
+        rows += grp
+    offs.append(len(rows))
+    rows += [-1] * (out_cap - len(rows))
+    return np.array(rows, np.int32), np.array(offs, np.int32)
+
+
+def test_chunk_map_brute_force_small():
+    rng = np.random.default_rng(5)
+    for trial in range(400):
+        R = int(rng.integers(1, 4))
+        G = int(rng.integers(1, 4))
+        C = R * G
+        A = int(rng.choice([1, 2, 4, 3]))
+        sizes = rng.integers(0, 4, C).astype(np.int32)
+        order = rng.permutation(C).astype(np.int32)
+        n = int(sizes.sum())
+        slack = int(rng.integers(0, 5))
+        out_cap = int(np.sum(-(-np.add.reduceat(sizes[order], np.arange(0, C, R)) // A) * A)) + slack
+        row_map, offs = oracle.chunk_map(sizes, order, R, A, n + slack, out_cap)
+        ref_rows, ref_offs = _brute_chunk_rows(sizes, order, R, A, out_cap)
+        np.testing.assert_array_equal(row_map, ref_rows)
+        np.testing.assert_array_equal(offs, ref_offs)
+
+
+def test_chunk_copies_roundtrip_and_special_cases():
+    w = workloads.chunked(600, seed=7, H=24, num_ranks=3, num_experts=4, align=8, num_empty=3)
+    x = _bits(w.x)
+    s = w.split_sizes.numpy()
+    q = w.sorted_idx.numpy()
+    p = w.probs.numpy()
+    out, op, rm, offs = oracle.sort_chunks_and_pad(x, p, s, q, 3, 8, w.out_cap)
+    ref_rows, ref_offs = _brute_chunk_rows(s, q, 3, 8, w.out_cap)
+    np.testing.assert_array_equal(rm, ref_rows)
+    np.testing.assert_array_equal(offs, ref_offs)
+    mapped = ref_rows >= 0
+    np.testing.assert_array_equal(out[mapped], x[ref_rows[mapped]])
+    assert not out[~mapped].any() and not op[~mapped].any()
+    np.testing.assert_array_equal(op[mapped], p[ref_rows[mapped]])
+    pg = np.diff(offs)
+    ng = np.add.reduceat(s[q], np.arange(0, len(q), 3))
+    assert np.all(pg % 8 == 0) and np.all(ng <= pg) and np.all(pg < ng + 8)
+    back, bp = oracle.unpad_and_restore_chunks(out, op, rm, s, w.N_cap)
+    np.testing.assert_array_equal(back, x)                 # restore . pad = id
+    np.testing.assert_array_equal(bp, p)
+    # backward of the pad drops padding-row gradients; of the restore, zero
+    # gradient on padding rows
+    gpad = np.random.default_rng(0).integers(0, 2 ** 16, out.shape).astype(np.uint16)
+    d_in, _ = oracle.sort_chunks_and_pad_bwd(gpad, None, rm, s, w.N_cap)
+    np.testing.assert_array_equal(d_in[ref_rows[mapped]], gpad[mapped])
+    d_pad, _ = oracle.unpad_and_restore_chunks_bwd(x, None, rm, w.out_cap)
+    assert not d_pad[~mapped].any()
+    np.testing.assert_array_equal(d_pad[mapped], x[ref_rows[mapped]])
+
+
+def test_chunk_alignment_one_identity_order_is_memcpy():
+    s = np.array([3, 0, 5, 2, 4, 1], np.int32)
+    q = np.arange(6, dtype=np.int32)
+    x = np.arange(15 * 4, dtype=np.float32).reshape(15, 4)
+    out, _, rm, offs = oracle.sort_chunks_and_pad(x, None, s, q, 2, 1, 15)
+    np.testing.assert_array_equal(out, x)
+    np.testing.assert_array_equal(rm, np.arange(15))
+    # A = 1 with a shuffled order is a pure chunk permutation
+    q2 = np.array([5, 4, 3, 2, 1, 0], np.int32)
+    out2, _, rm2, _ = oracle.sort_chunks_and_pad(x, None, s, q2, 3, 1, 15)
+    src = np.concatenate([[0], np.cumsum(s)])
+    exp = np.concatenate([x[src[c]:src[c] + s[c]] for c in q2])
+    np.testing.assert_array_equal(out2, exp)
+
+
+def test_chunk_restore_zero_tail_and_errors():
+    s = np.array([2, 1, 0, 3], np.int32)          # 6 tokens in a buffer of 9
+    q = np.array([1, 3, 0, 2], np.int32)
+    x = np.arange(9 * 2, dtype=np.uint16).reshape(9, 2) + 1
+    out, _, rm, offs = oracle.sort_chunks_and_pad(x, None, s, q, 2, 4, 12)
+    np.testing.assert_array_equal(offs, [0, 4, 8])
+    back, _ = oracle.unpad_and_restore_chunks(out, None, rm, s, 9)
+    np.testing.assert_array_equal(back[:6], x[:6])
+    assert not back[6:].any()
+    with pytest.raises(oracle.OracleError):      # order is not a permutation
+        oracle.chunk_map(s, np.array([0, 0, 1, 2], np.int32), 2, 4, 9, 12)
+    with pytest.raises(oracle.OracleError):      # negative size
+        oracle.chunk_map(np.array([2, -1, 0, 3], np.int32), q, 2, 4, 9, 12)
+    with pytest.raises(oracle.OracleError):      # padded groups exceed capacity
+        oracle.chunk_map(s, q, 2, 4, 9, 7)
+    with pytest.raises(oracle.OracleError):      # tokens exceed the input buffer
+        oracle.chunk_map(s, q, 2, 4, 5, 12)
+    # an all-empty group takes no rows
+    s0 = np.array([0, 0, 2, 1], np.int32)
+    _, offs0 = oracle.chunk_map(s0, np.arange(4, dtype=np.int32), 2, 4, 3, 8)
+    np.testing.assert_array_equal(offs0, [0, 0, 4])
+
+
+def _one_token_unpermute(x_vals, p_vals):
+    """Unpermute of a single token whose k slots carry rows x_vals (exact
+    bf16 values, one hidden element) with weights p_vals."""
+    k = len(x_vals)
+    idx = np.arange(k, dtype=np.int32)[None, :]
+    m, _ = oracle.row_id_map(idx, k)
+    P = _to_bf16_torch(np.array(x_vals, np.float32))[:, None]
+    assert np.array_equal(_bf16_to_f32(P[:, 0]), np.array(x_vals, np.float32))
+    probs = None if p_vals is None else np.array([p_vals], np.float32)
+    return int(oracle.unpermute(P, probs, idx, m)[0, 0])
+
+
+def test_unpermute_crafted_fusion_survives_bf16():
+    """acc0 = -(1 - 2^-14 + 2^-20); slot 1 adds (1 - 2^-7 + 2^-20)(1 + 2^-7)
+    = 1 - 2^-14 + 2^-20 + 2^-27.  One rounding leaves exactly 2^-27 (bf16
+    0x3200); rounding the product first loses 2^-27 and gives +0."""
+    p0 = 1.0 - 2.0 ** -14 + 2.0 ** -20
+    p1 = 1.0 - 2.0 ** -7 + 2.0 ** -20
+    assert np.float32(p0) == p0 and np.float32(p1) == p1
+    assert _one_token_unpermute([-1.0, 1.0 + 2.0 ** -7], [p0, p1]) == 0x3200
+
+
+def test_unpermute_crafted_slot_order():
+    """Slots (2^30, -2^30, 1) summed in slot order give 1 (0x3F80); summed in
+    the reverse order the 1 is absorbed by -2^30 and the result is 0."""
+    assert _one_token_unpermute([2.0 ** 30, -(2.0 ** 30), 1.0], None) == 0x3F80
+    assert _one_token_unpermute([2.0 ** 30, -(2.0 ** 30), 1.0], [1, 1, 1]) == 0x3F80
+
+
+def test_unpermute_starts_from_positive_zero():
+    """All contributions -0: (+0) + (-0) = +0 under round-to-nearest."""
+    assert _one_token_unpermute([-0.0, -0.0], None) == 0x0000
+    assert _one_token_unpermute([-0.0, -0.0], [0.5, 0.25]) == 0x0000
+    assert _one_token_unpermute([-0.0], None) == 0x0000
