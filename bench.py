@@ -1,0 +1,321 @@
+"""Benchmark of the MoE permute / unpermute hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole routed path over one batch of synthetic
+input already resident in HBM:
+  routed workloads (finegrain, skewed, tiny):
+      row map -> permute (+probs) -> weighted unpermute
+      -> unpermute backward (act grad + prob grads) -> permute backward
+  chunk workloads (chunks8k, chunks32k):
+      sort-and-pad (+probs) -> unpad-and-restore (+probs)
+The default workload is the fine-grained MoE layer (T=4096, H=2048, E=64,
+k=6).  Every call goes straight through the C ABI (ctypes, precomputed
+device pointers) on torch's current stream.
+
+Printed: one JSON line with the throughput in algorithmic GB/s (bytes the
+method must move, divided by the measured step time), the per-op times
+measured with HIP events inside the timed region, the roofline of the
+dominant kernel, and the CPU oracle's rate on a bounded sample as a
+reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "permute+unpermute roundtrip GB/s & % of HBM peak (µs/call) per T,H,E,k"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="finegrain",
+                    choices=["tiny", "finegrain", "skewed", "chunks8k", "chunks32k"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured hipGraph")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- bytes ----
+
+def routed_bytes(T, H, E, k):
+    """Algorithmic bytes per op of a routed step (bf16 rows, fp32 probs,
+    int32 indices; each (t, j) lookup reads topk_idx and row_id_map)."""
+    row = 2 * H
+    look = 8 * T * k
+    return {
+        "row_map": 4 * T * k + 4 * E * T + 4 * (E + 1),
+        "permute": T * row + T * k * row + look + 4 * T * k + 4 * T * k,
+        "unpermute": T * k * row + T * row + look + 4 * T * k,
+        "unpermute_bwd": T * row + 2 * T * k * row + look + 4 * T * k + 4 * T * k,
+        "permute_bwd": T * k * row + T * row + look + 4 * T * k + 4 * T * k,
+    }
+
+
+def chunk_bytes(N, H, cap, eb=2):
+    row = eb * H
+    return {
+        "sort_chunks_and_pad": N * row + cap * row + 4 * N + 4 * cap + 4 * cap + 4 * cap,
+        "unpad_and_restore": N * row + N * row + 4 * cap + 4 * N + 4 * N,
+    }
+
+
+# --------------------------------------------------------------- setup ----
+
+class Step:
+    """A list of (name, fn, args) calls straight into the C ABI; the stream
+    argument (always last) is supplied at run time."""
+
+    def __init__(self):
+        self.ops = []
+        self.keep = []
+
+    def add(self, name, fn, *args):
+        self.ops.append((name, fn, args))
+
+    def run(self, events=None, stream=None):
+        import torch
+        s = ctypes.c_void_p(stream if stream is not None
+                            else torch.cuda.current_stream().cuda_stream)
+        for name, fn, args in self.ops:
+            if events is not None:
+                events[name][0].record()
+            st = fn(*args, s)
+            if events is not None:
+                events[name][1].record()
+            if st != 0:
+                raise RuntimeError(f"{name}: status {st}")
+
+
+def build_routed(m, w):
+    import torch
+    import workloads
+    dev = "cuda:0"
+    T, H, E, k = w.T, w.H, w.num_experts, w.k
+    lib = m._binding._lib
+    x, idx, probs, dy = (w.x.to(dev), w.topk_idx.to(dev), w.probs.to(dev), w.dy.to(dev))
+    rm = torch.empty((E, T), dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ws_n = m.moe_make_row_id_map_workspace_bytes(T, k, E)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    P = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    pp = torch.empty(T * k, dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dP = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    dprob = torch.empty((T, k), dtype=torch.float32, device=dev)
+    d_pp = workloads.random_rows(1, T * k, seed=7, device=dev).float().reshape(-1)
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dprob2 = torch.empty((T, k), dtype=torch.float32, device=dev)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    step = Step()
+    step.keep = [x, idx, probs, dy, rm, off, ws, P, pp, y, dP, dprob, d_pp, dx, dprob2]
+    n = T * k
+    step.add("row_map", lib.moe_make_row_id_map, p(idx), T, k, E, p(rm), p(off), None, p(ws),
+             ws_n,)
+    step.add("permute", lib.moe_permute, p(x), p(probs), p(idx), p(rm), T, H, k, E, n, p(P),
+             p(pp), None,)
+    step.add("unpermute", lib.moe_unpermute, p(P), p(probs), p(idx), p(rm), T, H, k, E, n, p(y),
+             None,)
+    step.add("unpermute_bwd", lib.moe_unpermute_bwd, p(dy), p(P), p(probs), p(idx), p(rm), T, H,
+             k, E, n, p(dP), p(dprob), None,)
+    step.add("permute_bwd", lib.moe_permute_bwd, p(dP), p(d_pp), p(idx), p(rm), T, H, k, E, n,
+             p(dx), p(dprob2), None,)
+    return step, routed_bytes(T, H, E, k)
+
+
+def build_chunks(m, cw):
+    import torch
+    dev = "cuda:0"
+    lib = m._binding._lib
+    x, probs = cw.x.to(dev), cw.probs.to(dev)
+    sizes, order = cw.split_sizes.to(dev), cw.sorted_idx.to(dev)
+    G = cw.C // cw.chunks_per_group
+    out = torch.empty((cw.out_cap, cw.H), dtype=x.dtype, device=dev)
+    out_p = torch.empty(cw.out_cap, dtype=torch.float32, device=dev)
+    rm = torch.empty(cw.out_cap, dtype=torch.int32, device=dev)
+    off = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    back = torch.empty_like(x)
+    back_p = torch.empty_like(probs)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    step = Step()
+    step.keep = [x, probs, sizes, order, out, out_p, rm, off, back, back_p]
+    eb = x.element_size()
+    step.add("sort_chunks_and_pad", lib.moe_sort_chunks_and_pad, p(x), p(probs), eb, 4,
+             cw.N_cap, cw.H, p(sizes), p(order), cw.C, cw.chunks_per_group, cw.align, cw.out_cap,
+             p(out), p(out_p), p(rm), p(off), None,)
+    step.add("unpad_and_restore", lib.moe_unpad_and_restore_chunks, p(out), p(out_p), eb, 4,
+             p(rm), p(sizes), cw.C, cw.out_cap, cw.H, cw.N_cap, p(back), p(back_p), None,)
+    return step, chunk_bytes(int(cw.split_sizes.sum()), cw.H, cw.out_cap, eb)
+
+
+# --------------------------------------------------------- CPU baseline ----
+
+def cpu_baseline(name, w, target_s, step_bytes):
+    """The oracle, untuned and single-threaded, on a bounded sample of the
+    same workload: whole steps on a prefix of the tokens, repeated until
+    about target_s seconds of CPU work."""
+    import numpy as np
+    import oracle
+    import workloads
+    if name.startswith("chunks"):
+        xb = workloads.bf16_bits(w.x)
+        p = w.probs.numpy()
+        s = w.split_sizes.numpy()
+        q = w.sorted_idx.numpy()
+
+        def one():
+            out, op, rm, _ = oracle.sort_chunks_and_pad(xb, p, s, q, w.chunks_per_group,
+                                                        w.align, w.out_cap)
+            oracle.unpad_and_restore_chunks(out, op, rm, s, w.N_cap)
+        frac = 1.0
+        sample = f"whole {name} roundtrip"
+    else:
+        T = w.T
+        Ts = min(T, max(64, int(T * 0.25)))          # a token prefix
+        idx = w.topk_idx.numpy()[:Ts]
+        pr = w.probs.numpy()[:Ts]
+        xb = workloads.bf16_bits(w.x[:Ts])
+        dyb = workloads.bf16_bits(w.dy[:Ts])
+        d_pp = np.linspace(-1, 1, Ts * w.k, dtype=np.float32)
+
+        def one():
+            rm, _ = oracle.row_id_map(idx, w.num_experts)
+            P, _ = oracle.permute(xb, pr, idx, rm)
+            oracle.unpermute(P, pr, idx, rm)
+            dP, _ = oracle.unpermute_bwd(dyb, P, pr, idx, rm)
+            oracle.permute_bwd(dP, d_pp, idx, rm)
+        frac = Ts / T
+        sample = f"whole steps on the first {Ts} of {T} tokens"
+    one()                                           # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        one()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    per_step = el / reps
+    gbs = step_bytes * frac / per_step / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}, {reps} repetitions, {el:.1f} s, single thread",
+            "seconds_per_full_step": round(per_step / frac, 4)}
+
+
+# ----------------------------------------------------------------- main ----
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); this path is "
+              "built and measured per GPU and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import unpermute_moe_make_amd as m
+    import workloads
+
+    torch.cuda.init()
+    name = args.workload
+    if name in workloads.ROUTED:
+        w = workloads.ROUTED[name]()
+        step, op_bytes = build_routed(m, w)
+        cfg = {"workload": name, "T": w.T, "H": w.H, "E": w.num_experts, "k": w.k,
+               "step": "row_map+permute+unpermute+unpermute_bwd+permute_bwd",
+               "probs": "fp32", "launch": "eager, C ABI via ctypes"}
+    else:
+        w = workloads.CHUNKED[name]()
+        step, op_bytes = build_chunks(m, w)
+        cfg = {"workload": name, "N": w.N_cap, "H": w.H, "chunks": w.C,
+               "chunks_per_group": w.chunks_per_group, "align": w.align, "out_cap": w.out_cap,
+               "step": "sort_chunks_and_pad+unpad_and_restore", "probs": "fp32",
+               "launch": "eager, C ABI via ctypes"}
+    step_bytes = sum(op_bytes.values())
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    names = [n for n, _, _ in step.ops]
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for n in names} for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step.run(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / K * 1e3
+
+    per_op = {}
+    for n in names:
+        times = sorted(evs[i][n][0].elapsed_time(evs[i][n][1]) * 1e3 for i in range(K))
+        mean = sum(times) / K
+        per_op[n] = {"us_mean": round(mean, 2), "us_median": round(times[K // 2], 2),
+                     "bytes": op_bytes[n],
+                     "GBps": round(op_bytes[n] / (mean * 1e-6) / 1e9, 1),
+                     "pct_hbm_peak": round(100 * op_bytes[n] / (mean * 1e-6) / 1e9 /
+                                           HBM_PEAK_GBS, 1)}
+    dom = max(names, key=lambda n: per_op[n]["us_mean"])
+    achieved = op_bytes[dom] / (per_op[dom]["us_mean"] * 1e-6) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": cfg,
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        "step_bytes": step_bytes,
+        "per_op": per_op,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if args.graph:
+        # The same step (same buffers) captured once and replayed.
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            step.run(stream=s2.cuda_stream)
+        torch.cuda.current_stream().wait_stream(s2)
+        with torch.cuda.graph(g, stream=s2):
+            step.run(stream=s2.cuda_stream)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) / K * 1e3
+        result["graph_replay"] = {"ms_per_step": round(gms, 4),
+                                  "GBps": round(step_bytes / (gms * 1e-3) / 1e9, 1)}
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(name, w, args.cpu_seconds, step_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,305 @@
+/*
+ * moe_perm.h -- C ABI of the MI355X (gfx950) MoE token permute / unpermute
+ * library: routing row map, permute, fixed-order unpermute, fused chunk
+ * sort-and-pad / unpad-and-restore, and the backward of each.
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [TE-mask]   d9d 0.1.0 wheel, d9d/kernel/moe/permute_with_probs.py (a copy
+ *               of TransformerEngine's mask-map permutation): make_row_id_map
+ *               and its worked example, _permute_kernel, _unpermute_kernel,
+ *               _unpermute_bwd_with_merging_probs_kernel and the two autograd
+ *               functions.
+ *   [MCORE-BI]  Megatron-core API docs, core.transformer.moe.batch_invariant:
+ *               unpermute_with_bf16_rank_partials, _rank_tree_unpermute_kernel,
+ *               _rank_tree_unpermute_bwd_kernel, _unpermute_loop.
+ *   [MOE-OPS]   moe-ops 0.1.0 README: "Why this library" and "Routing
+ *               permute / unpermute".
+ *   [XTUNER]    xtuner issue "permute different with torch version".
+ *   [TE-3509]   TransformerEngine PR "[PyTorch] Fuse MoE chunk sorting and
+ *               padding": Description, Changes, Validation, Diagram.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronises; each call enqueues its
+ *     kernels on `stream` and returns.  No call reads device memory from the
+ *     host, so every call can be captured in a hipGraph; sizes read on the
+ *     device (routing, chunk sizes) may change between graph replays.
+ *   - bf16 tensors are passed as `void*` holding 16-bit bf16 patterns,
+ *     row-major and contiguous.  Probabilities are fp32 unless stated.
+ *   - Index tensors are int32.  Row offsets are computed in 64 bits.
+ *   - Rows whose byte size is a multiple of 16 and whose base pointers are
+ *     16-byte aligned move as 16-byte vectors; otherwise an element-wise path
+ *     runs (same results).  Pointers must at least be aligned to their
+ *     element size (MOE_ERR_ALIGN otherwise).
+ *   - Host-side argument checks run before any HIP call and return a status
+ *     code; a non-zero return means nothing was enqueued.
+ *   - Data-dependent faults that only the device can see (an expert index
+ *     out of range, a repeated expert in one token, a map entry out of range,
+ *     bad chunk metadata, a capacity overflow) never cause an out-of-bounds
+ *     access: the offending element is skipped and, when `dev_status` is
+ *     non-NULL, the matching MOE_DEV_* bit is OR-ed into *dev_status (an int32
+ *     in device memory the caller zeroes beforehand).  Outputs are then
+ *     unspecified.
+ *   - num_tokens == 0 (or n_cap == 0) is valid: outputs that still have a
+ *     defined value (expert_offsets) are written, nothing else is touched.
+ *   - Calls on one stream are ordered; calls that write the same buffers from
+ *     different streams race.
+ */
+#ifndef MOE_PERM_H
+#define MOE_PERM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_PERM_API __attribute__((visibility("default")))
+
+/* Host-side status codes returned by every call. */
+enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    MOE_ERR_SHAPE = 2,       /* a size argument is out of range/inconsistent   */
+    MOE_ERR_ALIGN = 3,       /* a pointer is not aligned to its element size   */
+    MOE_ERR_UNSUPPORTED = 4, /* a size beyond what the kernels support         */
+    MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
+    MOE_ERR_HIP = 6          /* a kernel launch failed (hipGetLastError)       */
+};
+
+/* Device-side status bits OR-ed into *dev_status. */
+#define MOE_DEV_BAD_EXPERT 0x1 /* top-k index outside [0, num_experts)         */
+#define MOE_DEV_DUP_EXPERT 0x2 /* one expert twice in a token's top-k          */
+#define MOE_DEV_BAD_ROW 0x4    /* row_id_map / row_map entry outside its range */
+#define MOE_DEV_BAD_CHUNKS 0x8 /* negative split size or order not a permutation */
+#define MOE_DEV_OVERFLOW 0x10  /* tokens exceed n_cap or padded rows exceed out_cap */
+
+/* Largest supported sizes (MOE_ERR_UNSUPPORTED beyond). */
+#define MOE_MAX_EXPERTS 2048
+#define MOE_MAX_TOPK 64
+#define MOE_MAX_CHUNKS 2048
+
+/* Name of a host status code (static string, never NULL). */
+MOE_PERM_API const char *moe_status_string(int status);
+
+/* ------------------------------------------------------------------------ *
+ * (1) Routing row map -- stable counting sort.
+ *
+ * [TE-mask] make_row_id_map and its worked example: per expert, count the
+ * routed tokens per token block, exclusive-scan the counts in expert-major
+ * order, and give each routed (token, expert) pair the row
+ *     expert_offsets[e] + (number of tokens t' < t also routed to e).
+ * [MOE-OPS] "Routing permute / unpermute": a counting sort (histogram plus
+ * exclusive prefix sums), O(T*k).  [XTUNER]: the same rows as a stable
+ * argsort of the flattened top-k indices -- the single convention here.
+ *
+ *   topk_idx        [num_tokens][topk] int32, token t's experts in slot order;
+ *                   the experts of one token must be distinct.
+ *   row_id_map      out [num_experts][num_tokens] int32: destination row of
+ *                   (t, e), or -1 when t is not routed to e.  Rows are
+ *                   expert-major, tokens ascending inside an expert, and
+ *                   cover [0, num_tokens*topk) exactly once.
+ *   expert_offsets  out [num_experts + 1] int32: exclusive scan of the
+ *                   per-expert counts; expert_offsets[E] = num_tokens*topk.
+ *   dev_status      optional; MOE_DEV_BAD_EXPERT, MOE_DEV_DUP_EXPERT.
+ *   workspace       device scratch of at least
+ *                   moe_make_row_id_map_workspace_bytes(...) bytes, 256-byte
+ *                   aligned; contents need no initialisation.
+ * Limits: 1 <= topk <= min(num_experts, MOE_MAX_TOPK),
+ *         num_experts <= MOE_MAX_EXPERTS, num_tokens*topk < 2^31.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API size_t moe_make_row_id_map_workspace_bytes(int num_tokens, int topk,
+                                                        int num_experts);
+MOE_PERM_API int moe_make_row_id_map(const int32_t *topk_idx, int num_tokens, int topk,
+                                     int num_experts, int32_t *row_id_map,
+                                     int32_t *expert_offsets, int32_t *dev_status,
+                                     void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * (2) Permute -- gather-copy of each token row to its top-k rows.
+ *
+ * [TE-mask] _permute_kernel: a token's hidden row is stored unchanged to each
+ * destination row it is routed to; with probabilities, the slot's
+ * probability is stored at the same destination index.
+ *   out[r(t,j)][:]  = x[t][:]          (bitwise)
+ *   out_probs[r(t,j)] = probs[t][j]    (when both pointers are non-NULL)
+ * with r(t,j) = row_id_map[topk_idx[t][j]][t].
+ *
+ *   x          [num_tokens][hidden] bf16.
+ *   probs      [num_tokens][topk] fp32 or NULL.
+ *   out        [num_out_rows][hidden] bf16; num_out_rows must equal
+ *              num_tokens*topk (no token dropping).
+ *   out_probs  [num_out_rows] fp32 or NULL.
+ *   dev_status optional; MOE_DEV_BAD_EXPERT, MOE_DEV_BAD_ROW.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_permute(const void *x, const float *probs, const int32_t *topk_idx,
+                             const int32_t *row_id_map, int num_tokens, int hidden,
+                             int topk, int num_experts, int num_out_rows, void *out,
+                             float *out_probs, int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * (4) Unpermute -- token-owned, fixed-order combine.
+ *
+ * [MCORE-BI] unpermute_with_bf16_rank_partials / _rank_tree_unpermute_kernel
+ * with BF16_RANK_PARTIALS (one EP rank): each output token adds its routed
+ * rows in top-k slot order as fp32 fused multiply-adds of probability and
+ * row, starting from zero, then rounds to bf16:
+ *   acc = +0.0f; for j in 0..topk-1: acc = fmaf(probs[t][j], in[r(t,j)][h], acc)
+ *   out[t][h] = bf16_round_nearest_even(acc)
+ * probs == NULL uses unit weights (identical to plain fp32 adds).
+ * [MOE-OPS] "Why this library": a gather-add that writes each output once, no
+ * atomics.  Results are bitwise reproducible and independent of launch shape.
+ *
+ *   in         [num_in_rows][hidden] bf16, num_in_rows == num_tokens*topk.
+ *   probs      [num_tokens][topk] fp32 or NULL.
+ *   out        [num_tokens][hidden] bf16.
+ *   dev_status optional; MOE_DEV_BAD_EXPERT, MOE_DEV_BAD_ROW.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_unpermute(const void *in, const float *probs, const int32_t *topk_idx,
+                               const int32_t *row_id_map, int num_tokens, int hidden,
+                               int topk, int num_experts, int num_in_rows, void *out,
+                               int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Unpermute backward.
+ *
+ * [TE-mask] _unpermute_bwd_with_merging_probs_kernel; [MCORE-BI]
+ * _rank_tree_unpermute_bwd_kernel (one writer per permuted row):
+ *   d_in[r(t,j)][h] = bf16(fp32(d_out[t][h]) * probs[t][j])  (fp32 product,
+ *                                                            then bf16 RNE)
+ *   d_probs[t][j]   = sum_h fp32(fwd_in[r(t,j)][h]) * fp32(d_out[t][h])
+ * The order of the prob-grad sum is not fixed by the pages; here it is an
+ * fp32 blocked tree that depends only on hidden and the launch shape chosen
+ * for it, so results are bitwise reproducible.
+ * With probs == NULL, d_in[r(t,j)] = d_out[t] bitwise and d_probs must be
+ * NULL.  fwd_in may be NULL only when d_probs is NULL.
+ *
+ *   d_out   [num_tokens][hidden] bf16 (gradient of the unpermute output).
+ *   fwd_in  [num_rows][hidden] bf16 (the unpermute's forward input).
+ *   d_in    [num_rows][hidden] bf16, num_rows == num_tokens*topk.
+ *   d_probs [num_tokens][topk] fp32 or NULL.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_unpermute_bwd(const void *d_out, const void *fwd_in, const float *probs,
+                                   const int32_t *topk_idx, const int32_t *row_id_map,
+                                   int num_tokens, int hidden, int topk, int num_experts,
+                                   int num_rows, void *d_in, float *d_probs,
+                                   int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Permute backward.
+ *
+ * [TE-mask] _moe_permute_mask_map.backward: the gradient of the permute is
+ * the unweighted unpermute of the permuted gradient, and the permuted-prob
+ * gradient is gathered back to the token's slots:
+ *   d_x[t][h]     = bf16_rne(sum over j in slot order, fp32, from +0, of
+ *                            d_out[r(t,j)][h])
+ *   d_probs[t][j] = d_out_probs[r(t,j)]      (when both are non-NULL)
+ *
+ *   d_out        [num_rows][hidden] bf16, num_rows == num_tokens*topk.
+ *   d_out_probs  [num_rows] fp32 or NULL.
+ *   d_x          [num_tokens][hidden] bf16.
+ *   d_probs      [num_tokens][topk] fp32 or NULL.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_permute_bwd(const void *d_out, const float *d_out_probs,
+                                 const int32_t *topk_idx, const int32_t *row_id_map,
+                                 int num_tokens, int hidden, int topk, int num_experts,
+                                 int num_rows, void *d_x, float *d_probs,
+                                 int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * (3) Fused chunk sort-and-pad.
+ *
+ * [TE-3509] Description / Changes / Diagram: rank chunks are regrouped into
+ * expert order and each expert group is zero-padded to an alignment, in one
+ * copy that moves tokens and probabilities together; a padded
+ * destination -> source row map is kept for the restore and the backward.
+ * Chunk order and padding are explicit; routing metadata stays on the GPU;
+ * the output size is fixed by the caller so graph replays can change the
+ * routing; token counts are kernel arguments read on the device.
+ *
+ *   in           [n_cap][hidden] elements of elem_bytes (2: bf16/fp16,
+ *                4: fp32), copied bitwise.  Chunk c occupies split_sizes[c]
+ *                rows, chunks back to back in input order from row 0.
+ *   probs        [n_cap] elements of prob_bytes (2 or 4), or NULL.
+ *   split_sizes  [num_chunks] int32, device.
+ *   sorted_idx   [num_chunks] int32, device: input chunk at sorted position
+ *                q.  Positions [g*R, (g+1)*R) form group g, R =
+ *                chunks_per_group, G = num_chunks / R groups.
+ *   align        group g takes padded_g = ceil(n_g / align) * align rows
+ *                (an empty group takes none), n_g = its token count.
+ *   out          [out_cap][hidden]: group g's chunks back to back from
+ *                padded_offsets[g], then zero rows up to padded_offsets[g+1];
+ *                rows from padded_offsets[G] to out_cap are zero.
+ *   out_probs    [out_cap] or NULL (zero on padding rows).
+ *   row_map      out [out_cap] int32: source row of each destination row,
+ *                -1 for padding and tail rows.
+ *   padded_offsets out [G + 1] int32: exclusive scan of padded_g.
+ *   dev_status   optional; MOE_DEV_BAD_CHUNKS, MOE_DEV_OVERFLOW (then
+ *                row_map is all -1 and out all zero).
+ * Limits: num_chunks % chunks_per_group == 0, num_chunks <= MOE_MAX_CHUNKS,
+ *         align >= 1.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_sort_chunks_and_pad(const void *in, const void *probs, int elem_bytes,
+                                         int prob_bytes, int n_cap, int hidden,
+                                         const int32_t *split_sizes, const int32_t *sorted_idx,
+                                         int num_chunks, int chunks_per_group, int align,
+                                         int out_cap, void *out, void *out_probs,
+                                         int32_t *row_map, int32_t *padded_offsets,
+                                         int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * (3) Unpad and restore.
+ *
+ * [TE-3509] Description: padding is removed and the original order restored
+ * in one copy, driven by the saved row map:
+ *   out[row_map[d]] = in[d]   for every d with row_map[d] >= 0
+ *   out[s] = 0                for s in [sum(split_sizes), n_cap)
+ *
+ *   in        [out_cap][hidden] (elem_bytes), probs [out_cap] or NULL.
+ *   row_map   [out_cap] from moe_sort_chunks_and_pad.
+ *   split_sizes [num_chunks] device (gives the token total).
+ *   out       [n_cap][hidden], out_probs [n_cap] or NULL.
+ *   dev_status optional; MOE_DEV_BAD_ROW, MOE_DEV_BAD_CHUNKS, MOE_DEV_OVERFLOW.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_unpad_and_restore_chunks(const void *in, const void *probs,
+                                              int elem_bytes, int prob_bytes,
+                                              const int32_t *row_map,
+                                              const int32_t *split_sizes, int num_chunks,
+                                              int out_cap, int hidden, int n_cap, void *out,
+                                              void *out_probs, int32_t *dev_status,
+                                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Chunk backwards.  [TE-3509] Changes: padding is zero-filled and contributes
+ * zero gradient.
+ *   moe_sort_chunks_and_pad_bwd: gradient of the sort-and-pad w.r.t. its
+ *     input = the restore applied to the padded gradient (padding-row
+ *     gradients are dropped, rows past the token total are zero).
+ *   moe_unpad_and_restore_chunks_bwd: gradient of the restore w.r.t. the
+ *     padded buffer = the pad copy applied to the restored gradient
+ *     (padding rows get zero gradient).
+ * Arguments as in the forward calls they mirror.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_sort_chunks_and_pad_bwd(const void *d_out, const void *d_out_probs,
+                                             int elem_bytes, int prob_bytes,
+                                             const int32_t *row_map,
+                                             const int32_t *split_sizes, int num_chunks,
+                                             int out_cap, int hidden, int n_cap, void *d_in,
+                                             void *d_in_probs, int32_t *dev_status,
+                                             hipStream_t stream);
+MOE_PERM_API int moe_unpad_and_restore_chunks_bwd(const void *d_out, const void *d_out_probs,
+                                                  int elem_bytes, int prob_bytes,
+                                                  const int32_t *row_map, int out_cap,
+                                                  int hidden, int n_cap, void *d_in,
+                                                  void *d_in_probs, int32_t *dev_status,
+                                                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_PERM_H */

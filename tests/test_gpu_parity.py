@@ -1,0 +1,641 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle.
+
+Integer, index and copy results must match bit for bit, and so must the
+fixed slot-order unpermute (and the permute backward, which is the same
+combine with unit weights).  The only tolerance is the prob-grad row dot
+product, whose summation order the pages leave open: |g - ref| <= 1e-5 * S
+with S = sum_h |fwd_in[r][h] * d_out[t][h]|.
+
+Outputs are pre-filled with sentinels (bf16 0x7FC1, int -2, a NaN payload
+for fp32) so an element the kernels fail to write shows up as a mismatch.
+Small workloads are compared in full; the 16384 x 7168 workload is compared
+in full where a torch gather/scatter can express the expected result on the
+GPU, and on a seeded sample of tokens run through the oracle otherwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+S_BF16 = 0x7FC1
+S_F32 = np.array([0x7FC00123], np.uint32).view(np.float32)[0]
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import unpermute_moe_make_amd as mod
+    return mod
+
+
+# ----------------------------------------------------------------- helpers --
+
+def bits(t):
+    return workloads.bf16_bits(t.cpu()) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def sentinel_bf16(shape):
+    t = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    t.view(torch.int16).fill_(S_BF16)
+    return t
+
+
+def sentinel_f32(shape):
+    t = torch.empty(shape, dtype=torch.float32, device=DEV)
+    t.view(torch.int32).fill_(int(np.array([S_F32]).view(np.int32)[0]))
+    return t
+
+
+def sentinel_i32(shape):
+    return torch.full(shape, -2, dtype=torch.int32, device=DEV)
+
+
+def f32_bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def assert_bits_equal(got, exp, what):
+    got = np.asarray(got)
+    exp = np.asarray(exp)
+    assert got.shape == exp.shape, (what, got.shape, exp.shape)
+    if got.dtype == np.float32:
+        got, exp = f32_bits(got), f32_bits(exp)
+    bad = np.nonzero(got != exp)
+    n = bad[0].size
+    assert n == 0, f"{what}: {n} mismatches, first at {[b[:5] for b in bad]}"
+
+
+def oracle_rows(idx, row_map):
+    """r(t, j) from the oracle's row map."""
+    T, k = idx.shape
+    return row_map[idx, np.arange(T)[:, None]]
+
+
+def sub_problem(idx, sample):
+    """Top-k and a row map for a token subset whose rows are i*k + j."""
+    sidx = idx[sample]
+    s, k = sidx.shape
+    E = int(idx.max()) + 1
+    smap = np.full((E, s), -1, np.int32)
+    for i in range(s):
+        for j in range(k):
+            smap[sidx[i, j], i] = i * k + j
+    return sidx, smap
+
+
+def dprob_ok(got, fwd_rows, dy_rows, ref):
+    """|got - ref| <= 1e-5 * sum_h |a*b| per (token, slot)."""
+    a = (fwd_rows.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    b = (dy_rows.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    scale = np.einsum("tjh,th->tj", np.abs(a), np.abs(b))
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    worst = float(np.max(err / np.maximum(scale, 1e-300)))
+    assert np.all(err <= 1e-5 * scale + 1e-37), f"prob grad off by {worst:.3g} of scale"
+    return worst
+
+
+_CACHE = {}
+
+
+def routed(name):
+    if name not in _CACHE:
+        w = workloads.ROUTED[name]()
+        m_, off = oracle.row_id_map(w.topk_idx.numpy(), w.num_experts)
+        _CACHE[name] = (w, m_, off)
+    return _CACHE[name]
+
+
+def to_dev(w):
+    return (w.x.to(DEV), w.topk_idx.to(DEV), w.probs.to(DEV),
+            None if w.dy is None else w.dy.to(DEV))
+
+
+# ------------------------------------------------------------ (1) row map --
+
+@pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
+def test_row_map_configs(m, name):
+    w, ref_map, ref_off = routed(name)
+    say(f"row_map {name} T={w.T} E={w.num_experts} k={w.k}")
+    idx = w.topk_idx.to(DEV)
+    rm = sentinel_i32((w.num_experts, w.T))
+    off = sentinel_i32((w.num_experts + 1,))
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    m.moe_make_row_id_map(idx, w.num_experts, row_id_map=rm, expert_offsets=off, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert_bits_equal(rm.cpu().numpy(), ref_map, "row_id_map")
+    assert_bits_equal(off.cpu().numpy(), ref_off, "expert_offsets")
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (63, 5, 2), (64, 5, 2), (255, 8, 3), (256, 8, 3),
+                                   (257, 8, 3), (1000, 3, 3), (700, 2048, 8), (300, 64, 9),
+                                   (130, 100, 64), (5000, 1, 1), (4097, 257, 7)])
+def test_row_map_edges(m, T, E, k):
+    say(f"row_map edge T={T} E={E} k={k}")
+    w = workloads.random_routed(T, 8, E, k, seed=T * 31 + E, with_dy=False, zipf_s=0.7)
+    ref_map, ref_off = oracle.row_id_map(w.topk_idx.numpy(), E)
+    rm = sentinel_i32((E, T))
+    off = sentinel_i32((E + 1,))
+    m.moe_make_row_id_map(w.topk_idx.to(DEV), E, row_id_map=rm, expert_offsets=off)
+    assert_bits_equal(rm.cpu().numpy(), ref_map, "row_id_map")
+    assert_bits_equal(off.cpu().numpy(), ref_off, "expert_offsets")
+
+
+def test_row_map_empty(m):
+    say("row_map T=0")
+    off = sentinel_i32((9,))
+    m.moe_make_row_id_map(torch.zeros((0, 2), dtype=torch.int32, device=DEV), 8,
+                          expert_offsets=off)
+    assert_bits_equal(off.cpu().numpy(), np.zeros(9, np.int32), "expert_offsets")
+
+
+def test_row_map_bad_routing_sets_status(m):
+    say("row_map bad expert / duplicate expert")
+    idx = torch.tensor([[0, 1], [2, 9], [3, 3], [1, 0]], dtype=torch.int32, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    m.moe_make_row_id_map(idx, 4, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == m.DEV_BAD_EXPERT | m.DEV_DUP_EXPERT
+    # the permute sees the bad expert too and skips it without faulting
+    x = torch.ones(4, 16, dtype=torch.bfloat16, device=DEV)
+    rm, _ = m.moe_make_row_id_map(torch.tensor([[0, 1], [2, 3], [3, 2], [1, 0]],
+                                               dtype=torch.int32, device=DEV), 4)
+    st.zero_()
+    m.moe_permute(x, idx, rm, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & m.DEV_BAD_EXPERT
+
+
+# --------------------------------------------- (2) permute, (4) unpermute --
+
+@pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
+def test_permute_configs(m, name):
+    w, ref_map, _ = routed(name)
+    T, H, k = w.T, w.H, w.k
+    say(f"permute {name} T={T} H={H} k={k}")
+    x, idx, probs, _ = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    out = sentinel_bf16((T * k, H))
+    out_p = sentinel_f32((T * k,))
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    m.moe_permute(x, idx, rm, probs, out=out, out_probs=out_p, dev_status=st)
+    rows = torch.from_numpy(oracle_rows(w.topk_idx.numpy(), ref_map).astype(np.int64)).to(DEV)
+    exp = torch.empty_like(out)
+    exp[rows.flatten()] = x.repeat_interleave(k, dim=0)         # torch scatter, full size
+    assert torch.equal(out.view(torch.int16), exp.view(torch.int16))
+    exp_p = torch.empty_like(out_p)
+    exp_p[rows.flatten()] = probs.flatten()
+    assert torch.equal(out_p.view(torch.int32), exp_p.view(torch.int32))
+    assert int(st.item()) == 0
+    # oracle on a sample of tokens (full for the small workloads)
+    sample = np.arange(T) if T <= 4096 else np.sort(
+        np.random.default_rng(0).choice(T, 512, replace=False))
+    if T <= 4096:
+        o, op = oracle.permute(workloads.bf16_bits(w.x), w.probs.numpy(), w.topk_idx.numpy(),
+                               ref_map)
+        assert_bits_equal(bits(out), o, "permute")
+        assert_bits_equal(out_p.cpu().numpy(), op, "permuted probs")
+    else:
+        r = oracle_rows(w.topk_idx.numpy(), ref_map)[sample].flatten()
+        sidx, smap = sub_problem(w.topk_idx.numpy(), sample)
+        o, op = oracle.permute(workloads.bf16_bits(w.x[sample]), w.probs.numpy()[sample], sidx,
+                               smap)
+        assert_bits_equal(bits(out[torch.from_numpy(r).to(DEV)]), o, "permute sample")
+        assert_bits_equal(out_p.cpu().numpy()[r], op, "permuted probs sample")
+
+
+@pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
+@pytest.mark.parametrize("weighted", [True, False])
+def test_unpermute_configs(m, name, weighted):
+    w, ref_map, _ = routed(name)
+    T, H, k = w.T, w.H, w.k
+    say(f"unpermute {name} weighted={weighted}")
+    _, idx, probs, _ = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    P = workloads.random_rows(T * k, H, seed=77, device=DEV)
+    out = sentinel_bf16((T, H))
+    m.moe_unpermute(P, idx, rm, probs if weighted else None, out=out)
+    p_np = w.probs.numpy() if weighted else None
+    if T <= 4096:
+        ref = oracle.unpermute(bits(P), p_np, w.topk_idx.numpy(), ref_map)
+        assert_bits_equal(bits(out), ref, "unpermute")
+    else:
+        sample = np.sort(np.random.default_rng(1).choice(T, 512, replace=False))
+        r = oracle_rows(w.topk_idx.numpy(), ref_map)[sample].flatten()
+        sidx, smap = sub_problem(w.topk_idx.numpy(), sample)
+        rows = bits(P[torch.from_numpy(r).to(DEV)])
+        ref = oracle.unpermute(rows, None if p_np is None else p_np[sample], sidx, smap)
+        assert_bits_equal(bits(out)[sample], ref, "unpermute sample")
+
+
+@pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
+def test_unpermute_bwd_configs(m, name):
+    w, ref_map, _ = routed(name)
+    T, H, k = w.T, w.H, w.k
+    say(f"unpermute_bwd {name}")
+    _, idx, probs, dy = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    fwd_in = workloads.random_rows(T * k, H, seed=78, device=DEV)
+    d_in = sentinel_bf16((T * k, H))
+    d_p = sentinel_f32((T, k))
+    m.moe_unpermute_bwd(dy, idx, rm, probs, fwd_in, d_in=d_in, d_probs=d_p)
+    r_all = oracle_rows(w.topk_idx.numpy(), ref_map)
+    sample = np.arange(T) if T <= 4096 else np.sort(
+        np.random.default_rng(2).choice(T, 384, replace=False))
+    r = r_all[sample].flatten()
+    sidx, smap = sub_problem(w.topk_idx.numpy(), sample)
+    fin_rows = bits(fwd_in[torch.from_numpy(r).to(DEV)])
+    dy_rows = workloads.bf16_bits(w.dy[sample])
+    ref_in, ref_p = oracle.unpermute_bwd(dy_rows, fin_rows, w.probs.numpy()[sample], sidx, smap)
+    if T <= 4096:
+        # every row of d_in, in the oracle's own layout
+        full_in, _ = oracle.unpermute_bwd(workloads.bf16_bits(w.dy), bits(fwd_in),
+                                          w.probs.numpy(), w.topk_idx.numpy(), ref_map)
+        assert_bits_equal(bits(d_in), full_in, "unpermute_bwd act grad")
+    else:
+        assert_bits_equal(bits(d_in[torch.from_numpy(r).to(DEV)]), ref_in,
+                          "unpermute_bwd act grad sample")
+    got_p = d_p.cpu().numpy()[sample]
+    worst = dprob_ok(got_p, fin_rows.reshape(len(sample), k, H), dy_rows, ref_p)
+    say(f"  prob-grad worst error / scale = {worst:.3g}")
+    # unweighted: plain scatter of d_out
+    d_in0 = sentinel_bf16((T * k, H))
+    m.moe_unpermute_bwd(dy, idx, rm, None, None, d_in=d_in0)
+    exp = torch.empty_like(d_in0)
+    exp[torch.from_numpy(r_all.flatten().astype(np.int64)).to(DEV)] = \
+        dy.repeat_interleave(k, dim=0)
+    assert torch.equal(d_in0.view(torch.int16), exp.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
+def test_permute_bwd_configs(m, name):
+    w, ref_map, _ = routed(name)
+    T, H, k = w.T, w.H, w.k
+    say(f"permute_bwd {name}")
+    _, idx, _, _ = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    dP = workloads.random_rows(T * k, H, seed=79, device=DEV)
+    dpp = torch.randn(T * k, generator=torch.Generator().manual_seed(80)).to(DEV)
+    d_x = sentinel_bf16((T, H))
+    d_p = sentinel_f32((T, k))
+    m.moe_permute_bwd(dP, idx, rm, dpp, d_x=d_x, d_probs=d_p)
+    if T <= 4096:
+        ref_x, ref_p = oracle.permute_bwd(bits(dP), dpp.cpu().numpy(), w.topk_idx.numpy(),
+                                          ref_map)
+        assert_bits_equal(bits(d_x), ref_x, "permute_bwd")
+        assert_bits_equal(d_p.cpu().numpy(), ref_p, "permute_bwd probs")
+    else:
+        sample = np.sort(np.random.default_rng(3).choice(T, 512, replace=False))
+        r = oracle_rows(w.topk_idx.numpy(), ref_map)[sample].flatten()
+        sidx, smap = sub_problem(w.topk_idx.numpy(), sample)
+        ref_x, ref_p = oracle.permute_bwd(bits(dP[torch.from_numpy(r).to(DEV)]),
+                                          dpp.cpu().numpy()[r], sidx, smap)
+        assert_bits_equal(bits(d_x)[sample], ref_x, "permute_bwd sample")
+        assert_bits_equal(d_p.cpu().numpy()[sample], ref_p, "permute_bwd probs sample")
+
+
+@pytest.mark.parametrize("T,H,E,k", [(1, 8, 2, 1), (37, 7, 9, 3), (100, 24, 16, 2),
+                                     (64, 64, 8, 9), (40, 136, 80, 64), (33, 2056, 12, 5),
+                                     (20, 7168, 16, 4), (9, 20480, 8, 8), (17, 20481, 4, 2),
+                                     (300, 512, 32, 1)])
+def test_row_kernels_edges(m, T, H, E, k):
+    say(f"row kernels edge T={T} H={H} E={E} k={k}")
+    w = workloads.random_routed(T, H, E, k, seed=H + k)
+    ref_map, _ = oracle.row_id_map(w.topk_idx.numpy(), E)
+    x, idx, probs, dy = to_dev(w)
+    rm, _ = m.moe_make_row_id_map(idx, E)
+    torch.cuda.synchronize()
+    assert_bits_equal(rm.cpu().numpy(), ref_map, "row_id_map")
+    xb, pb, ib = workloads.bf16_bits(w.x), w.probs.numpy(), w.topk_idx.numpy()
+    out, out_p = m.moe_permute(x, idx, rm, probs, out=sentinel_bf16((T * k, H)),
+                               out_probs=sentinel_f32((T * k,)))
+    o, op = oracle.permute(xb, pb, ib, ref_map)
+    assert_bits_equal(bits(out), o, "permute")
+    assert_bits_equal(out_p.cpu().numpy(), op, "permuted probs")
+    P = workloads.random_rows(T * k, H, seed=5, device=DEV)
+    y = m.moe_unpermute(P, idx, rm, probs, out=sentinel_bf16((T, H)))
+    assert_bits_equal(bits(y), oracle.unpermute(bits(P), pb, ib, ref_map), "unpermute")
+    d_in, d_p = m.moe_unpermute_bwd(dy, idx, rm, probs, P, d_in=sentinel_bf16((T * k, H)),
+                                    d_probs=sentinel_f32((T, k)))
+    ref_in, ref_p = oracle.unpermute_bwd(workloads.bf16_bits(w.dy), bits(P), pb, ib, ref_map)
+    assert_bits_equal(bits(d_in), ref_in, "unpermute_bwd")
+    rows = oracle_rows(ib, ref_map)
+    dprob_ok(d_p.cpu().numpy(), bits(P)[rows], workloads.bf16_bits(w.dy), ref_p)
+    dpp = torch.randn(T * k, generator=torch.Generator().manual_seed(3)).to(DEV)
+    d_x, d_pp = m.moe_permute_bwd(P, idx, rm, dpp, d_x=sentinel_bf16((T, H)),
+                                  d_probs=sentinel_f32((T, k)))
+    rx, rp = oracle.permute_bwd(bits(P), dpp.cpu().numpy(), ib, ref_map)
+    assert_bits_equal(bits(d_x), rx, "permute_bwd")
+    assert_bits_equal(d_pp.cpu().numpy(), rp, "permute_bwd probs")
+
+
+def test_row_kernels_misaligned_views(m):
+    """Row pointers that are 2- but not 16-byte aligned take the element path."""
+    T, H, E, k = 50, 64, 8, 3
+    say("row kernels misaligned views")
+    w = workloads.random_routed(T, H, E, k, seed=9)
+    ref_map, _ = oracle.row_id_map(w.topk_idx.numpy(), E)
+    idx = w.topk_idx.to(DEV)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    xbuf = torch.empty(T * H + 1, dtype=torch.bfloat16, device=DEV)
+    x = xbuf[1:].view(T, H)
+    x.copy_(w.x.to(DEV))
+    obuf = sentinel_bf16((T * k * H + 1,))
+    out = obuf[1:].view(T * k, H)
+    m.moe_permute(x, idx, rm, out=out)
+    o, _ = oracle.permute(workloads.bf16_bits(w.x), None, w.topk_idx.numpy(), ref_map)
+    assert_bits_equal(bits(out), o, "permute misaligned")
+    ybuf = sentinel_bf16((T * H + 1,))
+    y = ybuf[1:].view(T, H)
+    m.moe_unpermute(out, idx, rm, w.probs.to(DEV), out=y)
+    assert_bits_equal(bits(y), oracle.unpermute(o, w.probs.numpy(), w.topk_idx.numpy(), ref_map),
+                      "unpermute misaligned")
+
+
+def test_roundtrip_k1_identity(m):
+    say("permute -> unpermute, k=1, unit weights")
+    w = workloads.random_routed(1000, 2048, 16, 1, seed=4)
+    x, idx, _, _ = to_dev(w)
+    rm, _ = m.moe_make_row_id_map(idx, 16)
+    P, _ = m.moe_permute(x, idx, rm)
+    y = m.moe_unpermute(P, idx, rm)
+    assert torch.equal(y.view(torch.int16), x.view(torch.int16))
+
+
+def test_bitwise_repeatable(m):
+    say("repeatability of the prob-grad reduction and the combine")
+    w, ref_map, _ = routed("finegrain")
+    _, idx, probs, dy = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    P = workloads.random_rows(w.T * w.k, w.H, seed=11, device=DEV)
+    first = None
+    for _ in range(5):
+        y = m.moe_unpermute(P, idx, rm, probs)
+        d_in, d_p = m.moe_unpermute_bwd(dy, idx, rm, probs, P)
+        cur = (y.view(torch.int16).clone(), d_in.view(torch.int16).clone(),
+               d_p.view(torch.int32).clone())
+        if first is None:
+            first = cur
+        else:
+            for a, b in zip(first, cur):
+                assert torch.equal(a, b)
+
+
+def test_graph_replay_routing(m):
+    """Map + permute + unpermute captured once, replayed with new routings."""
+    T, H, E, k = 1024, 1024, 32, 4
+    say("graph replay, routing")
+    idx_s = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    probs_s = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    x_s = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    rm = torch.empty((E, T), dtype=torch.int32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(m.moe_make_row_id_map_workspace_bytes(T, k, E), dtype=torch.uint8,
+                     device=DEV)
+    P = torch.empty((T * k, H), dtype=torch.bfloat16, device=DEV)
+    pp = torch.empty(T * k, dtype=torch.float32, device=DEV)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        m.moe_make_row_id_map(idx_s, E, row_id_map=rm, expert_offsets=off, workspace=ws)
+        m.moe_permute(x_s, idx_s, rm, probs_s, out=P, out_probs=pp)
+        m.moe_unpermute(P, idx_s, rm, probs_s, out=y)
+
+    w0 = workloads.random_routed(T, H, E, k, seed=1000, with_dy=False)
+    idx_s.copy_(w0.topk_idx)
+    probs_s.copy_(w0.probs)
+    x_s.copy_(w0.x)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(8):
+        w = workloads.random_routed(T, H, E, k, seed=1001 + rep, with_dy=False,
+                                    zipf_s=0.3 * rep)
+        idx_s.copy_(w.topk_idx)
+        probs_s.copy_(w.probs)
+        x_s.copy_(w.x)
+        P.view(torch.int16).fill_(S_BF16)
+        g.replay()
+        torch.cuda.synchronize()
+        ref_map, ref_off = oracle.row_id_map(w.topk_idx.numpy(), E)
+        assert_bits_equal(rm.cpu().numpy(), ref_map, f"replay {rep} row map")
+        assert_bits_equal(off.cpu().numpy(), ref_off, f"replay {rep} offsets")
+        o, _ = oracle.permute(workloads.bf16_bits(w.x), None, w.topk_idx.numpy(), ref_map)
+        assert_bits_equal(bits(P), o, f"replay {rep} permute")
+        ref_y = oracle.unpermute(o, w.probs.numpy(), w.topk_idx.numpy(), ref_map)
+        assert_bits_equal(bits(y), ref_y, f"replay {rep} unpermute")
+
+
+# ------------------------------------------------ (3) chunk sort / restore --
+
+def _chunk_ref(cw, sizes=None):
+    s = (cw.split_sizes if sizes is None else sizes).numpy()
+    xb = workloads.bf16_bits(cw.x) if cw.x.dtype == torch.bfloat16 else cw.x.numpy()
+    return oracle.sort_chunks_and_pad(xb, cw.probs.numpy(), s, cw.sorted_idx.numpy(),
+                                      cw.chunks_per_group, cw.align, cw.out_cap)
+
+
+def _run_chunks(m, cw, x, probs, sizes, order, st=None):
+    out = sentinel_bf16((cw.out_cap, cw.H)) if x.dtype == torch.bfloat16 else \
+        torch.full((cw.out_cap, cw.H), float("nan"), dtype=x.dtype, device=DEV)
+    out_p = sentinel_f32((cw.out_cap,)) if probs.dtype == torch.float32 else \
+        torch.full((cw.out_cap,), float("nan"), dtype=probs.dtype, device=DEV)
+    rm = sentinel_i32((cw.out_cap,))
+    off = sentinel_i32((cw.C // cw.chunks_per_group + 1,))
+    m.moe_sort_chunks_and_pad(x, sizes, order, cw.chunks_per_group, cw.align, cw.out_cap, probs,
+                              out=out, out_probs=out_p, row_map=rm, padded_offsets=off,
+                              dev_status=st)
+    return out, out_p, rm, off
+
+
+def _raw(t):
+    t = t.cpu()
+    if t.dtype == torch.bfloat16 or t.dtype == torch.float16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.view(torch.int32).numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("name", ["chunks8k", "chunks32k"])
+def test_chunks_configs(m, name):
+    cw = workloads.CHUNKED[name]()
+    say(f"sort_chunks_and_pad + restore {name} N={cw.N_cap} cap={cw.out_cap}")
+    x, probs = cw.x.to(DEV), cw.probs.to(DEV)
+    sizes, order = cw.split_sizes.to(DEV), cw.sorted_idx.to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, out_p, rm, off = _run_chunks(m, cw, x, probs, sizes, order, st)
+    r_out, r_p, r_rm, r_off = _chunk_ref(cw)
+    assert int(st.item()) == 0
+    assert_bits_equal(rm.cpu().numpy(), r_rm, "row_map")
+    assert_bits_equal(off.cpu().numpy(), r_off, "padded_offsets")
+    assert_bits_equal(_raw(out), r_out, "padded tokens")
+    assert_bits_equal(out_p.cpu().numpy(), r_p, "padded probs")
+    back = sentinel_bf16((cw.N_cap, cw.H))
+    back_p = sentinel_f32((cw.N_cap,))
+    m.moe_unpad_and_restore_chunks(out, rm, sizes, cw.N_cap, out_p, out=back, out_probs=back_p,
+                                   dev_status=st)
+    ref_b, ref_bp = oracle.unpad_and_restore_chunks(r_out, r_p, r_rm, cw.split_sizes.numpy(),
+                                                    cw.N_cap)
+    assert_bits_equal(_raw(back), ref_b, "restored tokens")
+    assert_bits_equal(back_p.cpu().numpy(), ref_bp, "restored probs")
+    assert torch.equal(back.view(torch.int16), x.view(torch.int16))   # restore . pad = id
+    # backwards: gradients of random bits
+    gpad = workloads.random_rows(cw.out_cap, cw.H, seed=3, device=DEV)
+    gpp = torch.rand(cw.out_cap, generator=torch.Generator().manual_seed(4)).to(DEV)
+    d_in, d_inp = m.moe_sort_chunks_and_pad_bwd(gpad, rm, sizes, cw.N_cap, gpp,
+                                                d_in=sentinel_bf16((cw.N_cap, cw.H)),
+                                                d_in_probs=sentinel_f32((cw.N_cap,)))
+    rd, rdp = oracle.sort_chunks_and_pad_bwd(bits(gpad), gpp.cpu().numpy(), r_rm,
+                                             cw.split_sizes.numpy(), cw.N_cap)
+    assert_bits_equal(bits(d_in), rd, "sort_and_pad bwd")
+    assert_bits_equal(d_inp.cpu().numpy(), rdp, "sort_and_pad bwd probs")
+    grest = workloads.random_rows(cw.N_cap, cw.H, seed=5, device=DEV)
+    d_pad, d_padp = m.moe_unpad_and_restore_chunks_bwd(grest, rm, cw.out_cap, probs,
+                                                       d_in=sentinel_bf16((cw.out_cap, cw.H)),
+                                                       d_in_probs=sentinel_f32((cw.out_cap,)))
+    rp_, rpp = oracle.unpad_and_restore_chunks_bwd(bits(grest), cw.probs.numpy(), r_rm,
+                                                   cw.out_cap)
+    assert_bits_equal(bits(d_pad), rp_, "restore bwd")
+    assert_bits_equal(d_padp.cpu().numpy(), rpp, "restore bwd probs")
+    assert int(st.item()) == 0
+
+
+@pytest.mark.parametrize("case", ["fp32_tokens", "fp16_probs", "odd_hidden", "align1_identity",
+                                  "empty_group", "short_total", "big_cap", "all_empty"])
+def test_chunk_edges(m, case):
+    say(f"chunk edge {case}")
+    kw = dict(N=3000, seed=50, H=256, num_ranks=4, num_experts=6, align=16, num_empty=5)
+    if case == "fp32_tokens":
+        kw["dtype"] = torch.float32
+    if case == "odd_hidden":
+        kw["H"] = 37
+    cw = workloads.chunked(**kw)
+    sizes = cw.split_sizes.clone()
+    if case == "align1_identity":
+        cw.align = 1
+        cw.sorted_idx = torch.arange(cw.C, dtype=torch.int32)
+        cw.out_cap = cw.N_cap
+    if case == "empty_group":
+        order = cw.sorted_idx
+        for q in range(4, 8):            # every chunk of group 1 empty
+            sizes[order[q]] = 0
+        sizes[order[0]] += cw.N_cap - int(sizes.sum())
+    if case == "short_total":
+        sizes = workloads.chunk_sizes(2000, 4, 6, 5, torch.Generator().manual_seed(1))
+    if case == "big_cap":
+        cw.out_cap += 777
+    if case == "all_empty":
+        sizes = torch.zeros_like(sizes)
+    cw.split_sizes = sizes
+    probs = cw.probs.to(torch.float16) if case == "fp16_probs" else cw.probs
+    cw.probs = probs
+    x = cw.x.to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, out_p, rm, off = _run_chunks(m, cw, x, probs.to(DEV), sizes.to(DEV),
+                                      cw.sorted_idx.to(DEV), st)
+    xr = _raw(cw.x)
+    pr = _raw(probs)
+    r_out, r_p, r_rm, r_off = oracle.sort_chunks_and_pad(
+        xr, pr, sizes.numpy(), cw.sorted_idx.numpy(), cw.chunks_per_group, cw.align,
+        cw.out_cap)
+    assert int(st.item()) == 0
+    assert_bits_equal(rm.cpu().numpy(), r_rm, "row_map")
+    assert_bits_equal(off.cpu().numpy(), r_off, "padded_offsets")
+    assert_bits_equal(_raw(out), r_out, "padded tokens")
+    assert_bits_equal(_raw(out_p), r_p, "padded probs")
+    back, back_p = m.moe_unpad_and_restore_chunks(out, rm, sizes.to(DEV), cw.N_cap, out_p)
+    ref_b, ref_bp = oracle.unpad_and_restore_chunks(r_out, r_p, r_rm, sizes.numpy(), cw.N_cap)
+    assert_bits_equal(_raw(back), ref_b, "restored tokens")
+    assert_bits_equal(_raw(back_p), ref_bp, "restored probs")
+
+
+def test_chunk_bad_metadata_sets_status(m):
+    say("chunk bad metadata")
+    cw = workloads.chunked(1000, seed=51, H=64, num_ranks=2, num_experts=4, align=8,
+                           num_empty=1)
+    x, probs = cw.x.to(DEV), cw.probs.to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bad_order = cw.sorted_idx.clone()
+    bad_order[1] = bad_order[0]                        # not a permutation
+    out, out_p, rm, off = _run_chunks(m, cw, x, probs, cw.split_sizes.to(DEV),
+                                      bad_order.to(DEV), st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & m.DEV_BAD_CHUNKS
+    assert bool((rm == -1).all()) and bool((out.view(torch.int16) == 0).all())
+    st.zero_()
+    big = cw.split_sizes.clone()
+    big[0] += 5                                         # tokens exceed the buffer
+    _run_chunks(m, cw, x, probs, big.to(DEV), cw.sorted_idx.to(DEV), st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & m.DEV_OVERFLOW
+    st.zero_()
+    small_cap = workloads.Chunked(cw.name, cw.x, cw.probs, cw.split_sizes, cw.sorted_idx,
+                                  cw.chunks_per_group, cw.align, 512)
+    _run_chunks(m, small_cap, x, probs, cw.split_sizes.to(DEV), cw.sorted_idx.to(DEV), st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & m.DEV_OVERFLOW
+
+
+def test_chunk_graph_replay(m):
+    """Sort-and-pad + restore captured once at the 32768-token size, replayed
+    with eight different split-size draws at fixed buffer sizes."""
+    cw = workloads.chunks32k(with_replays=True)
+    say("chunk graph replay 32768 tokens, 8 routings")
+    x, probs = cw.x.to(DEV), cw.probs.to(DEV)
+    sizes_s = cw.split_sizes.to(DEV)
+    order = cw.sorted_idx.to(DEV)
+    G = cw.C // cw.chunks_per_group
+    out = torch.empty((cw.out_cap, cw.H), dtype=torch.bfloat16, device=DEV)
+    out_p = torch.empty(cw.out_cap, dtype=torch.float32, device=DEV)
+    rm = torch.empty(cw.out_cap, dtype=torch.int32, device=DEV)
+    off = torch.empty(G + 1, dtype=torch.int32, device=DEV)
+    back = torch.empty((cw.N_cap, cw.H), dtype=torch.bfloat16, device=DEV)
+    back_p = torch.empty(cw.N_cap, dtype=torch.float32, device=DEV)
+
+    def step():
+        m.moe_sort_chunks_and_pad(x, sizes_s, order, cw.chunks_per_group, cw.align, cw.out_cap,
+                                  probs, out=out, out_probs=out_p, row_map=rm,
+                                  padded_offsets=off)
+        m.moe_unpad_and_restore_chunks(out, rm, sizes_s, cw.N_cap, out_p, out=back,
+                                       out_probs=back_p)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    xb = workloads.bf16_bits(cw.x)
+    for rep, sizes in enumerate(cw.replays):
+        sizes_s.copy_(sizes)
+        out.view(torch.int16).fill_(S_BF16)
+        back.view(torch.int16).fill_(S_BF16)
+        g.replay()
+        torch.cuda.synchronize()
+        r_out, r_p, r_rm, r_off = oracle.sort_chunks_and_pad(
+            xb, cw.probs.numpy(), sizes.numpy(), cw.sorted_idx.numpy(), cw.chunks_per_group,
+            cw.align, cw.out_cap)
+        assert_bits_equal(rm.cpu().numpy(), r_rm, f"replay {rep} row_map")
+        assert_bits_equal(off.cpu().numpy(), r_off, f"replay {rep} offsets")
+        assert_bits_equal(bits(out), r_out, f"replay {rep} padded")
+        assert_bits_equal(out_p.cpu().numpy(), r_p, f"replay {rep} padded probs")
+        ref_b, ref_bp = oracle.unpad_and_restore_chunks(r_out, r_p, r_rm, sizes.numpy(),
+                                                        cw.N_cap)
+        assert_bits_equal(bits(back), ref_b, f"replay {rep} restored")
+        assert_bits_equal(back_p.cpu().numpy(), ref_bp, f"replay {rep} restored probs")

@@ -1,0 +1,33 @@
+"""MI355X-native MoE token permute / unpermute path.
+
+Hand-written HIP kernels for gfx950 behind a C ABI (include/moe_perm.h),
+with a thin ctypes binding whose functions carry the C names:
+
+  moe_make_row_id_map                 stable counting-sort routing row map
+  moe_permute / moe_permute_bwd       row scatter-copy and its gradient
+  moe_unpermute / moe_unpermute_bwd   fixed slot-order FMA combine, gradient
+  moe_sort_chunks_and_pad(_bwd)       fused chunk regroup + zero padding
+  moe_unpad_and_restore_chunks(_bwd)  the matching restore
+
+Importing the package loads libmoeperm.so and fails loudly if it is missing.
+"""
+from ._binding import (  # noqa: F401
+    DEV_BAD_CHUNKS,
+    DEV_BAD_EXPERT,
+    DEV_BAD_ROW,
+    DEV_DUP_EXPERT,
+    DEV_OVERFLOW,
+    EXPORTED,
+    MoeError,
+    library_path,
+    moe_make_row_id_map,
+    moe_make_row_id_map_workspace_bytes,
+    moe_permute,
+    moe_permute_bwd,
+    moe_sort_chunks_and_pad,
+    moe_sort_chunks_and_pad_bwd,
+    moe_unpad_and_restore_chunks,
+    moe_unpad_and_restore_chunks_bwd,
+    moe_unpermute,
+    moe_unpermute_bwd,
+)

@@ -1,0 +1,80 @@
+// Device helpers shared by the gfx950 kernels of the MoE permute library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_perm.h"
+
+namespace moe {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// bf16 -> fp32 is exact: the bf16 pattern is the top half of the binary32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_one(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, IEEE round to nearest, ties to even, on the 16 discarded
+// bits (adding 0x7fff plus the kept lsb carries exactly when the discarded
+// part is above half, or equal to half with an odd kept part).  NaN keeps
+// its sign and upper payload and gets the quiet bit.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rounded;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// A unit of a bf16 row: 8 elements in a 16-byte vector, or 1 element.
+template <int EPV> struct Bf16Unit;
+
+template <> struct Bf16Unit<8> {
+  using T = uint4;
+  __device__ __forceinline__ static void unpack(const uint4 &v, float *f) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  }
+  __device__ __forceinline__ static uint4 pack(const float *f) {
+    uint4 r;
+    r.x = pack_bf16x2(f[0], f[1]);
+    r.y = pack_bf16x2(f[2], f[3]);
+    r.z = pack_bf16x2(f[4], f[5]);
+    r.w = pack_bf16x2(f[6], f[7]);
+    return r;
+  }
+  __device__ __forceinline__ static uint4 zero() { return make_uint4(0u, 0u, 0u, 0u); }
+};
+
+template <> struct Bf16Unit<1> {
+  using T = uint16_t;
+  __device__ __forceinline__ static void unpack(const uint16_t &v, float *f) { f[0] = bf16_one(v); }
+  __device__ __forceinline__ static uint16_t pack(const float *f) {
+    return (uint16_t)f32_to_bf16(f[0]);
+  }
+  __device__ __forceinline__ static uint16_t zero() { return 0; }
+};
+
+template <typename U> __device__ __forceinline__ U zero_unit();
+template <> __device__ __forceinline__ uint4 zero_unit<uint4>() { return make_uint4(0u, 0u, 0u, 0u); }
+template <> __device__ __forceinline__ uint32_t zero_unit<uint32_t>() { return 0u; }
+template <> __device__ __forceinline__ uint16_t zero_unit<uint16_t>() { return 0; }
+
+// OR status bits into the caller's device status word (vector atomic).
+__device__ __forceinline__ void report(int32_t *status, int bits) {
+  if (status != nullptr && bits != 0) atomicOr(status, bits);
+}
+
+// Wave-wide fp32 sum by butterfly exchanges; every lane gets the total.
+// The exchange pattern is fixed, so the result is reproducible.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,459 @@
+// Token-row kernels: permute (row scatter-copy), the fixed-order combine
+// (unpermute, and permute backward), and the unpermute backward.
+//
+// gfx950 design.  One workgroup owns one token (and, for very long rows, a
+// slice of it: grid.y).  The first `k` lanes resolve the token's k
+// destination rows r_j = row_id_map[topk_idx[t][j]][t] (and its k weights)
+// into LDS with two parallel loads; meanwhile every lane has already issued
+// its loads of the token's own row where the kernel needs it.  Each lane then
+// moves VPT 16-byte vectors per row, all loads of a lane in flight before
+// its first store, so a wave keeps VPT*k*1 KiB outstanding.  Row offsets are
+// 64-bit.  There is no LDS tiling of the rows themselves: each byte is read
+// once and written once, and HBM bandwidth is the bound.
+//
+// Numerics of the combine (Megatron-core batch_invariant,
+// unpermute_with_bf16_rank_partials): per element acc = +0, then
+// acc = fmaf(p_j, x_j, acc) for j = 0..k-1 in slot order, then one
+// round-to-nearest-even to bf16.  The chain is per element, so the result
+// does not depend on the launch shape.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxTopk = MOE_MAX_TOPK;
+constexpr int kRowThreads = 512;  // largest row workgroup (keeps 256 VGPRs per lane available)
+
+// Resolve the token's slots into LDS.  Returns status bits of this lane.
+__device__ __forceinline__ int resolve_slots(const int32_t *__restrict__ topk_idx,
+                                             const int32_t *__restrict__ row_id_map, int t,
+                                             int T, int k, int E, int n_rows,
+                                             int64_t *__restrict__ srow) {
+  int bad = 0;
+  const int j = threadIdx.x;
+  if (j < k) {
+    const int e = topk_idx[(int64_t)t * k + j];
+    int64_t r = -1;
+    if ((unsigned)e >= (unsigned)E) {
+      bad |= MOE_DEV_BAD_EXPERT;
+    } else {
+      const int rr = row_id_map[(int64_t)e * T + t];
+      if ((unsigned)rr >= (unsigned)n_rows)
+        bad |= MOE_DEV_BAD_ROW;
+      else
+        r = rr;
+    }
+    srow[j] = r;
+  }
+  return bad;
+}
+
+// ---------------------------------------------------------------- permute --
+
+template <typename U, int VPT>
+__global__ __launch_bounds__(kRowThreads) void permute_kernel(
+    const U *__restrict__ x, const float *__restrict__ probs,
+    const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
+    int64_t V, int k, int E, int n_rows, U *__restrict__ out, float *__restrict__ out_probs,
+    int32_t *__restrict__ dev_status) {
+  __shared__ int64_t srow[kMaxTopk];
+  const int t = blockIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
+
+  // The token's own row: issue the loads before resolving the slots.
+  U v[VPT];
+  const U *xr = x + (int64_t)t * V;
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = c0 + (int64_t)i * blockDim.x;
+    if (c < V) v[i] = xr[c];
+  }
+  const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
+  if (blockIdx.y == 0 && threadIdx.x < k) {
+    report(dev_status, bad);
+    const int64_t r = srow[threadIdx.x];
+    if (r >= 0 && out_probs != nullptr) out_probs[r] = probs[(int64_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+
+  for (int j = 0; j < k; j++) {
+    const int64_t r = srow[j];
+    if (r < 0) continue;
+    U *orow = out + r * V;
+#pragma unroll
+    for (int i = 0; i < VPT; i++) {
+      const int64_t c = c0 + (int64_t)i * blockDim.x;
+      if (c < V) orow[c] = v[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine --
+
+// out[t] = bf16(fma chain over slots of p_j * in[r_j]); probs == NULL -> 1.
+// KB = slots loaded per batch (all of them when k <= 8).  Optionally gathers
+// gather_dst[t][j] = gather_src[r_j] (permute backward of the probs).
+template <int EPV, int VPT, int KB>
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(
+    const typename Bf16Unit<EPV>::T *__restrict__ in, const float *__restrict__ probs,
+    const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
+    int64_t V, int k, int E, int n_rows, typename Bf16Unit<EPV>::T *__restrict__ out,
+    const float *__restrict__ gather_src, float *__restrict__ gather_dst,
+    int32_t *__restrict__ dev_status) {
+  using Unit = Bf16Unit<EPV>;
+  using U = typename Unit::T;
+  __shared__ int64_t srow[kMaxTopk];
+  __shared__ float sp[kMaxTopk];
+  const int t = blockIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
+
+  const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
+  if (threadIdx.x < k) {
+    sp[threadIdx.x] = probs != nullptr ? probs[(int64_t)t * k + threadIdx.x] : 1.0f;
+    if (blockIdx.y == 0) {
+      report(dev_status, bad);
+      if (gather_dst != nullptr) {
+        const int64_t r = srow[threadIdx.x];
+        gather_dst[(int64_t)t * k + threadIdx.x] = r >= 0 ? gather_src[r] : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+
+  float acc[VPT][EPV];
+#pragma unroll
+  for (int i = 0; i < VPT; i++)
+#pragma unroll
+    for (int e = 0; e < EPV; e++) acc[i][e] = 0.0f;
+
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    U vals[KB][VPT];
+    // All loads of the batch first.
+#pragma unroll
+    for (int jj = 0; jj < KB; jj++) {
+      const int j = j0 + jj;
+      const int64_t r = (j < k) ? srow[j] : -1;
+#pragma unroll
+      for (int i = 0; i < VPT; i++) {
+        const int64_t c = c0 + (int64_t)i * blockDim.x;
+        vals[jj][i] = (r >= 0 && c < V) ? in[r * V + c] : Unit::zero();
+      }
+    }
+    // Then the fused multiply-adds, strictly in slot order.
+#pragma unroll
+    for (int jj = 0; jj < KB; jj++) {
+      const int j = j0 + jj;
+      if (j < k) {
+        const float p = sp[j];
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+          float f[EPV];
+          Unit::unpack(vals[jj][i], f);
+#pragma unroll
+          for (int e = 0; e < EPV; e++) acc[i][e] = __builtin_fmaf(p, f[e], acc[i][e]);
+        }
+      }
+    }
+  }
+
+  U *orow = out + (int64_t)t * V;
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = c0 + (int64_t)i * blockDim.x;
+    if (c < V) orow[c] = Unit::pack(acc[i]);
+  }
+}
+
+// ----------------------------------------------------- unpermute backward --
+
+// d_in[r_j] = bf16(fp32(d_out[t]) * p_j); d_probs[t][j] = <fwd_in[r_j], d_out[t]>.
+// A workgroup walks its row slice in passes of blockDim*VPT units.  When
+// d_probs is written the grid must not split rows (gridDim.y == 1), so the
+// workgroup sees the whole row and reduces each slot's dot product itself.
+template <int EPV, int VPT, int KB>
+__global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
+    const typename Bf16Unit<EPV>::T *__restrict__ d_out,
+    const typename Bf16Unit<EPV>::T *__restrict__ fwd_in, const float *__restrict__ probs,
+    const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
+    int64_t V, int k, int E, int n_rows, typename Bf16Unit<EPV>::T *__restrict__ d_in,
+    float *__restrict__ d_probs, int32_t *__restrict__ dev_status) {
+  using Unit = Bf16Unit<EPV>;
+  using U = typename Unit::T;
+  __shared__ int64_t srow[kMaxTopk];
+  __shared__ float sp[kMaxTopk];
+  __shared__ float sred[kRowThreads / kWave][KB];
+  const int t = blockIdx.x;
+  const int64_t pass = (int64_t)blockDim.x * VPT;
+  const int64_t stride = pass * gridDim.y;
+  const int64_t cfirst = (int64_t)blockIdx.y * pass + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const U *grow = d_out + (int64_t)t * V;
+
+  // First pass of the token's upstream gradient, issued before the slots.
+  U graw[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = cfirst + (int64_t)i * blockDim.x;
+    graw[i] = c < V ? grow[c] : Unit::zero();
+  }
+  const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
+  if (threadIdx.x < k) {
+    sp[threadIdx.x] = probs[(int64_t)t * k + threadIdx.x];
+    if (blockIdx.y == 0) report(dev_status, bad);
+  }
+  __syncthreads();
+
+  const bool want_dot = d_probs != nullptr;
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    float part[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; jj++) part[jj] = 0.0f;
+
+    for (int64_t cb = cfirst; cb < V; cb += stride) {
+      if (!(j0 == 0 && cb == cfirst)) {
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+          const int64_t c = cb + (int64_t)i * blockDim.x;
+          graw[i] = c < V ? grow[c] : Unit::zero();
+        }
+      }
+      U fin[KB][VPT];
+      if (want_dot) {
+#pragma unroll
+        for (int jj = 0; jj < KB; jj++) {
+          const int j = j0 + jj;
+          const int64_t r = (j < k) ? srow[j] : -1;
+#pragma unroll
+          for (int i = 0; i < VPT; i++) {
+            const int64_t c = cb + (int64_t)i * blockDim.x;
+            fin[jj][i] = (r >= 0 && c < V) ? fwd_in[r * V + c] : Unit::zero();
+          }
+        }
+      }
+      float g[VPT][EPV];
+#pragma unroll
+      for (int i = 0; i < VPT; i++) Unit::unpack(graw[i], g[i]);
+#pragma unroll
+      for (int jj = 0; jj < KB; jj++) {
+        const int j = j0 + jj;
+        if (j >= k) continue;
+        const int64_t r = srow[j];
+        const float p = sp[j];
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+          const int64_t c = cb + (int64_t)i * blockDim.x;
+          float prod[EPV];
+#pragma unroll
+          for (int e = 0; e < EPV; e++) prod[e] = g[i][e] * p;  // one fp32 rounding
+          if (r >= 0 && c < V) d_in[r * V + c] = Unit::pack(prod);
+          if (want_dot) {
+            float f[EPV];
+            Unit::unpack(fin[jj][i], f);
+#pragma unroll
+            for (int e = 0; e < EPV; e++) part[jj] = __builtin_fmaf(f[e], g[i][e], part[jj]);
+          }
+        }
+      }
+    }
+
+    if (want_dot) {
+#pragma unroll
+      for (int jj = 0; jj < KB; jj++) {
+        const float s = wave_sum(part[jj]);
+        if (lane == 0) sred[wv][jj] = s;
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < KB && j0 + (int)threadIdx.x < k) {
+        float s = 0.0f;
+        for (int w = 0; w < nwaves; w++) s += sred[w][threadIdx.x];
+        d_probs[(int64_t)t * k + j0 + threadIdx.x] = s;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------ launch shape --
+
+struct RowShape {
+  int threads;  // workgroup size, multiple of 64
+  int vpt;      // units per lane per row slice
+  int ysplit;   // row slices per token (grid.y)
+};
+
+// One workgroup per token row (slice): cover V units with `threads` lanes of
+// `vpt` units each, preferring the least idle lanes, then mid-size groups.
+RowShape row_shape(int64_t V, bool allow_split) {
+  const int kMaxThreads = kRowThreads;
+  int ysplit = 1;
+  if (allow_split && V > (int64_t)kMaxThreads * 4)
+    ysplit = (int)((V + (int64_t)kMaxThreads * 4 - 1) / ((int64_t)kMaxThreads * 4));
+  const int64_t Vs = (V + ysplit - 1) / ysplit;
+  // Fallback for an unsplit row longer than one full-size pass.
+  RowShape best{kMaxThreads, 4, ysplit};
+  int64_t best_waste = -1;
+  int best_score = 0;
+  const int vpts[] = {1, 2, 4};
+  for (int vpt : vpts) {
+    int64_t th = (Vs + vpt - 1) / vpt;
+    th = ((th + kWave - 1) / kWave) * kWave;
+    if (th > kMaxThreads) continue;
+    const int64_t waste = th * vpt - Vs;
+    // prefer 256..512 threads, then fewer units per lane
+    const int score = (th >= 256 && th <= 512 ? 0 : (th < 256 ? 1 : 2)) * 8 + vpt;
+    if (best_waste < 0 || waste < best_waste || (waste == best_waste && score < best_score)) {
+      best = RowShape{(int)th, vpt, ysplit};
+      best_waste = waste;
+      best_score = score;
+    }
+  }
+  return best;
+}
+
+template <typename U>
+hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *topk_idx,
+                            const int32_t *row_id_map, int T, int64_t V, int k, int E,
+                            int n_rows, void *out, float *out_probs, int32_t *dev_status,
+                            hipStream_t s) {
+  const RowShape sh = row_shape(V, true);
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const U *xp = static_cast<const U *>(x);
+  U *op = static_cast<U *>(out);
+  switch (sh.vpt) {
+    case 1:
+      hipLaunchKernelGGL((permute_kernel<U, 1>), grid, block, 0, s, xp, probs, topk_idx,
+                         row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
+      break;
+    case 2:
+      hipLaunchKernelGGL((permute_kernel<U, 2>), grid, block, 0, s, xp, probs, topk_idx,
+                         row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
+      break;
+    default:
+      hipLaunchKernelGGL((permute_kernel<U, 4>), grid, block, 0, s, xp, probs, topk_idx,
+                         row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int EPV, int VPT>
+void combine_k(const RowShape &sh, int T, const void *in, const float *probs,
+               const int32_t *topk_idx, const int32_t *row_id_map, int64_t V, int k, int E,
+               int n_rows, void *out, const float *gsrc, float *gdst, int32_t *st,
+               hipStream_t s) {
+  using U = typename Bf16Unit<EPV>::T;
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const U *ip = static_cast<const U *>(in);
+  U *op = static_cast<U *>(out);
+#define MOE_COMBINE(KBV)                                                                     \
+  hipLaunchKernelGGL((combine_kernel<EPV, VPT, KBV>), grid, block, 0, s, ip, probs, topk_idx, \
+                     row_id_map, T, V, k, E, n_rows, op, gsrc, gdst, st)
+  switch (k) {
+    case 1: MOE_COMBINE(1); break;
+    case 2: MOE_COMBINE(2); break;
+    case 3: MOE_COMBINE(3); break;
+    case 4: MOE_COMBINE(4); break;
+    case 5: MOE_COMBINE(5); break;
+    case 6: MOE_COMBINE(6); break;
+    case 7: MOE_COMBINE(7); break;
+    default: MOE_COMBINE(8); break;
+  }
+#undef MOE_COMBINE
+}
+
+template <int EPV, int VPT>
+void combine_bwd_k(const RowShape &sh, int T, const void *d_out, const void *fwd_in,
+                   const float *probs, const int32_t *topk_idx, const int32_t *row_id_map,
+                   int64_t V, int k, int E, int n_rows, void *d_in, float *d_probs, int32_t *st,
+                   hipStream_t s) {
+  using U = typename Bf16Unit<EPV>::T;
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const U *gp = static_cast<const U *>(d_out);
+  const U *fp = static_cast<const U *>(fwd_in);
+  U *dp = static_cast<U *>(d_in);
+#define MOE_COMBINE_BWD(KBV)                                                                  \
+  hipLaunchKernelGGL((combine_bwd_kernel<EPV, VPT, KBV>), grid, block, 0, s, gp, fp, probs,   \
+                     topk_idx, row_id_map, T, V, k, E, n_rows, dp, d_probs, st)
+  switch (k) {
+    case 1: MOE_COMBINE_BWD(1); break;
+    case 2: MOE_COMBINE_BWD(2); break;
+    case 3: MOE_COMBINE_BWD(3); break;
+    case 4: MOE_COMBINE_BWD(4); break;
+    case 5: MOE_COMBINE_BWD(5); break;
+    case 6: MOE_COMBINE_BWD(6); break;
+    case 7: MOE_COMBINE_BWD(7); break;
+    default: MOE_COMBINE_BWD(8); break;
+  }
+#undef MOE_COMBINE_BWD
+}
+
+template <int EPV>
+void combine_dispatch(const void *in, const float *probs, const int32_t *topk_idx,
+                      const int32_t *row_id_map, int T, int64_t V, int k, int E, int n_rows,
+                      void *out, const float *gsrc, float *gdst, int32_t *st, hipStream_t s) {
+  const RowShape sh = row_shape(V, true);
+  switch (sh.vpt) {
+    case 1: combine_k<EPV, 1>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+    case 2: combine_k<EPV, 2>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+    default: combine_k<EPV, 4>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+  }
+}
+
+template <int EPV>
+void combine_bwd_dispatch(const void *d_out, const void *fwd_in, const float *probs,
+                          const int32_t *topk_idx, const int32_t *row_id_map, int T, int64_t V,
+                          int k, int E, int n_rows, void *d_in, float *d_probs, int32_t *st,
+                          hipStream_t s) {
+  // The prob-grad reduction needs the whole row in one workgroup; rows
+  // longer than one pass are then walked in several passes.
+  const RowShape sh = row_shape(V, d_probs == nullptr);
+  switch (sh.vpt) {
+    case 1: combine_bwd_k<EPV, 1>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+    case 2: combine_bwd_k<EPV, 2>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+    default: combine_bwd_k<EPV, 4>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const void *x, const float *probs, const int32_t *topk_idx,
+                          const int32_t *row_id_map, int T, int H, int k, int E, int n_rows,
+                          void *out, float *out_probs, int32_t *dev_status, bool vec,
+                          hipStream_t s) {
+  if (vec)
+    return permute_dispatch<uint4>(x, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
+                                   out_probs, dev_status, s);
+  return permute_dispatch<uint16_t>(x, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out,
+                                    out_probs, dev_status, s);
+}
+
+hipError_t launch_combine(const void *in, const float *probs, const int32_t *topk_idx,
+                          const int32_t *row_id_map, int T, int H, int k, int E, int n_rows,
+                          void *out, const float *gather_src, float *gather_dst,
+                          int32_t *dev_status, bool vec, hipStream_t s) {
+  if (vec)
+    combine_dispatch<8>(in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
+                        gather_src, gather_dst, dev_status, s);
+  else
+    combine_dispatch<1>(in, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out, gather_src,
+                        gather_dst, dev_status, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float *probs,
+                              const int32_t *topk_idx, const int32_t *row_id_map, int T, int H,
+                              int k, int E, int n_rows, void *d_in, float *d_probs,
+                              int32_t *dev_status, bool vec, hipStream_t s) {
+  if (vec)
+    combine_bwd_dispatch<8>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows,
+                            d_in, d_probs, dev_status, s);
+  else
+    combine_bwd_dispatch<1>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H, k, E, n_rows,
+                            d_in, d_probs, dev_status, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -188,3 +188,11 @@ CHUNKED = {"chunks8k": chunks8k, "chunks32k": chunks32k}
 def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bf16 CPU tensor's bit patterns."""
     return t.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def random_rows(n: int, H: int, seed: int, device="cpu") -> torch.Tensor:
+    """[n, H] bf16 N(0,1) rows drawn with a torch generator on `device`
+    (used as arbitrary bf16 inputs to the combine and its gradients)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(n, H, generator=g, device=device).to(torch.bfloat16)
