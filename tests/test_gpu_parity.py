@@ -305,7 +305,7 @@ def test_permute_bwd_configs(m, name):
 
 
 @pytest.mark.parametrize("T,H,E,k", [(1, 8, 2, 1), (37, 7, 9, 3), (100, 24, 16, 2),
-                                     (64, 64, 8, 9), (40, 136, 80, 64), (33, 2056, 12, 5),
+                                     (64, 64, 12, 9), (40, 136, 80, 64), (33, 2056, 12, 5),
                                      (20, 7168, 16, 4), (9, 20480, 8, 8), (17, 20481, 4, 2),
                                      (300, 512, 32, 1)])
 def test_row_kernels_edges(m, T, H, E, k):
