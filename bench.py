@@ -46,6 +46,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a captured hipGraph")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after timing, run a plain device copy of MIB MiB three times "
+                         "(a known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -75,6 +78,36 @@ def chunk_bytes(N, H, cap, eb=2):
 
 # --------------------------------------------------------------- setup ----
 
+class HipEvents:
+    """Raw HIP events recorded through ctypes: far less host overhead per
+    record than torch.cuda.Event, so timing every op does not starve the GPU."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (the HIP runtime is already loaded by torch)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_us(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e3
+
+
 class Step:
     """A list of (name, fn, args) calls straight into the C ABI; the stream
     argument (always last) is supplied at run time."""
@@ -86,16 +119,16 @@ class Step:
     def add(self, name, fn, *args):
         self.ops.append((name, fn, args))
 
-    def run(self, events=None, stream=None):
+    def run(self, events=None, stream=None, hev=None):
         import torch
         s = ctypes.c_void_p(stream if stream is not None
                             else torch.cuda.current_stream().cuda_stream)
         for name, fn, args in self.ops:
             if events is not None:
-                events[name][0].record()
+                hev.record(events[name][0], s)
             st = fn(*args, s)
             if events is not None:
-                events[name][1].record()
+                hev.record(events[name][1], s)
             if st != 0:
                 raise RuntimeError(f"{name}: status {st}")
 
@@ -249,19 +282,19 @@ def main():
 
     K = args.steps
     names = [n for n, _, _ in step.ops]
-    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for n in names} for _ in range(K)]
+    hev = HipEvents()
+    evs = [{n: (hev.create(), hev.create()) for n in names} for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step.run(evs[i])
+        step.run(evs[i], hev=hev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / K * 1e3
 
     per_op = {}
     for n in names:
-        times = sorted(evs[i][n][0].elapsed_time(evs[i][n][1]) * 1e3 for i in range(K))
+        times = sorted(hev.elapsed_us(evs[i][n][0], evs[i][n][1]) for i in range(K))
         mean = sum(times) / K
         per_op[n] = {"us_mean": round(mean, 2), "us_median": round(times[K // 2], 2),
                      "bytes": op_bytes[n],
@@ -312,6 +345,14 @@ def main():
         gms = (time.perf_counter() - t0) / K * 1e3
         result["graph_replay"] = {"ms_per_step": round(gms, 4),
                                   "GBps": round(step_bytes / (gms * 1e-3) / 1e9, 1)}
+    if args.copy_probe > 0:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = {"read": 4 * n, "write": 4 * n}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(name, w, args.cpu_seconds, step_bytes)
     print(json.dumps(result), flush=True)

@@ -153,7 +153,8 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(
   }
 }
 
-template <typename U>
+// NTS: stream the (dense, sequential) destination rows.
+template <typename U, bool NTS>
 __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
     const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, int64_t W,
     int n_cap, const int32_t *__restrict__ row_map, int out_cap, U *__restrict__ out,
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
       const int64_t c = u - d * W;
       const int32_t s = row_map[d];
       if (s >= n_cap) bad |= MOE_DEV_BAD_ROW;
-      if (s >= 0 && s < n_cap) v[i] = in[(int64_t)s * W + c];
+      if (s >= 0 && s < n_cap) v[i] = ld_row<false>(in + (int64_t)s * W + c);
       if (c == 0 && out_probs != nullptr) {
         const bool ok = s >= 0 && s < n_cap;
         if (prob_bytes == 4)
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
 #pragma unroll
   for (int i = 0; i < kCopyIlp; i++) {
     const int64_t u = base + (int64_t)i * kCopyThreads;
-    if (u < total) out[u] = v[i];
+    if (u < total) st_row<NTS>(v[i], out + u);
   }
   report(dev_status, bad);
 }
@@ -203,7 +204,8 @@ __device__ __forceinline__ int64_t wave_total(const int32_t *__restrict__ sizes,
 
 // Flat index over [0, max(out_cap, n_cap)) x W: unit (i, c) scatters padded
 // row i (if mapped) and zero-fills restored row i (if past the token total).
-template <typename U>
+// NTL: stream the (dense, sequential) padded source rows.
+template <typename U, bool NTL>
 __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
     const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, int64_t W,
     const int32_t *__restrict__ row_map, const int32_t *__restrict__ split_sizes, int C,
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
         if (s >= n_cap) bad |= MOE_DEV_BAD_ROW;
         if (s >= 0 && s < n_cap) {
           dst[i] = s;
-          v[i] = in[u];
+          v[i] = ld_row<NTL>(in + u);
           if (c == 0 && out_probs != nullptr) {
             if (prob_bytes == 4)
               reinterpret_cast<uint32_t *>(out_probs)[s] =
@@ -248,9 +250,9 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
     if (u < total) {
       const int64_t d = u / W;
       const int64_t c = u - d * W;
-      if (dst[i] >= 0) out[(int64_t)dst[i] * W + c] = v[i];
+      if (dst[i] >= 0) st_row<false>(v[i], out + (int64_t)dst[i] * W + c);
       if (d >= n_act && d < n_cap) {
-        out[u] = zero_unit<U>();
+        st_row<false>(zero_unit<U>(), out + u);
         if (c == 0 && out_probs != nullptr) {
           if (prob_bytes == 4)
             reinterpret_cast<uint32_t *>(out_probs)[d] = 0u;
@@ -298,19 +300,25 @@ hipError_t launch_pad_copy(const void *in, const void *probs, int prob_bytes, in
   const dim3 grid(copy_blocks(units)), block(kCopyThreads);
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
+  const bool stream = units * 16 * 2 > kStreamBytes;
   switch (unit_bytes) {
     case 16:
-      hipLaunchKernelGGL(pad_copy_kernel<uint4>, grid, block, 0, s,
-                         static_cast<const uint4 *>(in), pp, prob_bytes, row_units, n_cap,
-                         row_map, out_cap, static_cast<uint4 *>(out), op, dev_status);
+      if (stream)
+        hipLaunchKernelGGL((pad_copy_kernel<v4u, true>), grid, block, 0, s,
+                           static_cast<const v4u *>(in), pp, prob_bytes, row_units, n_cap,
+                           row_map, out_cap, static_cast<v4u *>(out), op, dev_status);
+      else
+        hipLaunchKernelGGL((pad_copy_kernel<v4u, false>), grid, block, 0, s,
+                           static_cast<const v4u *>(in), pp, prob_bytes, row_units, n_cap,
+                           row_map, out_cap, static_cast<v4u *>(out), op, dev_status);
       break;
     case 4:
-      hipLaunchKernelGGL(pad_copy_kernel<uint32_t>, grid, block, 0, s,
+      hipLaunchKernelGGL((pad_copy_kernel<uint32_t, false>), grid, block, 0, s,
                          static_cast<const uint32_t *>(in), pp, prob_bytes, row_units, n_cap,
                          row_map, out_cap, static_cast<uint32_t *>(out), op, dev_status);
       break;
     default:
-      hipLaunchKernelGGL(pad_copy_kernel<uint16_t>, grid, block, 0, s,
+      hipLaunchKernelGGL((pad_copy_kernel<uint16_t, false>), grid, block, 0, s,
                          static_cast<const uint16_t *>(in), pp, prob_bytes, row_units, n_cap,
                          row_map, out_cap, static_cast<uint16_t *>(out), op, dev_status);
       break;
@@ -327,21 +335,28 @@ hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes
   const dim3 grid(copy_blocks(units)), block(kCopyThreads);
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
+  const bool stream = ((int64_t)out_cap + n_cap) * row_units * 16 > kStreamBytes;
   switch (unit_bytes) {
     case 16:
-      hipLaunchKernelGGL(restore_copy_kernel<uint4>, grid, block, 0, s,
-                         static_cast<const uint4 *>(in), pp, prob_bytes, row_units, row_map,
-                         split_sizes, C, out_cap, n_cap, static_cast<uint4 *>(out), op,
-                         dev_status);
+      if (stream)
+        hipLaunchKernelGGL((restore_copy_kernel<v4u, true>), grid, block, 0, s,
+                           static_cast<const v4u *>(in), pp, prob_bytes, row_units, row_map,
+                           split_sizes, C, out_cap, n_cap, static_cast<v4u *>(out), op,
+                           dev_status);
+      else
+        hipLaunchKernelGGL((restore_copy_kernel<v4u, false>), grid, block, 0, s,
+                           static_cast<const v4u *>(in), pp, prob_bytes, row_units, row_map,
+                           split_sizes, C, out_cap, n_cap, static_cast<v4u *>(out), op,
+                           dev_status);
       break;
     case 4:
-      hipLaunchKernelGGL(restore_copy_kernel<uint32_t>, grid, block, 0, s,
+      hipLaunchKernelGGL((restore_copy_kernel<uint32_t, false>), grid, block, 0, s,
                          static_cast<const uint32_t *>(in), pp, prob_bytes, row_units, row_map,
                          split_sizes, C, out_cap, n_cap, static_cast<uint32_t *>(out), op,
                          dev_status);
       break;
     default:
-      hipLaunchKernelGGL(restore_copy_kernel<uint16_t>, grid, block, 0, s,
+      hipLaunchKernelGGL((restore_copy_kernel<uint16_t, false>), grid, block, 0, s,
                          static_cast<const uint16_t *>(in), pp, prob_bytes, row_units, row_map,
                          split_sizes, C, out_cap, n_cap, static_cast<uint16_t *>(out), op,
                          dev_status);

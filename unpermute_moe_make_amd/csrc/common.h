@@ -10,6 +10,27 @@ namespace moe {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
+// 16 bytes as a native clang vector (the non-temporal builtins need one).
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Cache policy of a bulk row access: plain, or non-temporal (streamed past
+// the caches).  Each row byte is read once or written once per call.
+template <bool NT, typename U> __device__ __forceinline__ U ld_row(const U *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename U> __device__ __forceinline__ void st_row(U v, U *p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// A call that moves more bytes than the MI355X Infinity Cache (256 MiB)
+// holds streams its rows; a smaller call keeps plain accesses so the next
+// call on the same buffers can still hit the cache.  Which accesses of a
+// kernel stream was measured per kernel (non-temporal stores help dense,
+// sequential row writes and hurt scattered ones).
+constexpr int64_t kStreamBytes = 256ll << 20;
+
 // bf16 -> fp32 is exact: the bf16 pattern is the top half of the binary32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -32,22 +53,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int EPV> struct Bf16Unit;
 
 template <> struct Bf16Unit<8> {
-  using T = uint4;
-  __device__ __forceinline__ static void unpack(const uint4 &v, float *f) {
+  using T = v4u;
+  __device__ __forceinline__ static void unpack(const v4u &v, float *f) {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
     f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
     f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
     f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
   }
-  __device__ __forceinline__ static uint4 pack(const float *f) {
-    uint4 r;
+  __device__ __forceinline__ static v4u pack(const float *f) {
+    v4u r;
     r.x = pack_bf16x2(f[0], f[1]);
     r.y = pack_bf16x2(f[2], f[3]);
     r.z = pack_bf16x2(f[4], f[5]);
     r.w = pack_bf16x2(f[6], f[7]);
     return r;
   }
-  __device__ __forceinline__ static uint4 zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ static v4u zero() { return v4u{0u, 0u, 0u, 0u}; }
 };
 
 template <> struct Bf16Unit<1> {
@@ -60,7 +81,7 @@ template <> struct Bf16Unit<1> {
 };
 
 template <typename U> __device__ __forceinline__ U zero_unit();
-template <> __device__ __forceinline__ uint4 zero_unit<uint4>() { return make_uint4(0u, 0u, 0u, 0u); }
+template <> __device__ __forceinline__ v4u zero_unit<v4u>() { return v4u{0u, 0u, 0u, 0u}; }
 template <> __device__ __forceinline__ uint32_t zero_unit<uint32_t>() { return 0u; }
 template <> __device__ __forceinline__ uint16_t zero_unit<uint16_t>() { return 0; }
 

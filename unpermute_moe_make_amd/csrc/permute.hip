@@ -23,7 +23,15 @@ namespace moe {
 namespace {
 
 constexpr int kMaxTopk = MOE_MAX_TOPK;
-constexpr int kRowThreads = 512;  // largest row workgroup (keeps 256 VGPRs per lane available)
+// Largest row workgroup (512 keeps 256 VGPRs per lane available) and the
+// units per lane (0: chosen per row length); build-time tuning constants.
+#ifndef MOE_ROW_MAX_THREADS
+#define MOE_ROW_MAX_THREADS 512
+#endif
+#ifndef MOE_ROW_VPT
+#define MOE_ROW_VPT 0
+#endif
+constexpr int kRowThreads = MOE_ROW_MAX_THREADS;
 
 // Resolve the token's slots into LDS.  Returns status bits of this lane.
 __device__ __forceinline__ int resolve_slots(const int32_t *__restrict__ topk_idx,
@@ -67,7 +75,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = c0 + (int64_t)i * blockDim.x;
-    if (c < V) v[i] = xr[c];
+    if (c < V) v[i] = ld_row<false>(xr + c);
   }
   const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
   if (blockIdx.y == 0 && threadIdx.x < k) {
@@ -84,7 +92,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
 #pragma unroll
     for (int i = 0; i < VPT; i++) {
       const int64_t c = c0 + (int64_t)i * blockDim.x;
-      if (c < V) orow[c] = v[i];
+      if (c < V) st_row<false>(v[i], orow + c);
     }
   }
 }
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
 // out[t] = bf16(fma chain over slots of p_j * in[r_j]); probs == NULL -> 1.
 // KB = slots loaded per batch (all of them when k <= 8).  Optionally gathers
 // gather_dst[t][j] = gather_src[r_j] (permute backward of the probs).
-template <int EPV, int VPT, int KB>
+template <int EPV, int VPT, int KB, bool NT>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     const typename Bf16Unit<EPV>::T *__restrict__ in, const float *__restrict__ probs,
     const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 #pragma unroll
       for (int i = 0; i < VPT; i++) {
         const int64_t c = c0 + (int64_t)i * blockDim.x;
-        vals[jj][i] = (r >= 0 && c < V) ? in[r * V + c] : Unit::zero();
+        vals[jj][i] = (r >= 0 && c < V) ? ld_row<NT>(in + r * V + c) : Unit::zero();
       }
     }
     // Then the fused multiply-adds, strictly in slot order.
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = c0 + (int64_t)i * blockDim.x;
-    if (c < V) orow[c] = Unit::pack(acc[i]);
+    if (c < V) st_row<NT>(Unit::pack(acc[i]), orow + c);
   }
 }
 
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 // A workgroup walks its row slice in passes of blockDim*VPT units.  When
 // d_probs is written the grid must not split rows (gridDim.y == 1), so the
 // workgroup sees the whole row and reduces each slot's dot product itself.
-template <int EPV, int VPT, int KB>
+template <int EPV, int VPT, int KB, bool NT>
 __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
     const typename Bf16Unit<EPV>::T *__restrict__ d_out,
     const typename Bf16Unit<EPV>::T *__restrict__ fwd_in, const float *__restrict__ probs,
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = cfirst + (int64_t)i * blockDim.x;
-    graw[i] = c < V ? grow[c] : Unit::zero();
+    graw[i] = c < V ? ld_row<NT>(grow + c) : Unit::zero();
   }
   const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
   if (threadIdx.x < k) {
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
 #pragma unroll
         for (int i = 0; i < VPT; i++) {
           const int64_t c = cb + (int64_t)i * blockDim.x;
-          graw[i] = c < V ? grow[c] : Unit::zero();
+          graw[i] = c < V ? ld_row<NT>(grow + c) : Unit::zero();
         }
       }
       U fin[KB][VPT];
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
 #pragma unroll
           for (int i = 0; i < VPT; i++) {
             const int64_t c = cb + (int64_t)i * blockDim.x;
-            fin[jj][i] = (r >= 0 && c < V) ? fwd_in[r * V + c] : Unit::zero();
+            fin[jj][i] = (r >= 0 && c < V) ? ld_row<NT>(fwd_in + r * V + c) : Unit::zero();
           }
         }
       }
@@ -248,7 +256,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
           float prod[EPV];
 #pragma unroll
           for (int e = 0; e < EPV; e++) prod[e] = g[i][e] * p;  // one fp32 rounding
-          if (r >= 0 && c < V) d_in[r * V + c] = Unit::pack(prod);
+          if (r >= 0 && c < V) st_row<NT>(Unit::pack(prod), d_in + r * V + c);
           if (want_dot) {
             float f[EPV];
             Unit::unpack(fin[jj][i], f);
@@ -298,6 +306,7 @@ RowShape row_shape(int64_t V, bool allow_split) {
   int best_score = 0;
   const int vpts[] = {1, 2, 4};
   for (int vpt : vpts) {
+    if (MOE_ROW_VPT != 0 && vpt != MOE_ROW_VPT) continue;
     int64_t th = (Vs + vpt - 1) / vpt;
     th = ((th + kWave - 1) / kWave) * kWave;
     if (th > kMaxThreads) continue;
@@ -339,7 +348,7 @@ hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *to
   return hipGetLastError();
 }
 
-template <int EPV, int VPT>
+template <int EPV, int VPT, bool NT>
 void combine_k(const RowShape &sh, int T, const void *in, const float *probs,
                const int32_t *topk_idx, const int32_t *row_id_map, int64_t V, int k, int E,
                int n_rows, void *out, const float *gsrc, float *gdst, int32_t *st,
@@ -349,7 +358,7 @@ void combine_k(const RowShape &sh, int T, const void *in, const float *probs,
   const U *ip = static_cast<const U *>(in);
   U *op = static_cast<U *>(out);
 #define MOE_COMBINE(KBV)                                                                     \
-  hipLaunchKernelGGL((combine_kernel<EPV, VPT, KBV>), grid, block, 0, s, ip, probs, topk_idx, \
+  hipLaunchKernelGGL((combine_kernel<EPV, VPT, KBV, NT>), grid, block, 0, s, ip, probs, topk_idx, \
                      row_id_map, T, V, k, E, n_rows, op, gsrc, gdst, st)
   switch (k) {
     case 1: MOE_COMBINE(1); break;
@@ -364,7 +373,7 @@ void combine_k(const RowShape &sh, int T, const void *in, const float *probs,
 #undef MOE_COMBINE
 }
 
-template <int EPV, int VPT>
+template <int EPV, int VPT, bool NT>
 void combine_bwd_k(const RowShape &sh, int T, const void *d_out, const void *fwd_in,
                    const float *probs, const int32_t *topk_idx, const int32_t *row_id_map,
                    int64_t V, int k, int E, int n_rows, void *d_in, float *d_probs, int32_t *st,
@@ -375,7 +384,7 @@ void combine_bwd_k(const RowShape &sh, int T, const void *d_out, const void *fwd
   const U *fp = static_cast<const U *>(fwd_in);
   U *dp = static_cast<U *>(d_in);
 #define MOE_COMBINE_BWD(KBV)                                                                  \
-  hipLaunchKernelGGL((combine_bwd_kernel<EPV, VPT, KBV>), grid, block, 0, s, gp, fp, probs,   \
+  hipLaunchKernelGGL((combine_bwd_kernel<EPV, VPT, KBV, NT>), grid, block, 0, s, gp, fp, probs,   \
                      topk_idx, row_id_map, T, V, k, E, n_rows, dp, d_probs, st)
   switch (k) {
     case 1: MOE_COMBINE_BWD(1); break;
@@ -390,19 +399,19 @@ void combine_bwd_k(const RowShape &sh, int T, const void *d_out, const void *fwd
 #undef MOE_COMBINE_BWD
 }
 
-template <int EPV>
+template <int EPV, bool NT>
 void combine_dispatch(const void *in, const float *probs, const int32_t *topk_idx,
                       const int32_t *row_id_map, int T, int64_t V, int k, int E, int n_rows,
                       void *out, const float *gsrc, float *gdst, int32_t *st, hipStream_t s) {
   const RowShape sh = row_shape(V, true);
   switch (sh.vpt) {
-    case 1: combine_k<EPV, 1>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
-    case 2: combine_k<EPV, 2>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
-    default: combine_k<EPV, 4>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+    case 1: combine_k<EPV, 1, NT>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+    case 2: combine_k<EPV, 2, NT>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+    default: combine_k<EPV, 4, NT>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
   }
 }
 
-template <int EPV>
+template <int EPV, bool NT>
 void combine_bwd_dispatch(const void *d_out, const void *fwd_in, const float *probs,
                           const int32_t *topk_idx, const int32_t *row_id_map, int T, int64_t V,
                           int k, int E, int n_rows, void *d_in, float *d_probs, int32_t *st,
@@ -411,9 +420,9 @@ void combine_bwd_dispatch(const void *d_out, const void *fwd_in, const float *pr
   // longer than one pass are then walked in several passes.
   const RowShape sh = row_shape(V, d_probs == nullptr);
   switch (sh.vpt) {
-    case 1: combine_bwd_k<EPV, 1>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
-    case 2: combine_bwd_k<EPV, 2>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
-    default: combine_bwd_k<EPV, 4>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+    case 1: combine_bwd_k<EPV, 1, NT>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+    case 2: combine_bwd_k<EPV, 2, NT>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+    default: combine_bwd_k<EPV, 4, NT>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
   }
 }
 
@@ -424,7 +433,7 @@ hipError_t launch_permute(const void *x, const float *probs, const int32_t *topk
                           void *out, float *out_probs, int32_t *dev_status, bool vec,
                           hipStream_t s) {
   if (vec)
-    return permute_dispatch<uint4>(x, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
+    return permute_dispatch<v4u>(x, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
                                    out_probs, dev_status, s);
   return permute_dispatch<uint16_t>(x, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out,
                                     out_probs, dev_status, s);
@@ -434,12 +443,17 @@ hipError_t launch_combine(const void *in, const float *probs, const int32_t *top
                           const int32_t *row_id_map, int T, int H, int k, int E, int n_rows,
                           void *out, const float *gather_src, float *gather_dst,
                           int32_t *dev_status, bool vec, hipStream_t s) {
-  if (vec)
-    combine_dispatch<8>(in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
-                        gather_src, gather_dst, dev_status, s);
+  // Gathered rows in, dense rows out: both stream when the call is large.
+  const int64_t bytes = 2ll * H * ((int64_t)n_rows + T);
+  if (vec && bytes > kStreamBytes)
+    combine_dispatch<8, true>(in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
+                              gather_src, gather_dst, dev_status, s);
+  else if (vec)
+    combine_dispatch<8, false>(in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
+                               gather_src, gather_dst, dev_status, s);
   else
-    combine_dispatch<1>(in, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out, gather_src,
-                        gather_dst, dev_status, s);
+    combine_dispatch<1, false>(in, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out,
+                               gather_src, gather_dst, dev_status, s);
   return hipGetLastError();
 }
 
@@ -447,12 +461,16 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
                               const int32_t *topk_idx, const int32_t *row_id_map, int T, int H,
                               int k, int E, int n_rows, void *d_in, float *d_probs,
                               int32_t *dev_status, bool vec, hipStream_t s) {
-  if (vec)
-    combine_bwd_dispatch<8>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows,
-                            d_in, d_probs, dev_status, s);
+  const int64_t bytes = 2ll * H * ((int64_t)n_rows * (d_probs ? 2 : 1) + T);
+  if (vec && bytes > kStreamBytes)
+    combine_bwd_dispatch<8, true>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
+                                  n_rows, d_in, d_probs, dev_status, s);
+  else if (vec)
+    combine_bwd_dispatch<8, false>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
+                                   n_rows, d_in, d_probs, dev_status, s);
   else
-    combine_bwd_dispatch<1>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H, k, E, n_rows,
-                            d_in, d_probs, dev_status, s);
+    combine_bwd_dispatch<1, false>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H, k, E,
+                                   n_rows, d_in, d_probs, dev_status, s);
   return hipGetLastError();
 }
 
