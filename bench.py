@@ -44,8 +44,8 @@ def parse():
                     choices=["tiny", "finegrain", "skewed", "chunks8k", "chunks32k"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step replayed from a captured hipGraph")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip timing the step replayed from a captured hipGraph")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB three times "
                          "(a known-size reference for hardware byte counters)")
@@ -74,6 +74,47 @@ def chunk_bytes(N, H, cap, eb=2):
         "sort_chunks_and_pad": N * row + cap * row + 4 * N + 4 * cap + 4 * cap + 4 * cap,
         "unpad_and_restore": N * row + N * row + 4 * cap + 4 * N + 4 * N,
     }
+
+
+# Kernels each op launches (the op's events bracket all of them).
+OP_KERNELS = {
+    "row_map": ["rowmap_count_kernel", "rowmap_write_kernel"],
+    "permute": ["permute_kernel"],
+    "unpermute": ["combine_kernel"],
+    "unpermute_bwd": ["combine_bwd_kernel"],
+    "permute_bwd": ["combine_kernel"],
+    "sort_chunks_and_pad": ["chunk_map_kernel", "pad_copy_kernel"],
+    "unpad_and_restore": ["restore_copy_kernel"],
+}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources, to tell whether stored counters still apply."""
+    import hashlib
+    d = os.path.join(ROOT, "unpermute_moe_make_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def pmc_traffic(workload: str, op: str):
+    """HBM bytes per launch of the op's kernels from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (profiles/pmc_traffic.json), scaled by the
+    copy-kernel calibration factors; None when the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    e = d.get("workloads", {}).get(workload, {}).get(op)
+    if e is None:
+        return None
+    return round(e["fetch_kib"] * 1024 * d["fetch_factor"] +
+                 e["write_kib"] * 1024 * d["write_factor"])
 
 
 # --------------------------------------------------------------- setup ----
@@ -280,29 +321,47 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    K = args.steps
     names = [n for n, _, _ in step.ops]
     hev = HipEvents()
-    evs = [{n: (hev.create(), hev.create()) for n in names} for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
+    sv = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    # Breakdown pass: HIP events around every op (one marker pair per call).
+    K2 = max(10, args.steps // 2)
+    evs = [{n: (hev.create(), hev.create()) for n in names} for _ in range(K2)]
+    for i in range(K2):
         step.run(evs[i], hev=hev)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / K * 1e3
-
     per_op = {}
     for n in names:
-        times = sorted(hev.elapsed_us(evs[i][n][0], evs[i][n][1]) for i in range(K))
-        mean = sum(times) / K
-        per_op[n] = {"us_mean": round(mean, 2), "us_median": round(times[K // 2], 2),
+        times = sorted(hev.elapsed_us(evs[i][n][0], evs[i][n][1]) for i in range(K2))
+        mean = sum(times) / K2
+        per_op[n] = {"us_mean": round(mean, 2), "us_median": round(times[K2 // 2], 2),
                      "bytes": op_bytes[n],
                      "GBps": round(op_bytes[n] / (mean * 1e-6) / 1e9, 1),
                      "pct_hbm_peak": round(100 * op_bytes[n] / (mean * 1e-6) / 1e9 /
                                            HBM_PEAK_GBS, 1)}
     dom = max(names, key=lambda n: per_op[n]["us_mean"])
-    achieved = op_bytes[dom] / (per_op[dom]["us_mean"] * 1e-6) / 1e9
+
+    # Timed region: exactly K steps; events only around the dominant op.
+    K = args.steps
+    dev_ev = [(hev.create(), hev.create()) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        for n, fn, a in step.ops:
+            if n == dom:
+                hev.record(dev_ev[i][0], sv)
+            st = fn(*a, sv)
+            if n == dom:
+                hev.record(dev_ev[i][1], sv)
+            if st != 0:
+                raise RuntimeError(f"{n}: status {st}")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / K * 1e3
+    dom_us = sum(hev.elapsed_us(a, b) for a, b in dev_ev) / K
+
+    achieved = op_bytes[dom] / (dom_us * 1e-6) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -321,9 +380,11 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "step_bytes": step_bytes,
         "per_op": per_op,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": dom, "kernels": OP_KERNELS[dom],
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "us_per_launch": round(dom_us, 2),
+                     "bytes_per_launch": op_bytes[dom],
+                     "traffic": pmc_traffic(name, dom)},
     }
     if args.graph:
         # The same step (same buffers) captured once and replayed.

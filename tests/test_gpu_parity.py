@@ -139,7 +139,9 @@ def test_row_map_configs(m, name):
 
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (63, 5, 2), (64, 5, 2), (255, 8, 3), (256, 8, 3),
                                    (257, 8, 3), (1000, 3, 3), (700, 2048, 8), (300, 64, 9),
-                                   (130, 100, 64), (5000, 1, 1), (4097, 257, 7)])
+                                   (130, 100, 64), (5000, 1, 1), (4097, 257, 7),
+                                   (16384, 3, 2), (16385, 8, 2), (70000, 64, 4),
+                                   (300000, 2, 1)])
 def test_row_map_edges(m, T, E, k):
     say(f"row_map edge T={T} E={E} k={k}")
     w = workloads.random_routed(T, 8, E, k, seed=T * 31 + E, with_dy=False, zipf_s=0.7)

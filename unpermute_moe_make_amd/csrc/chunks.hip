@@ -1,72 +1,168 @@
-// Fused chunk sort-and-pad and unpad-and-restore: one map kernel and two
-// copy kernels (TransformerEngine PR "Fuse MoE chunk sorting and padding",
-// Description, Changes and Diagram).
+// Fused chunk sort-and-pad and unpad-and-restore (TransformerEngine PR "Fuse
+// MoE chunk sorting and padding", Description, Changes and Diagram): one map
+// kernel and two copy kernels.
 //
-// Map.  Every map workgroup rebuilds the small chunk tables in LDS from the
-// device-resident split sizes and chunk order (a few hundred integers) and
-// then writes its own slice of the padded destination -> source row map by
-// binary search, so the map costs one launch with no host round trip and no
-// serial pass over the rows.  Every workgroup validates the metadata the
-// same way; on bad metadata the whole map is -1 (so the copies write zeros)
-// and workgroup 0 reports the error.
+// Map.  Wave 0 of every map workgroup rebuilds the small chunk tables in LDS
+// from the device-resident split sizes and chunk order -- input-order source
+// offsets, sorted-order prefixes, padded group starts -- with cross-lane
+// shuffle scans and no workgroup barrier, so the build costs a few hundred
+// cycles after the metadata loads.  The workgroup then writes its slice of
+// the padded destination -> source row map by two binary searches per row.
+// Every workgroup validates the metadata the same way; on bad metadata the
+// whole map is -1 (so the copies write zeros) and workgroup 0 reports it.
 //
 // Copies.  Both walk a flat index over (row, unit) with 16-byte units where
-// the row allows, consecutive lanes on consecutive units, ILP units per lane
-// loaded before any is stored.  The pad copy writes every destination row
-// (zeros where the map is -1).  The restore scatters every mapped row back
-// to its source and writes zeros to the rows past the token total, which it
-// computes from the split sizes on the device.
+// the row allows, consecutive lanes on consecutive units, several units per
+// lane loaded before any is stored.  The pad copy writes every destination
+// row (zeros where the map is -1).  The restore scatters every mapped row
+// back to its source and writes zeros to the rows past the token total,
+// which it sums from the split sizes on the device.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-constexpr int kMapThreads = 512;
-constexpr int kMapRowsPerBlock = 2048;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyIlp = 4;
+constexpr int kUnitsPerIter = kCopyThreads * kCopyIlp;
+constexpr int kMapRows = 256;         // row_map entries per map workgroup (one per lane)
 
-// In-place exclusive scan of n int64 values in LDS by one workgroup.
-// Returns the total to every thread.  Contains barriers: call uniformly.
-__device__ int64_t block_exclusive_scan(int64_t *a, int n, int64_t *wave_tot) {
-  const int tid = threadIdx.x;
-  const int nth = blockDim.x;
-  const int per = (n + nth - 1) / nth;
-  const int beg = min(n, tid * per);
-  const int end = min(n, beg + per);
-  int64_t sum = 0;
-  for (int i = beg; i < end; i++) sum += a[i];
-  const int lane = tid & (kWave - 1);
-  const int w = tid / kWave;
-  int64_t incl = sum;
+// ----------------------------------------------------------- chunk tables --
+
+// Tables in LDS.  int32 entries are exact whenever the metadata is valid
+// (every prefix is at most the token total <= n_cap); padded starts are
+// int64 because a large alignment can push them past int32 before the
+// capacity check rejects them.
+struct ChunkTables {
+  int64_t *g_pad;    // [G+1] padded start of each group; g_pad[G] = padded total
+  int32_t *src_off;  // [C]   first source row of each input chunk
+  int32_t *qoff;     // [C+1] sorted-order prefix of chunk sizes
+  int32_t *order;    // [C]   input chunk at each sorted position
+  int32_t *size;     // [C]   chunk sizes (input order)
+  int32_t *seen;     // [C]   permutation check
+};
+
+inline size_t chunk_tables_bytes(int C, int G) {
+  return (size_t)(G + 1) * sizeof(int64_t) + (size_t)(5 * C + 1) * sizeof(int32_t);
+}
+
+__device__ inline ChunkTables carve_tables(void *lds, int C, int G) {
+  ChunkTables t;
+  t.g_pad = reinterpret_cast<int64_t *>(lds);
+  t.src_off = reinterpret_cast<int32_t *>(t.g_pad + G + 1);
+  t.qoff = t.src_off + C;
+  t.order = t.qoff + C + 1;
+  t.size = t.order + C;
+  t.seen = t.size + C;
+  return t;
+}
+
+// Exclusive scan across the 64 lanes of one wave; *total gets the sum.
+__device__ __forceinline__ int64_t wave_exclusive_scan(int64_t v, int64_t *total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t incl = v;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    const int64_t v = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += v;
+    const int64_t u = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += u;
   }
-  __syncthreads();  // callers may have just written a[]
-  if (lane == kWave - 1) wave_tot[w] = incl;
-  __syncthreads();
-  int64_t base = 0;
-  for (int i = 0; i < w; i++) base += wave_tot[i];
-  int64_t run = base + incl - sum;
-  for (int i = beg; i < end; i++) {
-    const int64_t c = a[i];
-    a[i] = run;
-    run += c;
+  *total = __shfl(incl, kWave - 1, kWave);
+  return incl - v;
+}
+
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v |= __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// Built by ONE wave (call from all 64 lanes of wave 0): each lane owns a
+// contiguous segment of chunks and of groups, scans run across lanes with
+// shuffles, and lanes exchange table entries through LDS ordered by
+// wave-level fences -- no workgroup barrier inside.  Returns the device
+// status bits (the same value in every lane); non-zero means the tables
+// must not be used.
+__device__ int build_chunk_tables_wave(const int32_t *__restrict__ split_sizes,
+                                       const int32_t *__restrict__ sorted_idx, int C, int R,
+                                       int A, int n_cap, int out_cap, const ChunkTables &t) {
+  const int G = C / R;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = (C + kWave - 1) / kWave;
+  const int c0 = min(C, lane * per), c1 = min(C, c0 + per);
+  int bad = 0;
+  int64_t seg = 0;
+  for (int c = c0; c < c1; c++) {
+    int s = split_sizes[c];
+    const int o = sorted_idx[c];
+    if (s < 0) bad |= MOE_DEV_BAD_CHUNKS;
+    if (s > n_cap) bad |= MOE_DEV_OVERFLOW;
+    if ((unsigned)o >= (unsigned)C) bad |= MOE_DEV_BAD_CHUNKS;
+    s = max(s, 0);
+    t.size[c] = s;
+    t.order[c] = o;
+    t.seen[c] = 0;
+    seg += s;
   }
-  int64_t total = 0;
-  for (int i = 0; i < nth / kWave; i++) total += wave_tot[i];
-  __syncthreads();
-  return total;
+  __syncwarp();
+  for (int q = c0; q < c1; q++) {
+    const int o = t.order[q];
+    if ((unsigned)o < (unsigned)C) atomicAdd(&t.seen[o], 1);
+  }
+  __syncwarp();
+  for (int c = c0; c < c1; c++)
+    if (t.seen[c] != 1) bad |= MOE_DEV_BAD_CHUNKS;
+  bad = wave_or(bad);
+
+  // Source offsets: exclusive scan of the sizes in input order.
+  int64_t n_act;
+  int64_t run = wave_exclusive_scan(seg, &n_act);
+  for (int c = c0; c < c1; c++) {
+    t.src_off[c] = (int32_t)min(run, (int64_t)INT32_MAX);
+    run += t.size[c];
+  }
+  if (n_act > n_cap) bad |= MOE_DEV_OVERFLOW;
+  // Sorted-order prefix of the sizes (only meaningful with a valid order).
+  int64_t sseg = 0;
+  if (!bad)
+    for (int q = c0; q < c1; q++) sseg += t.size[t.order[q]];
+  int64_t stot;
+  run = wave_exclusive_scan(sseg, &stot);
+  for (int q = c0; q < c1; q++) {
+    t.qoff[q] = (int32_t)min(run, (int64_t)INT32_MAX);
+    if (!bad) run += t.size[t.order[q]];
+  }
+  if (lane == kWave - 1) t.qoff[C] = (int32_t)min(stot, (int64_t)INT32_MAX);
+  __syncwarp();
+  // Groups: padded lengths, then their exclusive scan.
+  const int perg = (G + kWave - 1) / kWave;
+  const int g0 = min(G, lane * perg), g1 = min(G, g0 + perg);
+  int64_t gseg = 0;
+  for (int g = g0; g < g1; g++) {
+    const int64_t n = (int64_t)t.qoff[(g + 1) * R] - t.qoff[g * R];
+    const int64_t padded = ((n + A - 1) / A) * A;
+    t.g_pad[g] = padded;
+    gseg += padded;
+  }
+  int64_t pad_total;
+  run = wave_exclusive_scan(gseg, &pad_total);
+  for (int g = g0; g < g1; g++) {
+    const int64_t p = t.g_pad[g];
+    t.g_pad[g] = run;
+    run += p;
+  }
+  if (lane == kWave - 1) t.g_pad[G] = pad_total;
+  if (pad_total > out_cap) bad |= MOE_DEV_OVERFLOW;
+  __syncwarp();
+  return bad;
 }
 
 // Last index i in [lo, hi) with a[i] <= x, for non-decreasing a (a[lo] <= x).
-__device__ __forceinline__ int last_le(const int64_t *a, int lo, int hi, int64_t x) {
+template <typename T>
+__device__ __forceinline__ int last_le(const T *a, int lo, int hi, int64_t x) {
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a[mid] <= x)
+    if ((int64_t)a[mid] <= x)
       lo = mid;
     else
       hi = mid;
@@ -74,85 +170,58 @@ __device__ __forceinline__ int last_le(const int64_t *a, int lo, int hi, int64_t
   return lo;
 }
 
-__global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(
+// Source row of padded destination row d, or -1 for padding / tail rows.
+__device__ __forceinline__ int32_t chunk_src_row(const ChunkTables &t, int G, int R, int64_t d) {
+  if (d >= t.g_pad[G]) return -1;
+  const int g = last_le(t.g_pad, 0, G, d);
+  const int64_t local = d - t.g_pad[g];
+  const int32_t gs = t.qoff[g * R];
+  if (local >= (int64_t)t.qoff[(g + 1) * R] - gs) return -1;
+  const int64_t u = gs + local;  // position in the sorted token order
+  const int q = last_le(t.qoff, g * R, (g + 1) * R, u);
+  return (int32_t)(t.src_off[t.order[q]] + (u - t.qoff[q]));
+}
+
+__device__ __forceinline__ void copy_prob(const uint8_t *src, int64_t si, uint8_t *dst,
+                                          int64_t di, int prob_bytes) {
+  if (prob_bytes == 4)
+    reinterpret_cast<uint32_t *>(dst)[di] =
+        si >= 0 ? reinterpret_cast<const uint32_t *>(src)[si] : 0u;
+  else
+    reinterpret_cast<uint16_t *>(dst)[di] =
+        si >= 0 ? reinterpret_cast<const uint16_t *>(src)[si] : (uint16_t)0;
+}
+
+// --------------------------------------------------------------- the map --
+
+// Grid ceil(out_cap / kMapRows): wave 0 of every workgroup builds the tables,
+// then all lanes write the workgroup's slice of row_map.
+__global__ __launch_bounds__(kCopyThreads) void chunk_map_kernel(
     const int32_t *__restrict__ split_sizes, const int32_t *__restrict__ sorted_idx, int C, int R,
     int A, int n_cap, int out_cap, int32_t *__restrict__ row_map,
     int32_t *__restrict__ padded_offsets, int32_t *__restrict__ dev_status) {
-  const int G = C / R;
   extern __shared__ int64_t lds[];
-  int64_t *src_off = lds;             // [C]   input-order exclusive scan
-  int64_t *q_off = src_off + C;       // [C+1] sorted-order exclusive scan
-  int64_t *g_pad = q_off + C + 1;     // [G+1] padded group starts
-  int64_t *g_n = g_pad + G + 1;       // [G]   group token counts
-  int32_t *order = (int32_t *)(g_n + G);  // [C]
-  int32_t *seen = order + C;              // [C]
-  __shared__ int64_t wave_tot[kMapThreads / kWave];
   __shared__ int bad_s;
-
-  const int tid = threadIdx.x;
-  if (tid == 0) bad_s = 0;
-  for (int i = tid; i < C; i += kMapThreads) seen[i] = 0;
-  __syncthreads();
-  int bad = 0;
-  for (int i = tid; i < C; i += kMapThreads) {
-    const int s = split_sizes[i];
-    const int c = sorted_idx[i];
-    if (s < 0) bad |= MOE_DEV_BAD_CHUNKS;
-    if (s > n_cap) bad |= MOE_DEV_OVERFLOW;
-    src_off[i] = s < 0 ? 0 : s;
-    order[i] = c;
-    if ((unsigned)c >= (unsigned)C)
-      bad |= MOE_DEV_BAD_CHUNKS;
-    else
-      atomicAdd(&seen[c], 1);
+  const int G = C / R;
+  const ChunkTables t = carve_tables(lds, C, G);
+  if (threadIdx.x < kWave) {
+    const int bad = build_chunk_tables_wave(split_sizes, sorted_idx, C, R, A, n_cap, out_cap, t);
+    if (threadIdx.x == 0) bad_s = bad;
   }
   __syncthreads();
-  for (int i = tid; i < C; i += kMapThreads)
-    if (seen[i] != 1) bad |= MOE_DEV_BAD_CHUNKS;
-  if (bad) atomicOr(&bad_s, bad);
-  __syncthreads();
-  bad = bad_s;
-
-  for (int q = tid; q < C; q += kMapThreads) q_off[q] = bad ? 0 : src_off[order[q]];
-  __syncthreads();
-  // Scans are executed by every thread regardless of `bad` (barriers).
-  const int64_t n_act = block_exclusive_scan(src_off, C, wave_tot);
-  block_exclusive_scan(q_off, C, wave_tot);
-  if (tid == 0) q_off[C] = n_act;
-  __syncthreads();
-  for (int g = tid; g < G; g += kMapThreads) {
-    const int64_t n = q_off[(g + 1) * R] - q_off[g * R];
-    g_n[g] = n;
-    g_pad[g] = ((n + A - 1) / A) * A;
-  }
-  __syncthreads();
-  const int64_t pad_total = block_exclusive_scan(g_pad, G, wave_tot);
-  if (tid == 0) g_pad[G] = pad_total;
-  if (!bad && (n_act > n_cap || pad_total > out_cap)) bad = MOE_DEV_OVERFLOW;
-  __syncthreads();
-
+  const int bad = bad_s;
   if (blockIdx.x == 0) {
-    if (tid == 0) report(dev_status, bad);
-    for (int g = tid; g <= G; g += kMapThreads) padded_offsets[g] = bad ? 0 : (int32_t)g_pad[g];
+    if (threadIdx.x == 0) report(dev_status, bad);
+    for (int g = threadIdx.x; g <= G; g += kCopyThreads)
+      padded_offsets[g] = bad ? 0 : (int32_t)t.g_pad[g];
   }
-
-  const int d0 = blockIdx.x * kMapRowsPerBlock;
-  const int d1 = min(out_cap, d0 + kMapRowsPerBlock);
-  for (int d = d0 + tid; d < d1; d += kMapThreads) {
-    int32_t v = -1;
-    if (!bad && d < pad_total) {
-      const int g = last_le(g_pad, 0, G, d);
-      const int64_t local = d - g_pad[g];
-      if (local < g_n[g]) {
-        const int64_t u = q_off[g * R] + local;   // position in sorted order
-        const int q = last_le(q_off, g * R, (g + 1) * R, u);
-        v = (int32_t)(src_off[order[q]] + (u - q_off[q]));
-      }
-    }
-    row_map[d] = v;
-  }
+  const int64_t d0 = (int64_t)blockIdx.x * kMapRows;
+  const int64_t d1 = min((int64_t)out_cap, d0 + kMapRows);
+  for (int64_t d = d0 + threadIdx.x; d < d1; d += kCopyThreads)
+    row_map[d] = bad ? -1 : chunk_src_row(t, G, R, d);
 }
 
+// Pad copy driven by the row map: out[d] = in[row_map[d]] or zeros.
 // NTS: stream the (dense, sequential) destination rows.
 template <typename U, bool NTS>
 __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
@@ -160,7 +229,7 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
     int n_cap, const int32_t *__restrict__ row_map, int out_cap, U *__restrict__ out,
     uint8_t *__restrict__ out_probs, int32_t *__restrict__ dev_status) {
   const int64_t total = (int64_t)out_cap * W;
-  const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kCopyIlp + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kUnitsPerIter + threadIdx.x;
   U v[kCopyIlp];
   int bad = 0;
 #pragma unroll
@@ -170,18 +239,13 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
     if (u < total) {
       const int64_t d = u / W;
       const int64_t c = u - d * W;
-      const int32_t s = row_map[d];
-      if (s >= n_cap) bad |= MOE_DEV_BAD_ROW;
-      if (s >= 0 && s < n_cap) v[i] = ld_row<false>(in + (int64_t)s * W + c);
-      if (c == 0 && out_probs != nullptr) {
-        const bool ok = s >= 0 && s < n_cap;
-        if (prob_bytes == 4)
-          reinterpret_cast<uint32_t *>(out_probs)[d] =
-              ok ? reinterpret_cast<const uint32_t *>(probs)[s] : 0u;
-        else
-          reinterpret_cast<uint16_t *>(out_probs)[d] =
-              ok ? reinterpret_cast<const uint16_t *>(probs)[s] : (uint16_t)0;
+      int64_t s = row_map[d];
+      if (s >= n_cap) {
+        bad |= MOE_DEV_BAD_ROW;
+        s = -1;
       }
+      if (s >= 0) v[i] = ld_row<false>(in + s * W + c);
+      if (c == 0 && out_probs != nullptr) copy_prob(probs, s, out_probs, d, prob_bytes);
     }
   }
 #pragma unroll
@@ -191,6 +255,8 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
   }
   report(dev_status, bad);
 }
+
+// --------------------------------------------------------------- restore --
 
 // Token total of the chunk metadata, summed by one wave (every lane gets it).
 __device__ __forceinline__ int64_t wave_total(const int32_t *__restrict__ sizes, int C) {
@@ -213,7 +279,7 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
     int32_t *__restrict__ dev_status) {
   const int64_t rows = max(out_cap, n_cap);
   const int64_t total = rows * W;
-  const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kCopyIlp + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kUnitsPerIter + threadIdx.x;
   U v[kCopyIlp];
   int32_t dst[kCopyIlp];
   int bad = 0;
@@ -230,14 +296,7 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
         if (s >= 0 && s < n_cap) {
           dst[i] = s;
           v[i] = ld_row<NTL>(in + u);
-          if (c == 0 && out_probs != nullptr) {
-            if (prob_bytes == 4)
-              reinterpret_cast<uint32_t *>(out_probs)[s] =
-                  reinterpret_cast<const uint32_t *>(probs)[d];
-            else
-              reinterpret_cast<uint16_t *>(out_probs)[s] =
-                  reinterpret_cast<const uint16_t *>(probs)[d];
-          }
+          if (c == 0 && out_probs != nullptr) copy_prob(probs, d, out_probs, s, prob_bytes);
         }
       }
     }
@@ -253,12 +312,7 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
       if (dst[i] >= 0) st_row<false>(v[i], out + (int64_t)dst[i] * W + c);
       if (d >= n_act && d < n_cap) {
         st_row<false>(zero_unit<U>(), out + u);
-        if (c == 0 && out_probs != nullptr) {
-          if (prob_bytes == 4)
-            reinterpret_cast<uint32_t *>(out_probs)[d] = 0u;
-          else
-            reinterpret_cast<uint16_t *>(out_probs)[d] = 0;
-        }
+        if (c == 0 && out_probs != nullptr) copy_prob(probs, -1, out_probs, d, prob_bytes);
       }
     }
   }
@@ -266,8 +320,7 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
 }
 
 inline unsigned copy_blocks(int64_t units) {
-  const int64_t per = (int64_t)kCopyThreads * kCopyIlp;
-  return (unsigned)((units + per - 1) / per);
+  return (unsigned)((units + kUnitsPerIter - 1) / kUnitsPerIter);
 }
 
 }  // namespace
@@ -276,18 +329,9 @@ hipError_t launch_chunk_map(const int32_t *split_sizes, const int32_t *sorted_id
                             int A, int n_cap, int out_cap, int32_t *row_map,
                             int32_t *padded_offsets, int32_t *dev_status, hipStream_t s) {
   const int G = C / R;
-  const size_t lds = (size_t)(C + (C + 1) + (G + 1) + G) * sizeof(int64_t) +
-                     (size_t)2 * C * sizeof(int32_t);
-  const int blocks = out_cap > 0 ? (out_cap + kMapRowsPerBlock - 1) / kMapRowsPerBlock : 1;
-  if (lds > 65536) {
-    // Large chunk tables need more than the default 64 KiB of dynamic LDS
-    // (gfx950 has 160 KiB per workgroup).
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_map_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(chunk_map_kernel, dim3(blocks), dim3(kMapThreads), lds, s, split_sizes,
+  const size_t lds = chunk_tables_bytes(C, G);
+  const int blocks = out_cap > 0 ? (int)(((int64_t)out_cap + kMapRows - 1) / kMapRows) : 1;
+  hipLaunchKernelGGL(chunk_map_kernel, dim3(blocks), dim3(kCopyThreads), lds, s, split_sizes,
                      sorted_idx, C, R, A, n_cap, out_cap, row_map, padded_offsets, dev_status);
   return hipGetLastError();
 }
@@ -300,7 +344,7 @@ hipError_t launch_pad_copy(const void *in, const void *probs, int prob_bytes, in
   const dim3 grid(copy_blocks(units)), block(kCopyThreads);
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
-  const bool stream = units * 16 * 2 > kStreamBytes;
+  const bool stream = units * unit_bytes * 2 > kStreamBytes;
   switch (unit_bytes) {
     case 16:
       if (stream)
@@ -335,7 +379,7 @@ hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes
   const dim3 grid(copy_blocks(units)), block(kCopyThreads);
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
-  const bool stream = ((int64_t)out_cap + n_cap) * row_units * 16 > kStreamBytes;
+  const bool stream = ((int64_t)out_cap + n_cap) * row_units * unit_bytes > kStreamBytes;
   switch (unit_bytes) {
     case 16:
       if (stream)

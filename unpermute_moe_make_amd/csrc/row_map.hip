@@ -1,4 +1,4 @@
-// Routing row map by a stable counting sort, in three launches.
+// Routing row map by a stable counting sort.
 //
 // d9d permute_with_probs.py (TransformerEngine mask-map permutation),
 // make_row_id_map: per-expert counts per token block, an exclusive scan of
@@ -14,24 +14,33 @@
 // and an OR that finds its bit already set exposes a repeated expert.  The
 // stable in-tile rank of a routed token is then popcount(mask & lanes
 // below), i.e. mbcnt -- no atomic arrival order decides any row.
-//   count: masks -> workspace, per-(expert, block) counts.
-//   scan:  one workgroup scans the E x nb counts (expert-major) into bases
-//          and writes expert_offsets.
-//   write: grid (blocks, expert groups); each wave writes 64 consecutive
-//          row_id_map entries per expert (256-byte coalesced stores).
+//
+//   count:  masks -> workspace, per-(block, expert) counts [nb][E].
+//   write:  each block derives its bases itself -- expert totals, their
+//           exclusive scan, and the counts of the earlier blocks -- then
+//           each wave writes 64 consecutive row_id_map entries per expert of
+//           its expert group (256-byte coalesced stores).  Two launches.
+//   With many blocks (long token counts) the per-block walk over all
+//   earlier blocks would grow quadratically, so a column-scan kernel (one
+//   workgroup per expert, a parallel scan over the blocks) computes the
+//   bases once and the write kernel reads them: three launches.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTokPerBlock = 256;     // 4 waves x 64 tokens
+constexpr int kTokPerBlock = 256;  // 4 waves x 64 tokens
 constexpr int kWavesPerBlock = kTokPerBlock / kWave;
-constexpr int kExpertsPerWrite = 32;  // experts per write workgroup
-constexpr int kScanThreads = 1024;
+constexpr int kFusedMaxBlocks = 64;  // up to 16384 tokens: write derives bases itself
+constexpr int kScanThreads = 256;
+#ifndef MOE_MAP_EXPERTS_PER_WRITE
+#define MOE_MAP_EXPERTS_PER_WRITE 32
+#endif
+constexpr int kExpertsPerWrite = MOE_MAP_EXPERTS_PER_WRITE;  // experts per write workgroup
 
 __global__ __launch_bounds__(kTokPerBlock) void rowmap_count_kernel(
-    const int32_t *__restrict__ topk_idx, int T, int k, int E, int nb,
+    const int32_t *__restrict__ topk_idx, int T, int k, int E,
     unsigned long long *__restrict__ masks, int32_t *__restrict__ counts,
     int32_t *__restrict__ dev_status) {
   extern __shared__ unsigned long long smask[];  // [4][E]
@@ -68,22 +77,20 @@ __global__ __launch_bounds__(kTokPerBlock) void rowmap_count_kernel(
       masks[((int64_t)b * kWavesPerBlock + w) * E + e] = m;
       c += __popcll(m);
     }
-    counts[(int64_t)e * nb + b] = c;
+    counts[(int64_t)b * E + e] = c;
   }
 }
 
-// Exclusive scan of counts[E][nb] in expert-major order, in place; also
-// expert_offsets[e] = base of (e, block 0) and expert_offsets[E] = total.
-__global__ __launch_bounds__(kScanThreads) void rowmap_scan_kernel(
-    int32_t *__restrict__ counts, int n, int nb, int E, int32_t *__restrict__ expert_offsets) {
-  __shared__ int wave_tot[kScanThreads / kWave];
+// Exclusive scan of n ints in LDS by the whole workgroup (any blockDim that
+// is a multiple of 64); returns the total.  Contains barriers.
+__device__ int block_scan_lds(int *a, int n, int *wave_tot) {
   const int tid = threadIdx.x;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
+  const int nth = blockDim.x;
+  const int per = (n + nth - 1) / nth;
   const int beg = min(n, tid * per);
   const int end = min(n, beg + per);
   int sum = 0;
-  for (int i = beg; i < end; i++) sum += counts[i];
-
+  for (int i = beg; i < end; i++) sum += a[i];
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
   int incl = sum;
@@ -92,44 +99,94 @@ __global__ __launch_bounds__(kScanThreads) void rowmap_scan_kernel(
     const int v = __shfl_up(incl, d, kWave);
     if (lane >= d) incl += v;
   }
+  __syncthreads();
   if (lane == kWave - 1) wave_tot[w] = incl;
   __syncthreads();
-  int wbase = 0;
-  for (int i = 0; i < w; i++) wbase += wave_tot[i];
-
-  int run = wbase + incl - sum;
-  int e = beg / nb;
-  int b = beg - e * nb;
+  int base = 0;
+  for (int i = 0; i < w; i++) base += wave_tot[i];
+  int run = base + incl - sum;
   for (int i = beg; i < end; i++) {
-    const int c = counts[i];
-    counts[i] = run;
-    if (b == 0) expert_offsets[e] = run;
+    const int c = a[i];
+    a[i] = run;
     run += c;
-    if (++b == nb) {
-      b = 0;
-      e++;
-    }
   }
-  if (tid == kScanThreads - 1) expert_offsets[E] = wbase + incl;
+  int total = 0;
+  for (int i = 0; i < nth / kWave; i++) total += wave_tot[i];
+  __syncthreads();
+  return total;
 }
 
+// Column scan for long token counts: workgroup e turns counts[.][e] into
+// the exclusive prefix over blocks (in place) and writes the expert total.
+__global__ __launch_bounds__(kScanThreads) void rowmap_colscan_kernel(
+    int32_t *__restrict__ counts, int nb, int E, int32_t *__restrict__ totals) {
+  __shared__ int chunk[kScanThreads * 4];
+  __shared__ int wave_tot[kScanThreads / kWave];
+  const int e = blockIdx.x;
+  int carry = 0;
+  for (int b0 = 0; b0 < nb; b0 += kScanThreads * 4) {
+    const int n = min(kScanThreads * 4, nb - b0);
+    for (int i = threadIdx.x; i < n; i += kScanThreads) chunk[i] = counts[(int64_t)(b0 + i) * E + e];
+    __syncthreads();
+    const int tot = block_scan_lds(chunk, n, wave_tot);
+    for (int i = threadIdx.x; i < n; i += kScanThreads)
+      counts[(int64_t)(b0 + i) * E + e] = carry + chunk[i];
+    carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) totals[e] = carry;
+}
+
+// FUSED: derive totals and the earlier-block prefix from counts[nb][E];
+// otherwise counts already holds the prefix and totals the expert totals.
+// Grid (nb, ceil(E / kExpertsPerWrite)): block (b, y) writes the entries of
+// experts [y*G, y*G+G), G = kExpertsPerWrite, for the block's 256 tokens.
+template <bool FUSED>
 __global__ __launch_bounds__(kTokPerBlock) void rowmap_write_kernel(
-    const unsigned long long *__restrict__ masks, const int32_t *__restrict__ base, int T, int E,
-    int nb, int32_t *__restrict__ row_id_map) {
-  __shared__ unsigned long long smask[kWavesPerBlock][kExpertsPerWrite];
-  __shared__ int32_t sbase[kWavesPerBlock][kExpertsPerWrite];
+    const unsigned long long *__restrict__ masks, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ totals, int T, int E, int nb, int32_t *__restrict__ row_id_map,
+    int32_t *__restrict__ expert_offsets) {
+  extern __shared__ int s_off[];                         // [E] expert offsets
+  __shared__ int s_pre[kExpertsPerWrite];                // rows of earlier blocks
+  __shared__ int s_base[kWavesPerBlock][kExpertsPerWrite];
+  __shared__ unsigned long long s_mask[kWavesPerBlock][kExpertsPerWrite];
+  __shared__ int wave_tot[kTokPerBlock / kWave];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int e0 = blockIdx.y * kExpertsPerWrite;
   const int ne = min(kExpertsPerWrite, E - e0);
+
+  for (int e = tid; e < E; e += kTokPerBlock) {
+    int tot = 0, pre = 0;
+    const bool mine = e >= e0 && e < e0 + ne;
+    if (FUSED) {
+#pragma unroll 8
+      for (int b2 = 0; b2 < nb; b2++) {
+        const int c = counts[(int64_t)b2 * E + e];
+        tot += c;
+        pre += (b2 < b) ? c : 0;
+      }
+    } else {
+      tot = totals[e];
+      if (mine) pre = counts[(int64_t)b * E + e];
+    }
+    s_off[e] = tot;
+    if (mine) s_pre[e - e0] = pre;
+  }
+  __syncthreads();
+  const int total = block_scan_lds(s_off, E, wave_tot);
+  if (b == 0 && blockIdx.y == 0) {
+    for (int e = tid; e < E; e += kTokPerBlock) expert_offsets[e] = s_off[e];
+    if (tid == 0) expert_offsets[E] = total;
+  }
   if (tid < ne) {
     const int e = e0 + tid;
-    int run = base[(int64_t)e * nb + b];
+    int run = s_off[e] + s_pre[tid];
 #pragma unroll
     for (int w = 0; w < kWavesPerBlock; w++) {
       const unsigned long long m = masks[((int64_t)b * kWavesPerBlock + w) * E + e];
-      smask[w][tid] = m;
-      sbase[w][tid] = run;
+      s_mask[w][tid] = m;
+      s_base[w][tid] = run;
       run += __popcll(m);
     }
   }
@@ -140,11 +197,11 @@ __global__ __launch_bounds__(kTokPerBlock) void rowmap_write_kernel(
   const int t = b * kTokPerBlock + tid;
   if (t >= T) return;
   for (int i = 0; i < ne; i++) {
-    const unsigned long long m = smask[w][i];
+    const unsigned long long m = s_mask[w][i];
     // number of routed tokens below this lane in the wave tile
     const unsigned below = __builtin_amdgcn_mbcnt_hi(
         (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-    const int v = ((m >> lane) & 1ull) ? sbase[w][i] + (int)below : -1;
+    const int v = ((m >> lane) & 1ull) ? s_base[w][i] + (int)below : -1;
     row_id_map[(int64_t)(e0 + i) * T + t] = v;
   }
 }
@@ -156,13 +213,30 @@ __global__ void fill_kernel(int32_t *__restrict__ p, int n, int32_t v) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+struct Workspace {
+  unsigned long long *masks;
+  int32_t *counts;
+  int32_t *totals;
+};
+
+Workspace carve(void *ws, int nb, int E) {
+  char *p = reinterpret_cast<char *>(ws);
+  Workspace w;
+  w.masks = reinterpret_cast<unsigned long long *>(p);
+  p += align256((size_t)nb * kWavesPerBlock * E * sizeof(unsigned long long));
+  w.counts = reinterpret_cast<int32_t *>(p);
+  p += align256((size_t)nb * E * sizeof(int32_t));
+  w.totals = reinterpret_cast<int32_t *>(p);
+  return w;
+}
+
 }  // namespace
 
 size_t rowmap_workspace_bytes(int T, int k, int E) {
   (void)k;
   const size_t nb = (size_t)((T + kTokPerBlock - 1) / kTokPerBlock);
   return align256(nb * kWavesPerBlock * (size_t)E * sizeof(unsigned long long)) +
-         align256(nb * (size_t)E * sizeof(int32_t));
+         align256(nb * (size_t)E * sizeof(int32_t)) + align256((size_t)E * sizeof(int32_t));
 }
 
 hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *row_id_map,
@@ -174,18 +248,21 @@ hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *
     return hipGetLastError();
   }
   const int nb = (T + kTokPerBlock - 1) / kTokPerBlock;
-  auto *masks = reinterpret_cast<unsigned long long *>(ws);
-  auto *counts = reinterpret_cast<int32_t *>(
-      reinterpret_cast<char *>(ws) +
-      align256((size_t)nb * kWavesPerBlock * E * sizeof(unsigned long long)));
-  const size_t lds = (size_t)kWavesPerBlock * E * sizeof(unsigned long long);
-  hipLaunchKernelGGL(rowmap_count_kernel, dim3(nb), dim3(kTokPerBlock), lds, s, topk_idx, T, k,
-                     E, nb, masks, counts, dev_status);
-  hipLaunchKernelGGL(rowmap_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, E * nb, nb, E,
-                     expert_offsets);
-  hipLaunchKernelGGL(rowmap_write_kernel,
-                     dim3(nb, (E + kExpertsPerWrite - 1) / kExpertsPerWrite),
-                     dim3(kTokPerBlock), 0, s, masks, counts, T, E, nb, row_id_map);
+  const Workspace w = carve(ws, nb, E);
+  const size_t lds_count = (size_t)kWavesPerBlock * E * sizeof(unsigned long long);
+  const size_t lds_write = (size_t)E * sizeof(int);
+  const dim3 wgrid(nb, (E + kExpertsPerWrite - 1) / kExpertsPerWrite);
+  hipLaunchKernelGGL(rowmap_count_kernel, dim3(nb), dim3(kTokPerBlock), lds_count, s, topk_idx,
+                     T, k, E, w.masks, w.counts, dev_status);
+  if (nb <= kFusedMaxBlocks) {
+    hipLaunchKernelGGL(rowmap_write_kernel<true>, wgrid, dim3(kTokPerBlock), lds_write, s,
+                       w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
+  } else {
+    hipLaunchKernelGGL(rowmap_colscan_kernel, dim3(E), dim3(kScanThreads), 0, s, w.counts, nb,
+                       E, w.totals);
+    hipLaunchKernelGGL(rowmap_write_kernel<false>, wgrid, dim3(kTokPerBlock), lds_write, s,
+                       w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
+  }
   return hipGetLastError();
 }
 
