@@ -71,6 +71,7 @@ def _load():
             "oracle_unpermute": [P, P, P, P, I, I, I, I, L, P],
             "oracle_unpermute_bwd": [P, P, P, P, P, I, I, I, I, L, P, P],
             "oracle_permute_bwd": [P, P, P, P, I, I, I, I, L, P, P],
+            "oracle_unpermute_ep": [P, P, P, P, I, I, I, I, L, I, I, I, P],
             "oracle_chunk_map": [P, P, I, I, I, I, I, P, P],
             "oracle_sort_chunks_and_pad": [P, P, I, I, I, I, P, P, I, I, I, I, P, P, P, P],
             "oracle_unpad_and_restore_chunks": [P, P, I, I, P, P, I, I, I, I, P, P],
@@ -85,6 +86,8 @@ def _load():
         lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
         lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_f32.restype = ctypes.c_float
+        lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
         lib.oracle_fmaf.argtypes = [ctypes.c_float] * 3
         lib.oracle_fmaf.restype = ctypes.c_float
         _lib = lib
@@ -108,6 +111,10 @@ def _check(code, where):
 
 def f32_to_bf16(x: float) -> int:
     return int(_load().oracle_f32_to_bf16(x))
+
+
+def f64_to_bf16(x: float) -> int:
+    return int(_load().oracle_f64_to_bf16(x))
 
 
 def bf16_to_f32(b: int) -> float:
@@ -170,6 +177,22 @@ def unpermute(inp, probs, topk_idx, row_map):
     out = np.zeros((T, H), np.uint16)
     _check(_load().oracle_unpermute(_p(inp), _p(probs), _p(idx), _p(rm), T, H, k, E,
                                     inp.shape[0], _p(out)), "unpermute")
+    return out
+
+
+def unpermute_ep(inp, probs, topk_idx, row_map, ep_size, bf16_partials=True, fp64_cross=False):
+    """EP rank-ordered combine: experts split into ep_size equal ranges."""
+    inp = _arr(inp, np.uint16)
+    idx = _arr(topk_idx, np.int32)
+    rm = _arr(row_map, np.int32)
+    probs = _arr(probs, np.float32)
+    T, k = idx.shape
+    E = rm.shape[0]
+    H = inp.shape[1]
+    out = np.zeros((T, H), np.uint16)
+    _check(_load().oracle_unpermute_ep(_p(inp), _p(probs), _p(idx), _p(rm), T, H, k, E,
+                                       inp.shape[0], ep_size, int(bf16_partials),
+                                       int(fp64_cross), _p(out)), "unpermute_ep")
     return out
 
 

@@ -21,6 +21,10 @@
  *                              and prob-grad row dot products (exact
  *                              products summed in fp64, rounded once).
  *   oracle_permute_bwd      -- slot-order fp32 sum of the k gradient rows.
+ *   oracle_unpermute_ep     -- the same combine with experts split into EP
+ *                              ranks: per-rank slot-order partials (optionally
+ *                              rounded to bf16) added in rank order (fp32 or
+ *                              fp64), then bf16.
  *   oracle_chunk_map        -- padded destination -> source row map.
  *   oracle_sort_chunks_and_pad / oracle_unpad_and_restore_chunks
  *                           -- the two copies driven by that map.
@@ -246,6 +250,97 @@ int oracle_unpermute(const uint16_t *in, const float *probs, const int32_t *topk
                 acc = fmaf(p, bf16_to_f32(in[r * H + h]), acc);
             }
             out[(int64_t)t * H + h] = f32_to_bf16_rne(acc);
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- EP rank-ordered combine (one GPU) ----------------------------------- */
+
+/*
+ * binary64 -> bf16, round to nearest, ties to even, written from the
+ * definition: the bf16 grid near |d| has quantum 2^(e-8) for |d| in
+ * [2^(e-1), 2^e) (8 significant bits), never finer than the smallest bf16
+ * subnormal 2^-133; round |d| / quantum to the nearest integer (ties to
+ * even, nearbyint in the default rounding mode), scale back, and saturate
+ * to infinity above the largest finite bf16.
+ */
+static uint16_t f64_to_bf16_rne(double d)
+{
+    if (isnan(d)) {
+        float f = (float)d;
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        return (uint16_t)((u >> 16) | 0x0040u);
+    }
+    double a = fabs(d);
+    double r;
+    if (a == 0.0 || isinf(a)) {
+        r = a;
+    } else {
+        int e;
+        frexp(a, &e);                           /* a = m * 2^e, m in [0.5, 1) */
+        int qexp = e - 8;
+        if (qexp < -133) qexp = -133;
+        double q = ldexp(1.0, qexp);
+        r = nearbyint(a / q) * q;               /* a / q is exact (power of 2) */
+        const double max_bf16 = ldexp(255.0, 120); /* 0x7F7F: (2 - 2^-7) * 2^127 */
+        if (r > max_bf16) r = INFINITY;
+    }
+    float f = (float)(signbit(d) ? -r : r);     /* exact: r is on the bf16 grid */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+uint16_t oracle_f64_to_bf16(double d) { return f64_to_bf16_rne(d); }
+
+/*
+ * Megatron-core core.transformer.moe.batch_invariant: unpermute adds the
+ * contributions by EP rank, then by top-k slot (_unpermute_loop, the loop
+ * reference); with BF16_RANK_PARTIALS each rank's partial is the fp32
+ * fused multiply-add chain of prob and row in slot order, from zero, rounded
+ * to bf16 (unpermute_with_bf16_rank_partials); CROSS_RANK_FP64 adds the ranks
+ * in fp64.  On one GPU the ranks are expert ranges: the E experts split into
+ * ep_size equal ranges, rank(e) = e / (E / ep_size).
+ *   total = 0 (fp32, or fp64)
+ *   for rank = 0 .. ep_size-1:
+ *       partial = +0.0f
+ *       for j = 0 .. k-1 with rank(topk_idx[t][j]) == rank:
+ *           partial = fmaf(p[t][j], in[r_j][h], partial)
+ *       if bf16_partials: partial = bf16_rne(partial)
+ *       total = total + partial
+ *   out[t][h] = bf16_rne(total)
+ * probs == NULL means unit weights.
+ */
+int oracle_unpermute_ep(const uint16_t *in, const float *probs, const int32_t *topk_idx,
+                        const int32_t *row_id_map, int T, int H, int k, int E, int64_t n_rows,
+                        int ep_size, int bf16_partials, int fp64_cross, uint16_t *out)
+{
+    if (T < 0 || H < 1 || k < 1 || E < 1 || ep_size < 1 || E % ep_size != 0) return ORC_BAD_ARG;
+    int per_rank = E / ep_size;
+    for (int t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++) {
+            float total32 = 0.0f;
+            double total64 = 0.0;
+            for (int rank = 0; rank < ep_size; rank++) {
+                float partial = +0.0f;
+                for (int j = 0; j < k; j++) {
+                    int64_t r;
+                    int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
+                    if (s) return s;
+                    if (topk_idx[(int64_t)t * k + j] / per_rank != rank) continue;
+                    float p = probs ? probs[(int64_t)t * k + j] : 1.0f;
+                    partial = fmaf(p, bf16_to_f32(in[r * H + h]), partial);
+                }
+                if (bf16_partials) partial = bf16_to_f32(f32_to_bf16_rne(partial));
+                if (fp64_cross)
+                    total64 = total64 + (double)partial;
+                else
+                    total32 = total32 + partial;
+            }
+            out[(int64_t)t * H + h] = fp64_cross ? f64_to_bf16_rne(total64)
+                                                 : f32_to_bf16_rne(total32);
         }
     }
     return ORC_OK;

@@ -486,3 +486,140 @@ def test_unpermute_starts_from_positive_zero():
     assert _one_token_unpermute([-0.0, -0.0], None) == 0x0000
     assert _one_token_unpermute([-0.0, -0.0], [0.5, 0.25]) == 0x0000
     assert _one_token_unpermute([-0.0], None) == 0x0000
+
+
+# ------------------------------------------- EP rank-ordered combine -------
+
+def _rn(q: Fraction, mant_bits: int, min_exp: int = -126) -> Fraction:
+    """Round an exact rational to mant_bits significant bits (ties to even),
+    with the subnormal quantum of a format whose smallest normal exponent is
+    min_exp; independent of the oracle's conversions."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, min_exp)
+    quantum = Fraction(2) ** (e - (mant_bits - 1))
+    m = a / quantum
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * n * quantum
+
+
+def _bf16_bits_of(q: Fraction, negative: bool = None) -> int:
+    """bf16 pattern of RN8(q): sign kept for a zero result (RN of a tiny
+    negative is -0), infinity above the largest finite bf16."""
+    neg = (q < 0) if negative is None else negative
+    r = _rn(abs(q), 8)
+    if r > Fraction(255) * Fraction(2) ** 120:
+        mag = 0x7F80
+    else:
+        mag = int(np.array([float(r)], np.float32).view(np.uint32)[0] >> 16)
+    return mag | (0x8000 if neg else 0)
+
+
+def _ep_reference(P, probs, idx, m, ep, bf16_partials, fp64_cross):
+    """The rank-ordered combine with exact rationals: fp32 FMAs as RN24 of the
+    exact p*x + acc, bf16 partials as RN8, fp32 / fp64 rank sums as RN24 / RN53."""
+    T, k = idx.shape
+    E = m.shape[0]
+    per = E // ep
+    H = P.shape[1]
+    Pf = _bf16_to_f32(P)
+    out = np.empty((T, H), np.uint16)
+    for t in range(T):
+        for h in range(H):
+            total = Fraction(0)
+            for rank in range(ep):
+                acc = Fraction(0)
+                for j in range(k):
+                    e = int(idx[t, j])
+                    if e // per != rank:
+                        continue
+                    p = Fraction(1) if probs is None else Fraction(float(probs[t, j]))
+                    acc = _rn(p * Fraction(float(Pf[m[e, t], h])) + acc, 24)
+                if bf16_partials:
+                    acc = _rn(acc, 8)
+                total = _rn(total + acc, 53, -1022) if fp64_cross else _rn(total + acc, 24)
+            out[t, h] = _bf16_bits_of(total)
+    return out
+
+
+@pytest.mark.parametrize("ep,bf16_partials,fp64_cross", [(2, True, False), (4, True, True),
+                                                         (4, False, False), (8, False, True),
+                                                         (1, True, False)])
+def test_unpermute_ep_exact_rational(ep, bf16_partials, fp64_cross):
+    T, H, E, k = 5, 6, 8, 4
+    w = _routed(T, H, E, k, seed=200 + ep)
+    idx = w.topk_idx.numpy()
+    m, _ = oracle.row_id_map(idx, E)
+    rng = np.random.default_rng(ep)
+    P = _to_bf16_torch(rng.standard_normal((T * k, H)).astype(np.float32))
+    got = oracle.unpermute_ep(P, w.probs.numpy(), idx, m, ep, bf16_partials, fp64_cross)
+    ref = _ep_reference(P, w.probs.numpy(), idx, m, ep, bf16_partials, fp64_cross)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_unpermute_ep_one_rank_is_the_plain_combine():
+    w = _routed(60, 40, 16, 6, seed=210)
+    idx = w.topk_idx.numpy()
+    m, _ = oracle.row_id_map(idx, 16)
+    P = _to_bf16_torch(np.random.default_rng(3).standard_normal((360, 40)).astype(np.float32))
+    plain = oracle.unpermute(P, w.probs.numpy(), idx, m)
+    for partials in (True, False):
+        for fp64 in (True, False):
+            np.testing.assert_array_equal(
+                oracle.unpermute_ep(P, w.probs.numpy(), idx, m, 1, partials, fp64), plain)
+
+
+def _one_token_ep(x_vals, p_vals, experts, E, ep, partials, fp64):
+    k = len(x_vals)
+    idx = np.array([experts], np.int32)
+    m, _ = oracle.row_id_map(idx, E)
+    P = np.zeros((k, 1), np.uint16)
+    bits = _to_bf16_torch(np.array(x_vals, np.float32))
+    for j in range(k):
+        P[m[experts[j], 0], 0] = bits[j]
+    probs = None if p_vals is None else np.array([p_vals], np.float32)
+    return int(oracle.unpermute_ep(P, probs, idx, m, ep, partials, fp64)[0, 0])
+
+
+def test_unpermute_ep_crafted_rank_order():
+    """Slots (2^30 -> rank 1, 1 -> rank 0, -2^30 -> rank 1): by rank the 1 is
+    added to the cancelled rank-1 partial (result 1); in plain slot order it is
+    absorbed by 2^30 (result 0)."""
+    x = [2.0 ** 30, 1.0, -(2.0 ** 30)]
+    assert _one_token_ep(x, None, [2, 0, 3], 4, 2, True, False) == 0x3F80
+    assert _one_token_unpermute(x, None) == 0x0000
+
+
+def test_unpermute_ep_crafted_fp64_cross_sum():
+    """Partials 1+2^-8, 2^-30, 2^-30 (fp32 partials): the fp32 rank sum drops
+    the small terms and lands on the bf16 tie 1+2^-8 (-> even, 0x3F80); the
+    fp64 sum keeps them, above the tie (-> 0x3F81).  With bf16 partials the
+    first partial already rounds to 1 (tie to even)."""
+    x = [1.0, 2.0 ** -30, 2.0 ** -30]
+    p = [1.0 + 2.0 ** -8, 1.0, 1.0]
+    assert _one_token_ep(x, p, [0, 1, 2], 3, 3, False, False) == 0x3F80
+    assert _one_token_ep(x, p, [0, 1, 2], 3, 3, False, True) == 0x3F81
+    assert _one_token_ep(x, p, [0, 1, 2], 3, 3, True, True) == 0x3F80
+
+
+def test_f64_to_bf16_matches_exact_rounding():
+    rng = np.random.default_rng(4)
+    vals = np.concatenate([rng.standard_normal(2000),
+                           rng.standard_normal(300) * 1e-39, rng.standard_normal(300) * 1e-43,
+                           rng.standard_normal(300) * 3e38,
+                           np.array([0.0, 1.0 + 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -40,
+                                     3.3961e38, 3.3962e38, 2.0 ** -134, 2.0 ** -134 * 1.5])])
+    for v in vals:
+        got = oracle.f64_to_bf16(float(v))
+        exp = _bf16_bits_of(Fraction(float(v)), negative=bool(np.signbit(v)))
+        assert got == exp, (v, hex(got), hex(exp))
