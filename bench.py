@@ -156,6 +156,7 @@ class Step:
     def __init__(self):
         self.ops = []
         self.keep = []
+        self.extra = []   # (name, bytes, fn, args) timed outside the step
 
     def add(self, name, fn, *args):
         self.ops.append((name, fn, args))
@@ -207,6 +208,16 @@ def build_routed(m, w):
              k, E, n, p(dP), p(dprob), None,)
     step.add("permute_bwd", lib.moe_permute_bwd, p(dP), p(d_pp), p(idx), p(rm), T, H, k, E, n,
              p(dx), p(dprob2), None,)
+    # Rows beyond the step (SURVEY "next" rows), timed on their own.
+    y_ep = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    step.keep.append(y_ep)
+    ub = routed_bytes(T, H, E, k)["unpermute"]
+    step.extra = [
+        ("unpermute_ep8_bf16partials", ub, lib.moe_unpermute_ep,
+         (p(P), p(probs), p(idx), p(rm), T, H, k, E, n, 8, 1, p(y_ep), None)),
+        ("unpermute_ep8_bf16partials_fp64", ub, lib.moe_unpermute_ep,
+         (p(P), p(probs), p(idx), p(rm), T, H, k, E, n, 8, 3, p(y_ep), None)),
+    ]
     return step, routed_bytes(T, H, E, k)
 
 
@@ -406,6 +417,24 @@ def main():
         gms = (time.perf_counter() - t0) / K * 1e3
         result["graph_replay"] = {"ms_per_step": round(gms, 4),
                                   "GBps": round(step_bytes / (gms * 1e-3) / 1e9, 1)}
+    if step.extra:
+        extra = {}
+        for n, nbytes, fn, a in step.extra:
+            for _ in range(3):
+                fn(*a, sv)
+            evx = [(hev.create(), hev.create()) for _ in range(K2)]
+            for e0, e1 in evx:
+                hev.record(e0, sv)
+                st = fn(*a, sv)
+                hev.record(e1, sv)
+                if st != 0:
+                    raise RuntimeError(f"{n}: status {st}")
+            torch.cuda.synchronize()
+            us = sum(hev.elapsed_us(e0, e1) for e0, e1 in evx) / K2
+            extra[n] = {"us_mean": round(us, 2), "bytes": nbytes,
+                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "pct_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        result["extra_ops"] = extra
     if args.copy_probe > 0:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")

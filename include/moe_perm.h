@@ -165,6 +165,35 @@ MOE_PERM_API int moe_unpermute(const void *in, const float *probs, const int32_t
                                int32_t *dev_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Unpermute with an EP rank-ordered combine, on one GPU.
+ *
+ * [MCORE-BI] unpermute / _unpermute_loop (contributions added by EP rank,
+ * then by top-k slot), _rank_tree_unpermute_kernel with BF16_RANK_PARTIALS
+ * and CROSS_RANK_FP64, unpermute_with_bf16_rank_partials.  The experts split
+ * into ep_size equal ranges; rank(e) = e / (num_experts / ep_size):
+ *   total = 0                                   (fp32, or fp64 with
+ *                                                MOE_EP_FP64_CROSS)
+ *   for rank = 0 .. ep_size-1:
+ *     partial = +0.0f
+ *     for j in slot order with rank(topk_idx[t][j]) == rank:
+ *       partial = fmaf(probs[t][j], in[r(t,j)][h], partial)
+ *     if MOE_EP_BF16_PARTIALS: partial = bf16_rne(partial)
+ *     total += partial
+ *   out[t][h] = bf16_rne(total)                 (fp64 -> bf16 rounded once)
+ * ep_size == 1 gives the same bits as moe_unpermute.  The gradient of this
+ * combine (rounding steps taken as identity) is the one moe_unpermute_bwd
+ * computes.  Arguments as moe_unpermute, plus ep_size (a divisor of
+ * num_experts) and flags.
+ * ------------------------------------------------------------------------ */
+#define MOE_EP_BF16_PARTIALS 0x1
+#define MOE_EP_FP64_CROSS 0x2
+MOE_PERM_API int moe_unpermute_ep(const void *in, const float *probs, const int32_t *topk_idx,
+                                  const int32_t *row_id_map, int num_tokens, int hidden,
+                                  int topk, int num_experts, int num_in_rows, int ep_size,
+                                  int flags, void *out, int32_t *dev_status,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Unpermute backward.
  *
  * [TE-mask] _unpermute_bwd_with_merging_probs_kernel; [MCORE-BI]

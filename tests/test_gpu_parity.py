@@ -81,11 +81,11 @@ def oracle_rows(idx, row_map):
     return row_map[idx, np.arange(T)[:, None]]
 
 
-def sub_problem(idx, sample):
+def sub_problem(idx, sample, E=None):
     """Top-k and a row map for a token subset whose rows are i*k + j."""
     sidx = idx[sample]
     s, k = sidx.shape
-    E = int(idx.max()) + 1
+    E = int(idx.max()) + 1 if E is None else E
     smap = np.full((E, s), -1, np.int32)
     for i in range(s):
         for j in range(k):
@@ -238,6 +238,62 @@ def test_unpermute_configs(m, name, weighted):
         rows = bits(P[torch.from_numpy(r).to(DEV)])
         ref = oracle.unpermute(rows, None if p_np is None else p_np[sample], sidx, smap)
         assert_bits_equal(bits(out)[sample], ref, "unpermute sample")
+
+
+@pytest.mark.parametrize("name,ep", [("tiny", 4), ("finegrain", 8), ("finegrain", 64),
+                                     ("skewed", 8), ("skewed", 32)])
+@pytest.mark.parametrize("partials,fp64", [(True, False), (True, True), (False, False)])
+def test_unpermute_ep_configs(m, name, ep, partials, fp64):
+    w, ref_map, _ = routed(name)
+    T, H, k, E = w.T, w.H, w.k, w.num_experts
+    say(f"unpermute_ep {name} ep={ep} bf16_partials={partials} fp64={fp64}")
+    _, idx, probs, _ = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    P = workloads.random_rows(T * k, H, seed=81, device=DEV)
+    out = sentinel_bf16((T, H))
+    m.moe_unpermute_ep(P, idx, rm, ep, probs, bf16_partials=partials, fp64_cross=fp64, out=out)
+    if T <= 4096:
+        ref = oracle.unpermute_ep(bits(P), w.probs.numpy(), w.topk_idx.numpy(), ref_map, ep,
+                                  partials, fp64)
+        assert_bits_equal(bits(out), ref, "unpermute_ep")
+    else:
+        sample = np.sort(np.random.default_rng(5).choice(T, 384, replace=False))
+        r = oracle_rows(w.topk_idx.numpy(), ref_map)[sample].flatten()
+        sidx, smap = sub_problem(w.topk_idx.numpy(), sample, E)
+        rows = bits(P[torch.from_numpy(r).to(DEV)])
+        ref = oracle.unpermute_ep(rows, w.probs.numpy()[sample], sidx, smap, ep, partials, fp64)
+        assert_bits_equal(bits(out)[sample], ref, "unpermute_ep sample")
+
+
+def test_unpermute_ep_one_rank_equals_unpermute(m):
+    w, ref_map, _ = routed("finegrain")
+    say("unpermute_ep ep=1 vs unpermute")
+    _, idx, probs, _ = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    P = workloads.random_rows(w.T * w.k, w.H, seed=82, device=DEV)
+    y = m.moe_unpermute(P, idx, rm, probs)
+    for partials in (True, False):
+        for fp64 in (True, False):
+            y1 = m.moe_unpermute_ep(P, idx, rm, 1, probs, bf16_partials=partials,
+                                    fp64_cross=fp64)
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+
+
+@pytest.mark.parametrize("T,H,E,k,ep", [(37, 7, 12, 3, 3), (64, 64, 16, 9, 4), (40, 136, 80, 64, 8),
+                                        (9, 20480, 8, 8, 8), (50, 24, 6, 6, 6), (33, 72, 40, 5, 1)])
+def test_unpermute_ep_edges(m, T, H, E, k, ep):
+    say(f"unpermute_ep edge T={T} H={H} E={E} k={k} ep={ep}")
+    w = workloads.random_routed(T, H, E, k, seed=H + 7 * k)
+    ref_map, _ = oracle.row_id_map(w.topk_idx.numpy(), E)
+    _, idx, probs, _ = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    P = workloads.random_rows(T * k, H, seed=6, device=DEV)
+    for partials, fp64, use_p in ((True, False, True), (False, True, True), (True, True, False)):
+        y = m.moe_unpermute_ep(P, idx, rm, ep, probs if use_p else None, bf16_partials=partials,
+                               fp64_cross=fp64, out=sentinel_bf16((T, H)))
+        ref = oracle.unpermute_ep(bits(P), w.probs.numpy() if use_p else None,
+                                  w.topk_idx.numpy(), ref_map, ep, partials, fp64)
+        assert_bits_equal(bits(y), ref, f"unpermute_ep {partials} {fp64} {use_p}")
 
 
 @pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
@@ -641,3 +697,53 @@ def test_chunk_graph_replay(m):
                                                         cw.N_cap)
         assert_bits_equal(bits(back), ref_b, f"replay {rep} restored")
         assert_bits_equal(back_p.cpu().numpy(), ref_bp, f"replay {rep} restored probs")
+
+
+def _assert_bits_nan_aware(got, exp, what):
+    """Bit-exact, except that IEEE 754 leaves the payload of a NaN produced by
+    arithmetic open: where the oracle gives a NaN the kernel must give a NaN."""
+    got = np.asarray(got).astype(np.uint16)
+    exp = np.asarray(exp).astype(np.uint16)
+    nan_e = (exp & 0x7F80) == 0x7F80
+    nan_e &= (exp & 0x007F) != 0
+    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x007F) != 0)
+    assert np.array_equal(nan_g, nan_e), f"{what}: NaN positions differ"
+    assert_bits_equal(got[~nan_e], exp[~nan_e], what)
+
+
+def test_special_values(m):
+    """Infinities, NaNs, subnormals, signed zeros, values near the bf16 maximum
+    and rounding ties through the combine, its backward and the permute bwd."""
+    T, H, E, k = 64, 64, 8, 4
+    say("special values")
+    w = workloads.random_routed(T, H, E, k, seed=77)
+    ref_map, _ = oracle.row_id_map(w.topk_idx.numpy(), E)
+    rng = np.random.default_rng(9)
+    P = workloads.bf16_bits(workloads.random_rows(T * k, H, seed=8)).copy()
+    specials = np.array([0x7F80, 0xFF80, 0x7FC1, 0xFFA3, 0x0001, 0x8003, 0x007F, 0x7F7F, 0xFF7F,
+                         0x8000, 0x0000, 0x3F81, 0x0080], np.uint16)
+    pos = rng.choice(P.size, 600, replace=False)
+    P.ravel()[pos] = rng.choice(specials, 600)
+    probs = w.probs.numpy().copy()
+    probs.ravel()[rng.choice(probs.size, 40, replace=False)] = 1.0 + 2.0 ** -8
+    probs.ravel()[rng.choice(probs.size, 20, replace=False)] = 1e-30
+    probs.ravel()[rng.choice(probs.size, 10, replace=False)] = 3e38
+    idx = w.topk_idx.to(DEV)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    Pd = torch.from_numpy(P.view(np.int16)).to(DEV).view(torch.bfloat16)
+    pd = torch.from_numpy(probs).to(DEV)
+    ib = w.topk_idx.numpy()
+    y = m.moe_unpermute(Pd, idx, rm, pd)
+    _assert_bits_nan_aware(bits(y), oracle.unpermute(P, probs, ib, ref_map), "unpermute")
+    for partials, fp64 in ((True, False), (False, True), (True, True)):
+        y = m.moe_unpermute_ep(Pd, idx, rm, 4, pd, bf16_partials=partials, fp64_cross=fp64)
+        _assert_bits_nan_aware(bits(y), oracle.unpermute_ep(P, probs, ib, ref_map, 4, partials,
+                                                             fp64), "unpermute_ep")
+    dy = P[:T].copy()
+    dyd = torch.from_numpy(dy.view(np.int16)).to(DEV).view(torch.bfloat16)
+    d_in, _ = m.moe_unpermute_bwd(dyd, idx, rm, pd, Pd, probs_grad=False)
+    ref_in, _ = oracle.unpermute_bwd(dy, None, probs, ib, ref_map)
+    _assert_bits_nan_aware(bits(d_in), ref_in, "unpermute_bwd act grad")
+    d_x, _ = m.moe_permute_bwd(Pd, idx, rm)
+    ref_x, _ = oracle.permute_bwd(P, None, ib, ref_map)
+    _assert_bits_nan_aware(bits(d_x), ref_x, "permute_bwd")

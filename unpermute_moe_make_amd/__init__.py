@@ -6,6 +6,7 @@ with a thin ctypes binding whose functions carry the C names:
   moe_make_row_id_map                 stable counting-sort routing row map
   moe_permute / moe_permute_bwd       row scatter-copy and its gradient
   moe_unpermute / moe_unpermute_bwd   fixed slot-order FMA combine, gradient
+  moe_unpermute_ep                    the combine with EP rank-ordered partials
   moe_sort_chunks_and_pad(_bwd)       fused chunk regroup + zero padding
   moe_unpad_and_restore_chunks(_bwd)  the matching restore
 
@@ -17,6 +18,8 @@ from ._binding import (  # noqa: F401
     DEV_BAD_ROW,
     DEV_DUP_EXPERT,
     DEV_OVERFLOW,
+    EP_BF16_PARTIALS,
+    EP_FP64_CROSS,
     EXPORTED,
     MoeError,
     library_path,
@@ -30,4 +33,5 @@ from ._binding import (  # noqa: F401
     moe_unpad_and_restore_chunks_bwd,
     moe_unpermute,
     moe_unpermute_bwd,
+    moe_unpermute_ep,
 )

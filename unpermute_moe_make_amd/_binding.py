@@ -35,6 +35,7 @@ _SIGS = {
     "moe_make_row_id_map": ([_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
     "moe_permute": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_unpermute": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "moe_unpermute_ep": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_unpermute_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_permute_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_sort_chunks_and_pad": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P,
@@ -58,6 +59,10 @@ DEV_DUP_EXPERT = 0x2
 DEV_BAD_ROW = 0x4
 DEV_BAD_CHUNKS = 0x8
 DEV_OVERFLOW = 0x10
+
+# moe_unpermute_ep flags (include/moe_perm.h).
+EP_BF16_PARTIALS = 0x1
+EP_FP64_CROSS = 0x2
 
 
 class MoeError(RuntimeError):
@@ -205,6 +210,28 @@ def moe_unpermute(inp: torch.Tensor, topk_idx: torch.Tensor, row_id_map: torch.T
     _check(_lib.moe_unpermute(_ptr(inp), _ptr(probs), _ptr(topk_idx), _ptr(row_id_map), T, H, k,
                               E, T * k, _ptr(out), _ptr(_status_arg(dev_status)),
                               _stream(stream)), "moe_unpermute")
+    return out
+
+
+def moe_unpermute_ep(inp: torch.Tensor, topk_idx: torch.Tensor, row_id_map: torch.Tensor,
+                     ep_size: int, probs: Optional[torch.Tensor] = None, *,
+                     bf16_partials: bool = True, fp64_cross: bool = False, out=None,
+                     dev_status=None, stream=None) -> torch.Tensor:
+    """Rank-ordered combine: per-EP-rank slot-order fmaf partials (optionally
+    bf16-rounded) added in rank order (fp32 or fp64), then bf16."""
+    T, k, E = _routing(topk_idx, row_id_map)
+    _bf16_like_2d(inp, "inp")
+    H = inp.shape[1]
+    if inp.shape[0] != T * k:
+        raise ValueError("inp must have num_tokens*topk rows")
+    _opt(probs, "probs", torch.float32, (T, k))
+    out = torch.empty((T, H), dtype=inp.dtype, device=inp.device) if out is None else \
+        _need(out, "out", inp.dtype, (T, H))
+    flags = (EP_BF16_PARTIALS if bf16_partials else 0) | (EP_FP64_CROSS if fp64_cross else 0)
+    _check(_lib.moe_unpermute_ep(_ptr(inp), _ptr(probs), _ptr(topk_idx), _ptr(row_id_map), T, H,
+                                 k, E, T * k, ep_size, flags, _ptr(out),
+                                 _ptr(_status_arg(dev_status)), _stream(stream)),
+           "moe_unpermute_ep")
     return out
 
 

@@ -134,6 +134,27 @@ MOE_PERM_API int moe_unpermute(const void *in, const float *probs, const int32_t
                                         vec_ok(H, in, out), stream));
 }
 
+MOE_PERM_API int moe_unpermute_ep(const void *in, const float *probs, const int32_t *topk_idx,
+                                  const int32_t *row_id_map, int num_tokens, int hidden,
+                                  int topk, int num_experts, int num_in_rows, int ep_size,
+                                  int flags, void *out, int32_t *dev_status,
+                                  hipStream_t stream) {
+  const int T = num_tokens, H = hidden, k = topk, E = num_experts;
+  int st = check_rows(T, H, k, E, num_in_rows);
+  if (st) return st;
+  if (ep_size < 1 || E % ep_size != 0) return MOE_ERR_SHAPE;
+  if (flags & ~(MOE_EP_BF16_PARTIALS | MOE_EP_FP64_CROSS)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!in || !topk_idx || !row_id_map || !out) return MOE_ERR_NULL;
+  if (!aligned(in, 2) || !aligned(out, 2) || !aligned(probs, 4) || !aligned(topk_idx, 4) ||
+      !aligned(row_id_map, 4) || !aligned(dev_status, 4))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_combine_ep(
+      in, probs, topk_idx, row_id_map, T, H, k, E, num_in_rows, ep_size,
+      (flags & MOE_EP_BF16_PARTIALS) != 0, (flags & MOE_EP_FP64_CROSS) != 0, out, dev_status,
+      vec_ok(H, in, out), stream));
+}
+
 MOE_PERM_API int moe_unpermute_bwd(const void *d_out, const void *fwd_in, const float *probs,
                                    const int32_t *topk_idx, const int32_t *row_id_map,
                                    int num_tokens, int hidden, int topk, int num_experts,

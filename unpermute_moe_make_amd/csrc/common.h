@@ -37,16 +37,34 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_one(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // fp32 -> bf16, IEEE round to nearest, ties to even, on the 16 discarded
-// bits (adding 0x7fff plus the kept lsb carries exactly when the discarded
-// part is above half, or equal to half with an odd kept part).  NaN keeps
-// its sign and upper payload and gets the quiet bit.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rounded;
-}
+// bits; a NaN keeps its sign and upper payload and gets the quiet bit.  On
+// gfx950 the conversion is one instruction for two values
+// (v_cvt_pk_bf16_f32, which the compiler emits for a float -> __bf16
+// conversion); on MI355X it was checked equal, for all 2^32 fp32 inputs, to
+// the integer form: (u + 0x7fff + ((u >> 16) & 1)) >> 16 for non-NaN u,
+// (u >> 16) | 0x40 for NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_t b = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// fp64 -> bf16 RNE without double rounding: truncate to fp32 and OR the
+// sticky bit into its last place (round to odd keeps 16 guard bits), then
+// round that fp32 value to bf16 as above.
+__device__ __forceinline__ uint32_t f64_to_bf16(double d) {
+  const float f = __double2float_rz(d);
+  uint32_t u = __float_as_uint(f);
+  if (d == d && (double)f != d) u |= 1u;
+  return f32_to_bf16(__uint_as_float(u));
+}
+// Round an fp32 value to bf16 precision, keeping it as fp32.
+__device__ __forceinline__ float round_to_bf16(float f) {
+  return __uint_as_float(f32_to_bf16(f) << 16);
 }
 
 // A unit of a bf16 row: 8 elements in a 16-byte vector, or 1 element.

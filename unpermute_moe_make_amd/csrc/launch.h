@@ -24,6 +24,10 @@ hipError_t launch_combine(const void *in, const float *probs, const int32_t *top
                           const int32_t *row_id_map, int T, int H, int k, int E, int n_rows,
                           void *out, const float *gather_src, float *gather_dst,
                           int32_t *dev_status, bool vec, hipStream_t s);
+hipError_t launch_combine_ep(const void *in, const float *probs, const int32_t *topk_idx,
+                             const int32_t *row_id_map, int T, int H, int k, int E, int n_rows,
+                             int ep_size, bool bf16_partials, bool fp64_cross, void *out,
+                             int32_t *dev_status, bool vec, hipStream_t s);
 hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float *probs,
                               const int32_t *topk_idx, const int32_t *row_id_map, int T, int H,
                               int k, int E, int n_rows, void *d_in, float *d_probs,

@@ -16,6 +16,8 @@
 // acc = fmaf(p_j, x_j, acc) for j = 0..k-1 in slot order, then one
 // round-to-nearest-even to bf16.  The chain is per element, so the result
 // does not depend on the launch shape.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -170,6 +172,123 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
   for (int i = 0; i < VPT; i++) {
     const int64_t c = c0 + (int64_t)i * blockDim.x;
     if (c < V) st_row<NT>(Unit::pack(acc[i]), orow + c);
+  }
+}
+
+// ------------------------------------------------ EP rank-ordered combine --
+
+// Megatron-core batch_invariant unpermute with experts split into EP ranks
+// (rank(e) = e / per_rank): per rank, the fp32 fmaf chain of its slots in
+// slot order from zero (optionally rounded to bf16); the partials are added
+// in rank order from zero (fp32, or fp64 when FP64), then rounded to bf16.
+// Ranks without slots contribute +0, which cannot change a sum that started
+// from +0, so only the ranks present in the token are visited.  The slots
+// are ordered by (rank, slot) once per token in LDS.
+template <int EPV, int VPT, bool NT, bool FP64>
+__global__ __launch_bounds__(kRowThreads) void combine_ep_kernel(
+    const typename Bf16Unit<EPV>::T *__restrict__ in, const float *__restrict__ probs,
+    const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
+    int64_t V, int k, int E, int n_rows, int per_rank, int bf16_partials,
+    typename Bf16Unit<EPV>::T *__restrict__ out, int32_t *__restrict__ dev_status) {
+  using Unit = Bf16Unit<EPV>;
+  using U = typename Unit::T;
+  using Acc = typename std::conditional<FP64, double, float>::type;
+  constexpr int KB = 8;
+  __shared__ int64_t srow[kMaxTopk];
+  __shared__ float sp[kMaxTopk];
+  __shared__ int srank[kMaxTopk];
+  __shared__ int sorder[kMaxTopk];
+  const int t = blockIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
+
+  const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
+  if (threadIdx.x < k) {
+    const int j = threadIdx.x;
+    sp[j] = probs != nullptr ? probs[(int64_t)t * k + j] : 1.0f;
+    const int e = topk_idx[(int64_t)t * k + j];
+    srank[j] = ((unsigned)e < (unsigned)E) ? e / per_rank : 0;
+    if (blockIdx.y == 0) report(dev_status, bad);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // stable insertion sort of the slots by rank
+    for (int j = 0; j < k; j++) {
+      int i = j;
+      while (i > 0 && srank[sorder[i - 1]] > srank[j]) {
+        sorder[i] = sorder[i - 1];
+        i--;
+      }
+      sorder[i] = j;
+    }
+  }
+  __syncthreads();
+
+  Acc total[VPT][EPV];
+  float acc[VPT][EPV];
+#pragma unroll
+  for (int i = 0; i < VPT; i++)
+#pragma unroll
+    for (int e = 0; e < EPV; e++) {
+      total[i][e] = (Acc)0;
+      acc[i][e] = 0.0f;
+    }
+  int cur_rank = -1;
+  for (int s0 = 0; s0 < k; s0 += KB) {
+    U vals[KB][VPT];
+#pragma unroll
+    for (int ss = 0; ss < KB; ss++) {
+      const int s = s0 + ss;
+      const int64_t r = (s < k) ? srow[sorder[s]] : -1;
+#pragma unroll
+      for (int i = 0; i < VPT; i++) {
+        const int64_t c = c0 + (int64_t)i * blockDim.x;
+        vals[ss][i] = (r >= 0 && c < V) ? ld_row<NT>(in + r * V + c) : Unit::zero();
+      }
+    }
+#pragma unroll
+    for (int ss = 0; ss < KB; ss++) {
+      const int s = s0 + ss;
+      if (s >= k) break;
+      const int j = sorder[s];
+      const int rank = srank[j];
+      if (rank != cur_rank) {
+        if (cur_rank >= 0) {
+#pragma unroll
+          for (int i = 0; i < VPT; i++)
+#pragma unroll
+            for (int e = 0; e < EPV; e++) {
+              const float part = bf16_partials ? round_to_bf16(acc[i][e]) : acc[i][e];
+              total[i][e] = total[i][e] + (Acc)part;
+              acc[i][e] = 0.0f;
+            }
+        }
+        cur_rank = rank;
+      }
+      const float p = sp[j];
+#pragma unroll
+      for (int i = 0; i < VPT; i++) {
+        float f[EPV];
+        Unit::unpack(vals[ss][i], f);
+#pragma unroll
+        for (int e = 0; e < EPV; e++) acc[i][e] = __builtin_fmaf(p, f[e], acc[i][e]);
+      }
+    }
+  }
+  U *orow = out + (int64_t)t * V;
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    float res[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; e++) {
+      const float part = bf16_partials ? round_to_bf16(acc[i][e]) : acc[i][e];
+      const Acc tot = total[i][e] + (Acc)part;
+      if constexpr (FP64)
+        res[e] = __uint_as_float(f64_to_bf16(tot) << 16);   // exact bf16 value
+      else
+        res[e] = tot;
+    }
+    const int64_t c = c0 + (int64_t)i * blockDim.x;
+    if (c < V) st_row<NT>(Unit::pack(res), orow + c);
   }
 }
 
@@ -426,6 +545,35 @@ void combine_bwd_dispatch(const void *d_out, const void *fwd_in, const float *pr
   }
 }
 
+template <int EPV, bool NT, bool FP64>
+void combine_ep_dispatch(const void *in, const float *probs, const int32_t *topk_idx,
+                         const int32_t *row_id_map, int T, int64_t V, int k, int E, int n_rows,
+                         int per_rank, int bf16_partials, void *out, int32_t *st,
+                         hipStream_t s) {
+  using U = typename Bf16Unit<EPV>::T;
+  const RowShape sh = row_shape(V, true);
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const U *ip = static_cast<const U *>(in);
+  U *op = static_cast<U *>(out);
+  switch (sh.vpt) {
+    case 1:
+      hipLaunchKernelGGL((combine_ep_kernel<EPV, 1, NT, FP64>), grid, block, 0, s, ip, probs,
+                         topk_idx, row_id_map, T, V, k, E, n_rows, per_rank, bf16_partials, op,
+                         st);
+      break;
+    case 2:
+      hipLaunchKernelGGL((combine_ep_kernel<EPV, 2, NT, FP64>), grid, block, 0, s, ip, probs,
+                         topk_idx, row_id_map, T, V, k, E, n_rows, per_rank, bf16_partials, op,
+                         st);
+      break;
+    default:
+      hipLaunchKernelGGL((combine_ep_kernel<EPV, 4, NT, FP64>), grid, block, 0, s, ip, probs,
+                         topk_idx, row_id_map, T, V, k, E, n_rows, per_rank, bf16_partials, op,
+                         st);
+      break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const void *x, const float *probs, const int32_t *topk_idx,
@@ -471,6 +619,40 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
   else
     combine_bwd_dispatch<1, false>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H, k, E,
                                    n_rows, d_in, d_probs, dev_status, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_combine_ep(const void *in, const float *probs, const int32_t *topk_idx,
+                             const int32_t *row_id_map, int T, int H, int k, int E, int n_rows,
+                             int ep_size, bool bf16_partials, bool fp64_cross, void *out,
+                             int32_t *dev_status, bool vec, hipStream_t s) {
+  const int per_rank = E / ep_size;
+  const int bp = bf16_partials ? 1 : 0;
+  const bool stream = 2ll * H * ((int64_t)n_rows + T) > kStreamBytes;
+  if (vec) {
+    const int64_t V = H / 8;
+    if (fp64_cross)
+      stream ? combine_ep_dispatch<8, true, true>(in, probs, topk_idx, row_id_map, T, V, k, E,
+                                                  n_rows, per_rank, bp, out, dev_status, s)
+             : combine_ep_dispatch<8, false, true>(in, probs, topk_idx, row_id_map, T, V, k, E,
+                                                   n_rows, per_rank, bp, out, dev_status, s);
+    else
+      stream ? combine_ep_dispatch<8, true, false>(in, probs, topk_idx, row_id_map, T, V, k, E,
+                                                   n_rows, per_rank, bp, out, dev_status, s)
+             : combine_ep_dispatch<8, false, false>(in, probs, topk_idx, row_id_map, T, V, k, E,
+                                                    n_rows, per_rank, bp, out, dev_status, s);
+  } else {
+    if (fp64_cross)
+      combine_ep_dispatch<1, false, true>(in, probs, topk_idx, row_id_map, T, H, k, E, n_rows,
+                                          per_rank, bp, out, dev_status, s);
+    else
+      combine_ep_dispatch<1, false, false>(in, probs, topk_idx, row_id_map, T, H, k, E, n_rows,
+                                           per_rank, bp, out, dev_status, s);
+  }
   return hipGetLastError();
 }
 
