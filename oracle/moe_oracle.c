@@ -25,6 +25,8 @@
  *                              ranks: per-rank slot-order partials (optionally
  *                              rounded to bf16) added in rank order (fp32 or
  *                              fp64), then bf16.
+ *   oracle_topk_softmax(_bwd) -- top-k selection + softmax router and its
+ *                              gradient (fp64 arithmetic, rounded once).
  *   oracle_chunk_map        -- padded destination -> source row map.
  *   oracle_sort_chunks_and_pad / oracle_unpad_and_restore_chunks
  *                           -- the two copies driven by that map.
@@ -429,6 +431,76 @@ int oracle_permute_bwd(const uint16_t *d_out, const float *d_out_probs, const in
                 if (s) return s;
                 d_probs[(int64_t)t * k + j] = d_out_probs[r];
             }
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- fused top-k softmax router ------------------------------------------ */
+
+/*
+ * moe-ops README, "Fused Top-K Softmax": top-k selection and a softmax
+ * over the selected logits, with fp32 routing weights.  Per token:
+ *   the k largest logits, in descending order, a tie going to the lower
+ *   expert index (repeated selection of the maximum of the rest);
+ *   w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max) over the k selected,
+ *   in fp64, rounded once to fp32.
+ * logits: [T][E] of elem_bytes 2 (bf16 bits) or 4 (fp32); NaN logits are
+ * not supported.
+ */
+int oracle_topk_softmax(const void *logits, int elem_bytes, int T, int E, int k,
+                        int32_t *topk_idx, float *probs)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || (elem_bytes != 2 && elem_bytes != 4))
+        return ORC_BAD_ARG;
+    char *taken = (char *)malloc((size_t)E);
+    double *lv = (double *)malloc((size_t)k * sizeof(double));
+    if (!taken || !lv) { free(taken); free(lv); return ORC_NO_MEM; }
+    for (int t = 0; t < T; t++) {
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            int best = -1;
+            double bv = 0.0;
+            for (int e = 0; e < E; e++) {
+                if (taken[e]) continue;
+                double v = elem_bytes == 2
+                               ? (double)bf16_to_f32(((const uint16_t *)logits)[(int64_t)t * E + e])
+                               : (double)((const float *)logits)[(int64_t)t * E + e];
+                if (best < 0 || v > bv) { best = e; bv = v; }
+            }
+            taken[best] = 1;
+            topk_idx[(int64_t)t * k + j] = best;
+            lv[j] = bv;
+        }
+        double sum = 0.0;
+        for (int j = 0; j < k; j++) sum += exp(lv[j] - lv[0]);
+        for (int j = 0; j < k; j++) probs[(int64_t)t * k + j] = (float)(exp(lv[j] - lv[0]) / sum);
+    }
+    free(taken);
+    free(lv);
+    return ORC_OK;
+}
+
+/*
+ * Gradient of the router weights w.r.t. the logits (same section: exact
+ * softmax gradients scattered back to the logits): for the selected
+ * experts, d_logits[t][e_j] = w_j * (d_probs[t][j] - sum_i w_i d_probs[t][i])
+ * in fp64, rounded once to fp32; 0 for the experts not selected.
+ */
+int oracle_topk_softmax_bwd(const float *d_probs, const float *probs, const int32_t *topk_idx,
+                            int T, int E, int k, float *d_logits)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E) return ORC_BAD_ARG;
+    for (int64_t i = 0; i < (int64_t)T * E; i++) d_logits[i] = 0.0f;
+    for (int t = 0; t < T; t++) {
+        double dot = 0.0;
+        for (int j = 0; j < k; j++)
+            dot += (double)probs[(int64_t)t * k + j] * (double)d_probs[(int64_t)t * k + j];
+        for (int j = 0; j < k; j++) {
+            int e = topk_idx[(int64_t)t * k + j];
+            if (e < 0 || e >= E) return ORC_BAD_EXPERT;
+            double w = probs[(int64_t)t * k + j];
+            d_logits[(int64_t)t * E + e] = (float)(w * ((double)d_probs[(int64_t)t * k + j] - dot));
         }
     }
     return ORC_OK;

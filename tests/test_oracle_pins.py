@@ -623,3 +623,42 @@ def test_f64_to_bf16_matches_exact_rounding():
         got = oracle.f64_to_bf16(float(v))
         exp = _bf16_bits_of(Fraction(float(v)), negative=bool(np.signbit(v)))
         assert got == exp, (v, hex(got), hex(exp))
+
+
+# ------------------------------------------------ top-k softmax router -----
+
+@pytest.mark.parametrize("T,E,k,dtype", [(50, 32, 4, "f32"), (40, 64, 6, "bf16"),
+                                         (20, 8, 8, "f32"), (30, 5, 1, "bf16")])
+def test_topk_softmax_against_stable_sort_and_softmax(T, E, k, dtype):
+    import scipy.special
+    rng = np.random.default_rng(T + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 1] = logits[:, 0]                      # forced ties
+    if dtype == "bf16":
+        lb = _to_bf16_torch(logits)
+        lv = _bf16_to_f32(lb)
+        idx, probs = oracle.topk_softmax(lb, k)
+    else:
+        lv = logits
+        idx, probs = oracle.topk_softmax(logits, k)
+    ref_idx = np.argsort(-lv.astype(np.float64), axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(idx, ref_idx)      # descending, ties to lower index
+    sel = np.take_along_axis(lv.astype(np.float64), ref_idx, axis=1)
+    ref_p = scipy.special.softmax(sel, axis=1)
+    np.testing.assert_allclose(probs, ref_p, rtol=2e-7, atol=0)
+
+
+def test_topk_softmax_bwd_against_autograd():
+    T, E, k = 30, 16, 4
+    rng = np.random.default_rng(1)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, probs = oracle.topk_softmax(logits, k)
+    dp = rng.standard_normal((T, k)).astype(np.float32)
+    got = oracle.topk_softmax_bwd(dp, probs, idx, E)
+    lt = torch.from_numpy(logits.astype(np.float64)).requires_grad_(True)
+    sel = torch.gather(lt, 1, torch.from_numpy(idx.astype(np.int64)))
+    torch.softmax(sel, dim=1).backward(torch.from_numpy(dp.astype(np.float64)))
+    np.testing.assert_allclose(got, lt.grad.numpy(), rtol=1e-6, atol=1e-7)
+    selected = np.zeros((T, E), bool)
+    np.put_along_axis(selected, idx.astype(np.int64), True, axis=1)
+    assert np.all(got[~selected] == 0)
