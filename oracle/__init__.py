@@ -72,8 +72,8 @@ def _load():
             "oracle_unpermute_bwd": [P, P, P, P, P, I, I, I, I, L, P, P],
             "oracle_permute_bwd": [P, P, P, P, I, I, I, I, L, P, P],
             "oracle_unpermute_ep": [P, P, P, P, I, I, I, I, L, I, I, I, P],
-            "oracle_topk_softmax": [P, I, I, I, I, P, P],
-            "oracle_topk_softmax_bwd": [P, P, P, I, I, I, P],
+            "oracle_topk_softmax": [P, I, I, I, I, P, P, I],
+            "oracle_topk_softmax_bwd": [P, P, I, P, I, I, I, P, I],
             "oracle_chunk_map": [P, P, I, I, I, I, I, P, P],
             "oracle_sort_chunks_and_pad": [P, P, I, I, I, I, P, P, I, I, I, I, P, P, P, P],
             "oracle_unpad_and_restore_chunks": [P, P, I, I, P, P, I, I, I, I, P, P],
@@ -232,26 +232,30 @@ def permute_bwd(d_out, d_out_probs, topk_idx, row_map):
 
 # ---- router ---------------------------------------------------------------
 
-def topk_softmax(logits, k):
-    """logits: [T][E] float32, or uint16 bf16 bits.  Returns (idx int32, probs fp32)."""
+def topk_softmax(logits, k, prob_bytes=4):
+    """logits: [T][E] float32, or uint16 bf16 bits.  Returns (idx int32, weights):
+    weights fp32, or bf16 bit patterns (uint16) when prob_bytes is 2."""
     logits = np.ascontiguousarray(logits)
     T, E = logits.shape
     eb = logits.dtype.itemsize
     idx = np.empty((T, k), np.int32)
-    probs = np.empty((T, k), np.float32)
-    _check(_load().oracle_topk_softmax(_p(logits), eb, T, E, k, _p(idx), _p(probs)),
+    probs = np.empty((T, k), np.float32 if prob_bytes == 4 else np.uint16)
+    _check(_load().oracle_topk_softmax(_p(logits), eb, T, E, k, _p(idx), _p(probs), prob_bytes),
            "topk_softmax")
     return idx, probs
 
 
-def topk_softmax_bwd(d_probs, probs, topk_idx, num_experts):
-    d_probs = _arr(d_probs, np.float32)
-    probs = _arr(probs, np.float32)
+def topk_softmax_bwd(d_probs, probs, topk_idx, num_experts, logit_bytes=4):
+    """d_probs, probs: [T][k] fp32, or both uint16 bf16 bits.  Returns d_logits
+    [T][E]: fp32, or bf16 bit patterns when logit_bytes is 2."""
+    probs = np.ascontiguousarray(probs)
+    pb = probs.dtype.itemsize
+    d_probs = _arr(d_probs, probs.dtype)
     idx = _arr(topk_idx, np.int32)
     T, k = idx.shape
-    out = np.empty((T, num_experts), np.float32)
-    _check(_load().oracle_topk_softmax_bwd(_p(d_probs), _p(probs), _p(idx), T, num_experts, k,
-                                           _p(out)), "topk_softmax_bwd")
+    out = np.empty((T, num_experts), np.float32 if logit_bytes == 4 else np.uint16)
+    _check(_load().oracle_topk_softmax_bwd(_p(d_probs), _p(probs), pb, _p(idx), T, num_experts,
+                                           k, _p(out), logit_bytes), "topk_softmax_bwd")
     return out
 
 

@@ -440,18 +440,20 @@ int oracle_permute_bwd(const uint16_t *d_out, const float *d_out_probs, const in
 
 /*
  * moe-ops README, "Fused Top-K Softmax": top-k selection and a softmax
- * over the selected logits, with fp32 routing weights.  Per token:
+ * over the selected logits; the fp32_routing option there keeps the weights
+ * in fp32, otherwise they come in the activation dtype.  Per token:
  *   the k largest logits, in descending order, a tie going to the lower
  *   expert index (repeated selection of the maximum of the rest);
  *   w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max) over the k selected,
- *   in fp64, rounded once to fp32.
+ *   in fp64, rounded once to fp32 (prob_bytes 4) or bf16 (prob_bytes 2).
  * logits: [T][E] of elem_bytes 2 (bf16 bits) or 4 (fp32); NaN logits are
  * not supported.
  */
 int oracle_topk_softmax(const void *logits, int elem_bytes, int T, int E, int k,
-                        int32_t *topk_idx, float *probs)
+                        int32_t *topk_idx, void *probs, int prob_bytes)
 {
-    if (T < 0 || E < 1 || k < 1 || k > E || (elem_bytes != 2 && elem_bytes != 4))
+    if (T < 0 || E < 1 || k < 1 || k > E || (elem_bytes != 2 && elem_bytes != 4) ||
+        (prob_bytes != 2 && prob_bytes != 4))
         return ORC_BAD_ARG;
     char *taken = (char *)malloc((size_t)E);
     double *lv = (double *)malloc((size_t)k * sizeof(double));
@@ -474,7 +476,13 @@ int oracle_topk_softmax(const void *logits, int elem_bytes, int T, int E, int k,
         }
         double sum = 0.0;
         for (int j = 0; j < k; j++) sum += exp(lv[j] - lv[0]);
-        for (int j = 0; j < k; j++) probs[(int64_t)t * k + j] = (float)(exp(lv[j] - lv[0]) / sum);
+        for (int j = 0; j < k; j++) {
+            double w = exp(lv[j] - lv[0]) / sum;
+            if (prob_bytes == 4)
+                ((float *)probs)[(int64_t)t * k + j] = (float)w;
+            else
+                ((uint16_t *)probs)[(int64_t)t * k + j] = f64_to_bf16_rne(w);
+        }
     }
     free(taken);
     free(lv);
@@ -485,22 +493,43 @@ int oracle_topk_softmax(const void *logits, int elem_bytes, int T, int E, int k,
  * Gradient of the router weights w.r.t. the logits (same section: exact
  * softmax gradients scattered back to the logits): for the selected
  * experts, d_logits[t][e_j] = w_j * (d_probs[t][j] - sum_i w_i d_probs[t][i])
- * in fp64, rounded once to fp32; 0 for the experts not selected.
+ * in fp64, rounded once to the output type; 0 for the experts not selected.
+ * Weights and their gradients come as fp32 or bf16 (prob_bytes 4 or 2, read
+ * exactly); d_logits is fp32 or bf16 (logit_bytes 4 or 2).
  */
-int oracle_topk_softmax_bwd(const float *d_probs, const float *probs, const int32_t *topk_idx,
-                            int T, int E, int k, float *d_logits)
+static double load_real(const void *p, int bytes, int64_t i)
 {
-    if (T < 0 || E < 1 || k < 1 || k > E) return ORC_BAD_ARG;
-    for (int64_t i = 0; i < (int64_t)T * E; i++) d_logits[i] = 0.0f;
+    return bytes == 4 ? (double)((const float *)p)[i]
+                      : (double)bf16_to_f32(((const uint16_t *)p)[i]);
+}
+
+static void store_real(void *p, int bytes, int64_t i, double v)
+{
+    if (bytes == 4)
+        ((float *)p)[i] = (float)v;
+    else
+        ((uint16_t *)p)[i] = f64_to_bf16_rne(v);
+}
+
+int oracle_topk_softmax_bwd(const void *d_probs, const void *probs, int prob_bytes,
+                            const int32_t *topk_idx, int T, int E, int k, void *d_logits,
+                            int logit_bytes)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || (prob_bytes != 2 && prob_bytes != 4) ||
+        (logit_bytes != 2 && logit_bytes != 4))
+        return ORC_BAD_ARG;
+    for (int64_t i = 0; i < (int64_t)T * E; i++) store_real(d_logits, logit_bytes, i, 0.0);
     for (int t = 0; t < T; t++) {
         double dot = 0.0;
         for (int j = 0; j < k; j++)
-            dot += (double)probs[(int64_t)t * k + j] * (double)d_probs[(int64_t)t * k + j];
+            dot += load_real(probs, prob_bytes, (int64_t)t * k + j) *
+                   load_real(d_probs, prob_bytes, (int64_t)t * k + j);
         for (int j = 0; j < k; j++) {
             int e = topk_idx[(int64_t)t * k + j];
             if (e < 0 || e >= E) return ORC_BAD_EXPERT;
-            double w = probs[(int64_t)t * k + j];
-            d_logits[(int64_t)t * E + e] = (float)(w * ((double)d_probs[(int64_t)t * k + j] - dot));
+            double w = load_real(probs, prob_bytes, (int64_t)t * k + j);
+            double dp = load_real(d_probs, prob_bytes, (int64_t)t * k + j);
+            store_real(d_logits, logit_bytes, (int64_t)t * E + e, w * (dp - dot));
         }
     }
     return ORC_OK;

@@ -662,3 +662,59 @@ def test_topk_softmax_bwd_against_autograd():
     selected = np.zeros((T, E), bool)
     np.put_along_axis(selected, idx.astype(np.int64), True, axis=1)
     assert np.all(got[~selected] == 0)
+
+
+def _nearest_bf16(bits, ref):
+    """bits (uint16) round ref (float64) to nearest: within half a bf16 ulp."""
+    got = _bf16_to_f32(np.asarray(bits, np.uint16)).astype(np.float64)
+    ref = np.asarray(ref, np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)   # bf16: 8 significant bits
+    return np.abs(got - ref) <= 0.5 * ulp * (1 + 1e-9) + 1e-300
+
+
+def test_topk_softmax_bf16_weights_round_to_nearest():
+    """Weights in bf16 (the activation dtype) are the exact softmax rounded
+    once to nearest; fp32 routing keeps them in fp32."""
+    import scipy.special
+    rng = np.random.default_rng(11)
+    T, E, k = 60, 48, 6
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, w16 = oracle.topk_softmax(logits, k, prob_bytes=2)
+    idx32, w32 = oracle.topk_softmax(logits, k)
+    np.testing.assert_array_equal(idx, idx32)
+    sel = np.take_along_axis(logits.astype(np.float64), idx.astype(np.int64), axis=1)
+    assert w16.dtype == np.uint16
+    assert _nearest_bf16(w16, scipy.special.softmax(sel, axis=1)).all()
+
+
+@pytest.mark.parametrize("logits,k,expect", [
+    ([0.5, -1.0, 2.0], 1, [0x3F80]),                        # one expert: weight 1
+    ([1.0, 1.0, -3.0], 2, [0x3F00, 0x3F00]),                 # tie: 1/2 each
+    ([0.0, 0.0, 0.0, 0.0, -1.0], 4, [0x3E80] * 4),           # four equal: 1/4
+    ([0.0, float(np.log(3.0)), -5.0], 2, [0x3F40, 0x3E80]),  # 3/4 and 1/4
+])
+def test_topk_softmax_bf16_closed_forms(logits, k, expect):
+    _, w = oracle.topk_softmax(np.array([logits], np.float32), k, prob_bytes=2)
+    assert [int(v) for v in w[0]] == expect
+
+
+def test_topk_softmax_bwd_bf16_closed_form_and_autograd():
+    # w = (1/2, 1/2), dp = (1, 0): dot = 1/2, gradients +1/4 and -1/4 (exact)
+    w = np.array([[0x3F00, 0x3F00]], np.uint16)
+    dp = np.array([[0x3F80, 0x0000]], np.uint16)
+    g = oracle.topk_softmax_bwd(dp, w, np.array([[2, 0]], np.int32), 3, logit_bytes=2)
+    assert [int(v) for v in g[0]] == [0xBE80, 0x0000, 0x3E80]
+    # bf16 in, bf16 out: the fp64 gradient of the widened inputs, rounded to nearest
+    T, E, k = 25, 12, 3
+    rng = np.random.default_rng(2)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, w16 = oracle.topk_softmax(logits, k, prob_bytes=2)
+    dp16 = _to_bf16_torch(rng.standard_normal((T, k)).astype(np.float32))
+    got = oracle.topk_softmax_bwd(dp16, w16, idx, E, logit_bytes=2)
+    wv = _bf16_to_f32(w16).astype(np.float64)
+    dv = _bf16_to_f32(dp16).astype(np.float64)
+    # softmax Jacobian diag(w) - w w^T applied to dp, token by token
+    gsel = np.stack([(np.diag(wv[t]) - np.outer(wv[t], wv[t])) @ dv[t] for t in range(T)])
+    ref = np.zeros((T, E))
+    np.put_along_axis(ref, idx.astype(np.int64), gsel, axis=1)
+    assert _nearest_bf16(got, ref).all()
