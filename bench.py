@@ -210,13 +210,23 @@ def build_routed(m, w):
              p(dx), p(dprob2), None,)
     # Rows beyond the step (SURVEY "next" rows), timed on their own.
     y_ep = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    step.keep.append(y_ep)
+    logits = w.logits.to(dev).contiguous()
+    r_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    r_probs = torch.empty((T, k), dtype=torch.float32, device=dev)
+    d_logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    step.keep += [y_ep, logits, r_idx, r_probs, d_logits]
     ub = routed_bytes(T, H, E, k)["unpermute"]
+    eb = logits.element_size()
     step.extra = [
         ("unpermute_ep8_bf16partials", ub, lib.moe_unpermute_ep,
          (p(P), p(probs), p(idx), p(rm), T, H, k, E, n, 8, 1, p(y_ep), None)),
         ("unpermute_ep8_bf16partials_fp64", ub, lib.moe_unpermute_ep,
          (p(P), p(probs), p(idx), p(rm), T, H, k, E, n, 8, 3, p(y_ep), None)),
+        # router: logits in, k indices + k weights out; bwd: 3 k-vectors in, [T, E] out
+        ("topk_softmax", T * E * eb + T * k * 8, lib.moe_topk_softmax,
+         (p(logits), eb, T, E, k, p(r_idx), p(r_probs), 4)),
+        ("topk_softmax_bwd", T * k * 12 + T * E * 4, lib.moe_topk_softmax_bwd,
+         (p(dprob), p(probs), 4, p(idx), T, E, k, p(d_logits), 4, None)),
     ]
     return step, routed_bytes(T, H, E, k)
 

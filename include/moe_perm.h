@@ -240,6 +240,41 @@ MOE_PERM_API int moe_permute_bwd(const void *d_out, const float *d_out_probs,
                                  int32_t *dev_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Fused top-k softmax router (the step before the row map).
+ *
+ * [MOE-OPS] "Fused Top-K Softmax": top-k selection and softmax in one kernel;
+ * with the fp32_routing option the weights are fp32, without it they come
+ * in the activation dtype (here: prob_bytes 4 or 2).  The backward gives the
+ * exact softmax gradient scattered back to the logits.
+ *   topk_idx[t][0..k): the k largest logits of token t in descending order, a
+ *                      tie going to the lower expert index.
+ *   probs[t][j]      = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k
+ *                      selected logits, computed in fp32 and stored as fp32
+ *                      (prob_bytes 4) or rounded to nearest-even bf16
+ *                      (prob_bytes 2).  The sum's order is the kernel's own,
+ *                      so results match an exact softmax to a few fp32 ulp.
+ *   logits  [num_tokens][num_experts], logit_bytes 2 (bf16) or 4 (fp32).
+ *   Limits: 1 <= topk <= min(num_experts, MOE_MAX_TOPK), num_experts <=
+ *   MOE_MAX_EXPERTS.  NaN logits rank below every number (values then
+ *   unspecified; the indices stay distinct and in range).
+ *   Buffers: device memory, owned by the caller, element-aligned.
+ *
+ * moe_topk_softmax_bwd: d_logits[t][e] = w_j (d_probs[t][j] - sum_i w_i
+ * d_probs[t][i]) for e = topk_idx[t][j], +0 for experts not selected, in
+ * fp32 arithmetic.  probs and d_probs [num_tokens][topk] of prob_bytes 4 or
+ * 2; d_logits [num_tokens][num_experts] of logit_bytes 4 or 2 (bf16 rounded
+ * to nearest-even).  A token's expert indices must be distinct.
+ * dev_status: MOE_DEV_BAD_EXPERT for an index outside [0, num_experts).
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_topk_softmax(const void *logits, int logit_bytes, int num_tokens,
+                                  int num_experts, int topk, int32_t *topk_idx, void *probs,
+                                  int prob_bytes, hipStream_t stream);
+MOE_PERM_API int moe_topk_softmax_bwd(const void *d_probs, const void *probs, int prob_bytes,
+                                      const int32_t *topk_idx, int num_tokens, int num_experts,
+                                      int topk, void *d_logits, int logit_bytes,
+                                      int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * (3) Fused chunk sort-and-pad.
  *
  * [TE-3509] Description / Changes / Diagram: rank chunks are regrouped into

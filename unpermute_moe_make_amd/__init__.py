@@ -7,6 +7,7 @@ with a thin ctypes binding whose functions carry the C names:
   moe_permute / moe_permute_bwd       row scatter-copy and its gradient
   moe_unpermute / moe_unpermute_bwd   fixed slot-order FMA combine, gradient
   moe_unpermute_ep                    the combine with EP rank-ordered partials
+  moe_topk_softmax(_bwd)              fused top-k softmax router, gradient
   moe_sort_chunks_and_pad(_bwd)       fused chunk regroup + zero padding
   moe_unpad_and_restore_chunks(_bwd)  the matching restore
 
@@ -28,6 +29,8 @@ from ._binding import (  # noqa: F401
     moe_permute,
     moe_permute_bwd,
     moe_sort_chunks_and_pad,
+    moe_topk_softmax,
+    moe_topk_softmax_bwd,
     moe_sort_chunks_and_pad_bwd,
     moe_unpad_and_restore_chunks,
     moe_unpad_and_restore_chunks_bwd,

@@ -38,6 +38,8 @@ _SIGS = {
     "moe_unpermute_ep": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_unpermute_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_permute_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+    "moe_topk_softmax": ([_P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
+    "moe_topk_softmax_bwd": ([_P, _P, _I, _P, _I, _I, _I, _P, _I, _P, _P], _I),
     "moe_sort_chunks_and_pad": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P,
                                  _P, _P, _P], _I),
     "moe_unpad_and_restore_chunks": ([_P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P],
@@ -282,6 +284,54 @@ def moe_permute_bwd(d_out: torch.Tensor, topk_idx: torch.Tensor, row_id_map: tor
                                 _ptr(_status_arg(dev_status)), _stream(stream)),
            "moe_permute_bwd")
     return d_x, d_probs
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+
+def moe_topk_softmax(logits: torch.Tensor, topk: int, *, fp32_routing: bool = True,
+                     topk_idx=None, probs=None, stream=None):
+    """Top-k of each row of logits ([T, E], bf16 or fp32; descending, ties to
+    the lower index) and a softmax over the k.  Weights are fp32 with
+    fp32_routing, else in the logits' dtype.  Returns (topk_idx, probs)."""
+    _need(logits, "logits")
+    if logits.dim() != 2 or logits.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("logits must be a 2-D bf16 or fp32 tensor")
+    T, E = logits.shape
+    dev = logits.device
+    pdt = torch.float32 if fp32_routing else logits.dtype
+    topk_idx = torch.empty((T, topk), dtype=torch.int32, device=dev) if topk_idx is None else \
+        _need(topk_idx, "topk_idx", torch.int32, (T, topk))
+    probs = torch.empty((T, topk), dtype=pdt, device=dev) if probs is None else \
+        _need(probs, "probs", pdt, (T, topk))
+    _check(_lib.moe_topk_softmax(_ptr(logits), logits.element_size(), T, E, topk,
+                                 _ptr(topk_idx), _ptr(probs), probs.element_size(),
+                                 _stream(stream)), "moe_topk_softmax")
+    return topk_idx, probs
+
+
+def moe_topk_softmax_bwd(d_probs: torch.Tensor, probs: torch.Tensor, topk_idx: torch.Tensor,
+                         num_experts: int, *, logits_dtype=torch.float32, d_logits=None,
+                         dev_status=None, stream=None):
+    """Softmax gradient scattered to the selected experts: returns d_logits
+    [T, E] in logits_dtype (fp32 or bf16).  probs and d_probs share a dtype."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    if probs.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("probs must be fp32 or bf16")
+    _need(probs, "probs", probs.dtype, (T, k))
+    _need(d_probs, "d_probs", probs.dtype, (T, k))
+    if d_logits is None:
+        d_logits = torch.empty((T, num_experts), dtype=logits_dtype, device=probs.device)
+    elif d_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("d_logits must be fp32 or bf16")
+    _need(d_logits, "d_logits", d_logits.dtype, (T, num_experts))
+    _check(_lib.moe_topk_softmax_bwd(_ptr(d_probs), _ptr(probs), probs.element_size(),
+                                     _ptr(topk_idx), T, num_experts, k, _ptr(d_logits),
+                                     d_logits.element_size(), _ptr(_status_arg(dev_status)),
+                                     _stream(stream)), "moe_topk_softmax_bwd")
+    return d_logits
 
 
 # ---------------------------------------------------------------------------

@@ -202,6 +202,44 @@ MOE_PERM_API int moe_permute_bwd(const void *d_out, const float *d_out_probs,
                                         dev_status, vec_ok(H, d_out, d_x), stream));
 }
 
+MOE_PERM_API int moe_topk_softmax(const void *logits, int logit_bytes, int num_tokens,
+                                  int num_experts, int topk, int32_t *topk_idx, void *probs,
+                                  int prob_bytes, hipStream_t stream) {
+  const int T = num_tokens, E = num_experts, k = topk;
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_SHAPE;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if ((logit_bytes != 2 && logit_bytes != 4) || (prob_bytes != 2 && prob_bytes != 4))
+    return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !probs) return MOE_ERR_NULL;
+  if (!aligned(logits, (uintptr_t)logit_bytes) || !aligned(topk_idx, 4) ||
+      !aligned(probs, (uintptr_t)prob_bytes))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_topk_softmax(logits, logit_bytes, T, E, k, topk_idx, probs,
+                                             prob_bytes, stream));
+}
+
+MOE_PERM_API int moe_topk_softmax_bwd(const void *d_probs, const void *probs, int prob_bytes,
+                                      const int32_t *topk_idx, int num_tokens, int num_experts,
+                                      int topk, void *d_logits, int logit_bytes,
+                                      int32_t *dev_status, hipStream_t stream) {
+  const int T = num_tokens, E = num_experts, k = topk;
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_SHAPE;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if ((logit_bytes != 2 && logit_bytes != 4) || (prob_bytes != 2 && prob_bytes != 4))
+    return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!d_probs || !probs || !topk_idx || !d_logits) return MOE_ERR_NULL;
+  if (!aligned(d_probs, (uintptr_t)prob_bytes) || !aligned(probs, (uintptr_t)prob_bytes) ||
+      !aligned(topk_idx, 4) || !aligned(d_logits, (uintptr_t)logit_bytes) ||
+      !aligned(dev_status, 4))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_topk_softmax_bwd(d_probs, probs, prob_bytes, topk_idx, T, E, k,
+                                                 d_logits, logit_bytes, dev_status, stream));
+}
+
 MOE_PERM_API int moe_sort_chunks_and_pad(const void *in, const void *probs, int elem_bytes,
                                          int prob_bytes, int n_cap, int hidden,
                                          const int32_t *split_sizes, const int32_t *sorted_idx,

@@ -33,6 +33,13 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
                               int k, int E, int n_rows, void *d_in, float *d_probs,
                               int32_t *dev_status, bool vec, hipStream_t s);
 
+// Fused top-k softmax router and its gradient.
+hipError_t launch_topk_softmax(const void *logits, int logit_bytes, int T, int E, int k,
+                               int32_t *topk_idx, void *probs, int prob_bytes, hipStream_t s);
+hipError_t launch_topk_softmax_bwd(const void *d_probs, const void *probs, int prob_bytes,
+                                   const int32_t *topk_idx, int T, int E, int k, void *d_logits,
+                                   int logit_bytes, int32_t *dev_status, hipStream_t s);
+
 // Chunk map and the two chunk copies.  unit_bytes is 16, 4 or 2; the row
 // length in units is row_units.
 hipError_t launch_chunk_map(const int32_t *split_sizes, const int32_t *sorted_idx, int C, int R,

@@ -36,6 +36,7 @@ class Routed:
     num_experts: int
     dy: Optional[torch.Tensor] = None   # [T, H] bf16 upstream gradient
     seed: int = 0
+    logits: Optional[torch.Tensor] = None   # [T, E] router logits the routing came from
 
     @property
     def T(self):
@@ -100,7 +101,7 @@ def random_routed(T: int, H: int, E: int, k: int, seed: int, with_dy: bool = Tru
         logits = logits - zipf_s * torch.log1p(rank)[None, :]
     idx, probs = route(logits, k)
     dy = torch.randn(T, H, generator=g).to(torch.bfloat16) if with_dy else None
-    return Routed(name, x, idx, probs, E, dy, seed)
+    return Routed(name, x, idx, probs, E, dy, seed, logits)
 
 
 def tiny() -> Routed:
@@ -110,7 +111,7 @@ def tiny() -> Routed:
     logits = torch.randn(16, 32, generator=g).to(torch.bfloat16)
     idx, probs = route(logits, 4)
     dy = torch.randn(16, 64, generator=g).to(torch.bfloat16)
-    return Routed("tiny", x, idx, probs, 32, dy, 1)
+    return Routed("tiny", x, idx, probs, 32, dy, 1, logits)
 
 
 def finegrain() -> Routed:
