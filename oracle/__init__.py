@@ -74,6 +74,10 @@ def _load():
             "oracle_unpermute_ep": [P, P, P, P, I, I, I, I, L, I, I, I, P],
             "oracle_topk_softmax": [P, I, I, I, I, P, P, I],
             "oracle_topk_softmax_bwd": [P, P, I, P, I, I, I, P, I],
+            "oracle_mask_row_id_map": [P, I, I, I, I, P, P],
+            "oracle_mask_permute": [P, P, P, I, I, I, I, P, P],
+            "oracle_mask_unpermute": [P, P, P, P, I, I, I, I, P, P],
+            "oracle_mask_unpermute_bwd": [P, P, P, P, I, I, I, I, P, P],
             "oracle_chunk_map": [P, P, I, I, I, I, I, P, P],
             "oracle_sort_chunks_and_pad": [P, P, I, I, I, I, P, P, I, I, I, I, P, P, P, P],
             "oracle_unpad_and_restore_chunks": [P, P, I, I, P, P, I, I, I, I, P, P],
@@ -257,6 +261,71 @@ def topk_softmax_bwd(d_probs, probs, topk_idx, num_experts, logit_bytes=4):
     _check(_load().oracle_topk_softmax_bwd(_p(d_probs), _p(probs), pb, _p(idx), T, num_experts,
                                            k, _p(out), logit_bytes), "topk_softmax_bwd")
     return out
+
+
+# ---- TE mask-map interop ------------------------------------------------------
+
+def mask_row_id_map(routing_map, num_out=-1):
+    """routing_map: [T][E] uint8/bool or int32 mask.  Returns (map [T][2E+1]
+    int32, expert_offsets [E+1] int32); rows at or past num_out are dropped."""
+    rm = np.ascontiguousarray(routing_map)
+    if rm.dtype == np.bool_:
+        rm = rm.view(np.uint8)
+    if rm.dtype not in (np.uint8, np.int8, np.int32):
+        rm = rm.astype(np.int32)
+    T, E = rm.shape
+    m = np.empty((T, 2 * E + 1), np.int32)
+    off = np.empty(E + 1, np.int32)
+    _check(_load().oracle_mask_row_id_map(_p(rm), rm.dtype.itemsize, T, E, num_out, _p(m),
+                                          _p(off)), "mask_row_id_map")
+    return m, off
+
+
+def mask_permute(x, probs, row_map, n_rows, out=None):
+    """x: [T][H] bf16 bits; probs: [T][E] fp32 or None.  Returns (out, out_probs):
+    rows no map entry names keep the values of `out` (zeros by default)."""
+    x = _arr(x, np.uint16)
+    rm = _arr(row_map, np.int32)
+    probs = _arr(probs, np.float32)
+    T, H = x.shape
+    E = (rm.shape[1] - 1) // 2
+    out = np.zeros((n_rows, H), np.uint16) if out is None else np.array(out, np.uint16)
+    out_probs = None if probs is None else np.zeros(n_rows, np.float32)
+    _check(_load().oracle_mask_permute(_p(x), _p(probs), _p(rm), T, H, E, n_rows, _p(out),
+                                       _p(out_probs)), "mask_permute")
+    return out, out_probs
+
+
+def mask_unpermute(inp, merging_probs, row_map, permuted_probs=None):
+    """Returns (out [T][H] bf16 bits, unpermuted_probs [T][E] or None)."""
+    inp = _arr(inp, np.uint16)
+    rm = _arr(row_map, np.int32)
+    mp = _arr(merging_probs, np.float32)
+    pp = _arr(permuted_probs, np.float32)
+    n_rows, H = inp.shape
+    T = rm.shape[0]
+    E = (rm.shape[1] - 1) // 2
+    out = np.empty((T, H), np.uint16)
+    up = None if pp is None else np.empty((T, E), np.float32)
+    _check(_load().oracle_mask_unpermute(_p(inp), _p(mp), _p(pp), _p(rm), T, H, E, n_rows,
+                                         _p(out), _p(up)), "mask_unpermute")
+    return out, up
+
+
+def mask_unpermute_bwd(d_out, fwd_in, merging_probs, row_map, d_in=None):
+    """Returns (d_in [n_rows][H] bf16 bits, d_merging_probs [T][E] fp32)."""
+    d_out = _arr(d_out, np.uint16)
+    fwd_in = _arr(fwd_in, np.uint16)
+    mp = _arr(merging_probs, np.float32)
+    rm = _arr(row_map, np.int32)
+    n_rows, H = fwd_in.shape
+    T = rm.shape[0]
+    E = (rm.shape[1] - 1) // 2
+    d_in = np.zeros((n_rows, H), np.uint16) if d_in is None else np.array(d_in, np.uint16)
+    dmp = np.empty((T, E), np.float32)
+    _check(_load().oracle_mask_unpermute_bwd(_p(d_out), _p(fwd_in), _p(mp), _p(rm), T, H, E,
+                                             n_rows, _p(d_in), _p(dmp)), "mask_unpermute_bwd")
+    return d_in, dmp
 
 
 # ---- (3) chunk sort-and-pad / unpad-and-restore ------------------------------

@@ -27,6 +27,10 @@
  *                              fp64), then bf16.
  *   oracle_topk_softmax(_bwd) -- top-k selection + softmax router and its
  *                              gradient (fp64 arithmetic, rounded once).
+ *   oracle_mask_row_id_map  -- TE mask-map form: [T][2E+1] per-token map
+ *                              from a [T][E] routing mask, with dropping.
+ *   oracle_mask_permute / oracle_mask_unpermute(_bwd)
+ *                           -- the TE-order copies and combine on that map.
  *   oracle_chunk_map        -- padded destination -> source row map.
  *   oracle_sort_chunks_and_pad / oracle_unpad_and_restore_chunks
  *                           -- the two copies driven by that map.
@@ -530,6 +534,204 @@ int oracle_topk_softmax_bwd(const void *d_probs, const void *probs, int prob_byt
             double w = load_real(probs, prob_bytes, (int64_t)t * k + j);
             double dp = load_real(d_probs, prob_bytes, (int64_t)t * k + j);
             store_real(d_logits, logit_bytes, (int64_t)t * E + e, w * (dp - dot));
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- TE mask-map interop ------------------------------------------------ */
+
+/*
+ * d9d permute_with_probs.py (TransformerEngine mask-map permutation),
+ * make_row_id_map and its worked example.  routing_map[t][e] != 0 routes
+ * token t to expert e (mask_bytes 1 or 4).  Passes 1 and 2 give every routed
+ * pair its destination row: rows run expert-major, tokens ascending inside
+ * an expert.  Token dropping (moe_permute_with_probs, num_out_tokens: the
+ * count of rows not dropped): a row at or beyond num_out is dropped and
+ * becomes -1; num_out < 0 keeps every row.  Pass 3 then stores, per token,
+ * its kept rows sorted descending in map[t][0..n), the matching experts in
+ * map[t][E..E+n) and n in map[t][2E]; the entries the page leaves unused
+ * are set to -1 here.  expert_offsets[e] = kept rows of experts below e.
+ */
+struct row_expert { int32_t row, expert; };
+
+static int by_row_descending(const void *a, const void *b)
+{
+    const struct row_expert *x = (const struct row_expert *)a;
+    const struct row_expert *y = (const struct row_expert *)b;
+    return (x->row < y->row) - (x->row > y->row);
+}
+
+int oracle_mask_row_id_map(const void *routing_map, int mask_bytes, int T, int E, int num_out,
+                           int32_t *map, int32_t *expert_offsets)
+{
+    if (T < 0 || E < 1 || (mask_bytes != 1 && mask_bytes != 4)) return ORC_BAD_ARG;
+    const int64_t W = 2 * (int64_t)E + 1;
+    int32_t *dense = (int32_t *)malloc(((size_t)T * E + 1) * sizeof(int32_t));
+    struct row_expert *tok = (struct row_expert *)malloc((size_t)E * sizeof *tok);
+    if (!dense || !tok) { free(dense); free(tok); return ORC_NO_MEM; }
+    /* passes 1 and 2: the state [t][e] = destination row or -1 */
+    int64_t row = 0;
+    for (int e = 0; e < E; e++) {
+        if (expert_offsets) expert_offsets[e] = (int32_t)(num_out >= 0 && row > num_out ? num_out : row);
+        for (int t = 0; t < T; t++) {
+            int routed = mask_bytes == 1
+                             ? ((const uint8_t *)routing_map)[(int64_t)t * E + e] != 0
+                             : ((const int32_t *)routing_map)[(int64_t)t * E + e] != 0;
+            dense[(int64_t)t * E + e] = routed ? (int32_t)row++ : -1;
+        }
+    }
+    if (expert_offsets) expert_offsets[E] = (int32_t)(num_out >= 0 && row > num_out ? num_out : row);
+    /* dropping */
+    if (num_out >= 0)
+        for (int64_t i = 0; i < (int64_t)T * E; i++)
+            if (dense[i] >= num_out) dense[i] = -1;
+    /* pass 3: per token, the kept rows sorted descending with their experts */
+    for (int t = 0; t < T; t++) {
+        int n = 0;
+        for (int e = 0; e < E; e++)
+            if (dense[(int64_t)t * E + e] >= 0) {
+                tok[n].row = dense[(int64_t)t * E + e];
+                tok[n].expert = e;
+                n++;
+            }
+        qsort(tok, (size_t)n, sizeof *tok, by_row_descending);
+        int32_t *m = map + (int64_t)t * W;
+        for (int64_t i = 0; i < W; i++) m[i] = -1;
+        for (int i = 0; i < n; i++) {
+            m[i] = tok[i].row;
+            m[E + i] = tok[i].expert;
+        }
+        m[2 * E] = n;
+    }
+    free(dense);
+    free(tok);
+    return ORC_OK;
+}
+
+/* One slot of a token's mask map: its row (checked against n_rows) and expert. */
+static int mask_slot(const int32_t *map, int E, int n_rows, int t, int i, int *row, int *expert)
+{
+    const int32_t *m = map + (int64_t)t * (2 * (int64_t)E + 1);
+    *row = m[i];
+    *expert = m[E + i];
+    if (*expert < 0 || *expert >= E) return ORC_BAD_EXPERT;
+    if (*row < 0 || *row >= n_rows) return ORC_BAD_ROW;
+    return ORC_OK;
+}
+
+static int mask_count(const int32_t *map, int E, int t, int *n)
+{
+    *n = map[(int64_t)t * (2 * (int64_t)E + 1) + 2 * (int64_t)E];
+    return (*n < 0 || *n > E) ? ORC_BAD_ROW : ORC_OK;
+}
+
+/*
+ * Same page, _permute_kernel: each token row is copied to every row its map
+ * lists.  With probs ([T][E] fp32) the row's prob goes to out_probs[row],
+ * and a prob equal to zero marks a padded slot whose output row is zeros
+ * instead of the token (the routing_map padding rule).  Output rows that no
+ * map entry names are left as they were.
+ */
+int oracle_mask_permute(const uint16_t *x, const float *probs, const int32_t *map, int T, int H,
+                        int E, int n_rows, uint16_t *out, float *out_probs)
+{
+    if (T < 0 || H < 0 || E < 1 || n_rows < 0) return ORC_BAD_ARG;
+    for (int t = 0; t < T; t++) {
+        int n, s = mask_count(map, E, t, &n);
+        if (s) return s;
+        for (int i = 0; i < n; i++) {
+            int row, e;
+            s = mask_slot(map, E, n_rows, t, i, &row, &e);
+            if (s) return s;
+            int zero_row = 0;
+            if (probs) {
+                float p = probs[(int64_t)t * E + e];
+                if (out_probs) out_probs[row] = p;
+                zero_row = p == 0.0f;
+            }
+            for (int h = 0; h < H; h++)
+                out[(int64_t)row * H + h] = zero_row ? 0 : x[(int64_t)t * H + h];
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Same page, _unpermute_kernel: per token and element, an fp32 accumulator
+ * from zero visits the token's rows in map order (descending rows); each
+ * row is widened to fp32, multiplied by its merging prob (merging_probs
+ * [T][E], when given; one fp32 rounding), then added (a second rounding);
+ * the sum is rounded once to bf16.  With permuted_probs, unpermuted_probs
+ * [T][E] holds permuted_probs[row] at each routed expert and 0 elsewhere.
+ */
+int oracle_mask_unpermute(const uint16_t *in, const float *merging_probs,
+                          const float *permuted_probs, const int32_t *map, int T, int H, int E,
+                          int n_rows, uint16_t *out, float *unpermuted_probs)
+{
+    if (T < 0 || H < 0 || E < 1 || n_rows < 0) return ORC_BAD_ARG;
+    for (int t = 0; t < T; t++) {
+        int n, s = mask_count(map, E, t, &n);
+        if (s) return s;
+        for (int i = 0; i < n; i++) {
+            int row, e;
+            s = mask_slot(map, E, n_rows, t, i, &row, &e);
+            if (s) return s;
+        }
+        for (int h = 0; h < H; h++) {
+            float acc = 0.0f;
+            for (int i = 0; i < n; i++) {
+                int row, e;
+                mask_slot(map, E, n_rows, t, i, &row, &e);
+                float v = bf16_to_f32(in[(int64_t)row * H + h]);
+                if (merging_probs) v = v * merging_probs[(int64_t)t * E + e];
+                acc = acc + v;
+            }
+            out[(int64_t)t * H + h] = f32_to_bf16_rne(acc);
+        }
+        if (unpermuted_probs) {
+            for (int e = 0; e < E; e++) unpermuted_probs[(int64_t)t * E + e] = 0.0f;
+            if (permuted_probs)
+                for (int i = 0; i < n; i++) {
+                    int row, e;
+                    mask_slot(map, E, n_rows, t, i, &row, &e);
+                    unpermuted_probs[(int64_t)t * E + e] = permuted_probs[row];
+                }
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Same page, _unpermute_bwd_with_merging_probs_kernel: for each routed slot
+ * of token t, d_in[row] = bf16(fp32(d_out[t] * merging_probs[t][e])), and
+ * d_merging_probs[t][e] = sum_h fwd_in[row][h] * d_out[t][h] (fp64 here,
+ * rounded once to fp32); the other experts of the row get 0.  Rows of d_in
+ * that no map entry names are left as they were.
+ */
+int oracle_mask_unpermute_bwd(const uint16_t *d_out, const uint16_t *fwd_in,
+                              const float *merging_probs, const int32_t *map, int T, int H, int E,
+                              int n_rows, uint16_t *d_in, float *d_merging_probs)
+{
+    if (T < 0 || H < 0 || E < 1 || n_rows < 0 || !merging_probs) return ORC_BAD_ARG;
+    for (int t = 0; t < T; t++) {
+        int n, s = mask_count(map, E, t, &n);
+        if (s) return s;
+        if (d_merging_probs)
+            for (int e = 0; e < E; e++) d_merging_probs[(int64_t)t * E + e] = 0.0f;
+        for (int i = 0; i < n; i++) {
+            int row, e;
+            s = mask_slot(map, E, n_rows, t, i, &row, &e);
+            if (s) return s;
+            float p = merging_probs[(int64_t)t * E + e];
+            double dot = 0.0;
+            for (int h = 0; h < H; h++) {
+                float g = bf16_to_f32(d_out[(int64_t)t * H + h]);
+                float prod = g * p;
+                d_in[(int64_t)row * H + h] = f32_to_bf16_rne(prod);
+                dot += (double)bf16_to_f32(fwd_in[(int64_t)row * H + h]) * (double)g;
+            }
+            if (d_merging_probs) d_merging_probs[(int64_t)t * E + e] = (float)dot;
         }
     }
     return ORC_OK;

@@ -718,3 +718,160 @@ def test_topk_softmax_bwd_bf16_closed_form_and_autograd():
     ref = np.zeros((T, E))
     np.put_along_axis(ref, idx.astype(np.int64), gsel, axis=1)
     assert _nearest_bf16(got, ref).all()
+
+
+# ------------------------------------------------ TE mask-map interop ------
+
+def _brute_mask_map(mask, num_out=-1):
+    """Rows by enumerating routed (expert, token) pairs expert-major; then per
+    token the kept rows in descending order.  Independent of the oracle."""
+    T, E = mask.shape
+    dense = -np.ones((T, E), np.int64)
+    es, ts = np.nonzero(mask.T)              # expert-major, tokens ascending
+    dense[ts, es] = np.arange(es.size)
+    if num_out >= 0:
+        dense[dense >= num_out] = -1
+    out = []
+    for t in range(T):
+        pairs = sorted(((int(dense[t, e]), e) for e in range(E) if dense[t, e] >= 0),
+                       reverse=True)
+        out.append(pairs)
+    return out
+
+
+def _check_mask_map(m, pairs, E):
+    for t, pr in enumerate(pairs):
+        n = len(pr)
+        assert m[t, 2 * E] == n
+        assert list(m[t, :n]) == [r for r, _ in pr]
+        assert list(m[t, E:E + n]) == [e for _, e in pr]
+
+
+@pytest.mark.parametrize("dtype", [np.int32, np.uint8])
+def test_mask_map_worked_example(dtype):
+    """The worked example's third pass, entry for entry (unused entries -1)."""
+    g = _read_golden("p2_worked_example.txt")
+    mask = np.array(g["routing_map"], dtype=dtype)
+    T, E = mask.shape
+    m, off = oracle.mask_row_id_map(mask)
+    for t, row in enumerate(g["pass3"]):
+        for i, v in enumerate(row):
+            assert m[t, i] == (-1 if v == "r" else int(v)), (t, i)
+    np.testing.assert_array_equal(off, [0, 3, 5, 7])
+
+
+@pytest.mark.parametrize("T,E,density,num_out", [(40, 7, 0.3, -1), (65, 16, 0.5, -1),
+                                                 (33, 5, 0.9, 20), (50, 12, 0.4, 0),
+                                                 (20, 3, 1.0, 59), (1, 1, 1.0, -1)])
+def test_mask_map_brute_force(T, E, density, num_out):
+    rng = np.random.default_rng(T * E)
+    mask = (rng.random((T, E)) < density).astype(np.int32)
+    m, off = oracle.mask_row_id_map(mask, num_out)
+    _check_mask_map(m, _brute_mask_map(mask, num_out), E)
+    counts = mask.sum(0)
+    kept = np.minimum(np.concatenate([[0], np.cumsum(counts)]),
+                      counts.sum() if num_out < 0 else num_out)
+    np.testing.assert_array_equal(off, kept)
+
+
+def test_mask_map_every_small_mask():
+    """All 2^(T*E) masks of 3 tokens x 3 experts, with and without dropping."""
+    for bits in range(1 << 9):
+        mask = np.array([(bits >> i) & 1 for i in range(9)], np.uint8).reshape(3, 3)
+        for num_out in (-1, 0, 2, 5):
+            m, _ = oracle.mask_row_id_map(mask, num_out)
+            _check_mask_map(m, _brute_mask_map(mask, num_out), 3)
+
+
+def test_mask_permute_equals_topk_permute():
+    """A mask with k experts per token moves rows exactly as the top-k permute
+    with those experts (the row maps agree); probs are read from [T][E]."""
+    rng = np.random.default_rng(3)
+    T, E, k, H = 37, 9, 3, 16
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    mask = np.zeros((T, E), np.int32)
+    np.put_along_axis(mask, idx.astype(np.int64), 1, axis=1)
+    probs_te = rng.random((T, E)).astype(np.float32) + 0.1
+    probs_k = np.take_along_axis(probs_te, idx.astype(np.int64), axis=1)
+    x = _to_bf16_torch(rng.standard_normal((T, H)).astype(np.float32))
+    mm, _ = oracle.mask_row_id_map(mask)
+    out, out_p = oracle.mask_permute(x, probs_te, mm, T * k)
+    rm, _ = oracle.row_id_map(idx, E)
+    ref, ref_p = oracle.permute(x, probs_k, idx, rm)
+    np.testing.assert_array_equal(out, ref)
+    np.testing.assert_array_equal(out_p.view(np.uint32), ref_p.view(np.uint32))
+
+
+def test_mask_permute_zero_prob_pads():
+    """A routed slot whose prob is 0 (or -0) gets a zero row; its prob is still
+    stored.  Without probs every routed slot is a copy."""
+    x = np.array([[0x3F80, 0x4000], [0xC040, 0x3F00]], np.uint16)
+    mask = np.array([[1, 1, 0], [0, 1, 1]], np.int32)
+    probs = np.array([[0.5, 0.0, 0.0], [0.0, -0.0, 0.25]], np.float32)
+    mm, _ = oracle.mask_row_id_map(mask)      # rows: e0:t0=0, e1:t0=1,t1=2, e2:t1=3
+    out, out_p = oracle.mask_permute(x, probs, mm, 4)
+    np.testing.assert_array_equal(out, [[0x3F80, 0x4000], [0, 0], [0, 0], [0xC040, 0x3F00]])
+    np.testing.assert_array_equal(out_p.view(np.uint32),
+                                  np.array([0.5, 0.0, -0.0, 0.25], np.float32).view(np.uint32))
+    out2, _ = oracle.mask_permute(x, None, mm, 4)
+    np.testing.assert_array_equal(out2, x[[0, 0, 1, 1]])
+
+
+def test_mask_unpermute_adds_in_descending_row_order():
+    """Rows 2^24, 1, -2^24 for experts 0, 1, 2 of one token: in descending row
+    order (-2^24 + 1) + 2^24 = 1 exactly; ascending would round 2^24 + 1
+    to 2^24 and give 0."""
+    inp = np.array([[0x4B80], [0x3F80], [0xCB80]], np.uint16)   # 2^24, 1, -2^24
+    mm, _ = oracle.mask_row_id_map(np.ones((1, 3), np.int32))
+    out, _ = oracle.mask_unpermute(inp, None, mm)
+    assert int(out[0, 0]) == 0x3F80
+
+
+def test_mask_unpermute_multiplies_then_adds():
+    """Product (1+2^-7)(1+2^-23) rounds in fp32 before the add: the sum with
+    -(1+2^-7) is 2^-23 (bf16 0x3400); a fused multiply-add would keep
+    2^-23(1+2^-7) (0x3401).  Map order: expert 1's row, then expert 0's."""
+    inp = np.array([[0x3F81], [0xBF81]], np.uint16)     # rows of e0 and e1
+    mp = np.array([[1.0 + 2.0 ** -23, 1.0]], np.float32)
+    mm, _ = oracle.mask_row_id_map(np.ones((1, 2), np.int32))
+    out, _ = oracle.mask_unpermute(inp, mp, mm)
+    assert int(out[0, 0]) == 0x3400
+
+
+def test_mask_unpermute_probs_scatter_and_identity():
+    rng = np.random.default_rng(8)
+    T, E, H = 30, 6, 12
+    mask = np.zeros((T, E), np.int32)
+    mask[np.arange(T), rng.integers(0, E, T)] = 1          # one expert per token
+    mm, _ = oracle.mask_row_id_map(mask)
+    x = _to_bf16_torch(rng.standard_normal((T, H)).astype(np.float32))
+    perm, _ = oracle.mask_permute(x, None, mm, T)
+    pp = rng.random(T).astype(np.float32)
+    y, up = oracle.mask_unpermute(perm, None, mm, pp)
+    np.testing.assert_array_equal(y, x)                     # one slot, no probs: identity
+    rows = mm[:, 0]
+    ref = np.zeros((T, E), np.float32)
+    ref[np.arange(T), mm[:, E]] = pp[rows]
+    np.testing.assert_array_equal(up, ref)
+
+
+def test_mask_unpermute_bwd_against_direct_products():
+    rng = np.random.default_rng(9)
+    T, E, H = 20, 5, 24
+    mask = (rng.random((T, E)) < 0.5).astype(np.int32)
+    mm, _ = oracle.mask_row_id_map(mask)
+    R = int(mask.sum())
+    mp = rng.random((T, E)).astype(np.float32)
+    g = _to_bf16_torch(rng.standard_normal((T, H)).astype(np.float32))
+    fin = _to_bf16_torch(rng.standard_normal((R, H)).astype(np.float32))
+    d_in, dmp = oracle.mask_unpermute_bwd(g, fin, mp, mm)
+    gv, fv = _bf16_to_f32(g), _bf16_to_f32(fin)
+    for t in range(T):
+        for e in range(E):
+            if not mask[t, e]:
+                assert dmp[t, e] == 0.0
+    for t, pairs in enumerate(_brute_mask_map(mask)):
+        for r, e in pairs:
+            np.testing.assert_array_equal(d_in[r], _to_bf16_torch(gv[t] * mp[t, e]))
+            ref = float(np.dot(fv[r].astype(np.float64), gv[t].astype(np.float64)))
+            assert abs(dmp[t, e] - ref) <= 2.0 ** -24 * abs(ref) + 1e-45
