@@ -7,13 +7,13 @@
  *   [TE-mask]   d9d 0.1.0 wheel, d9d/kernel/moe/permute_with_probs.py (a copy
  *               of TransformerEngine's mask-map permutation): make_row_id_map
  *               and its worked example, _permute_kernel, _unpermute_kernel,
- *               _unpermute_bwd_with_merging_probs_kernel and the two autograd
- *               functions.
+ *               _unpermute_bwd_with_merging_probs_kernel, the two autograd
+ *               functions and moe_permute_with_probs (num_out_tokens).
  *   [MCORE-BI]  Megatron-core API docs, core.transformer.moe.batch_invariant:
  *               unpermute_with_bf16_rank_partials, _rank_tree_unpermute_kernel,
  *               _rank_tree_unpermute_bwd_kernel, _unpermute_loop.
- *   [MOE-OPS]   moe-ops 0.1.0 README: "Why this library" and "Routing
- *               permute / unpermute".
+ *   [MOE-OPS]   moe-ops 0.1.0 README: "Why this library", "Routing
+ *               permute / unpermute" and "Fused Top-K Softmax".
  *   [XTUNER]    xtuner issue "permute different with torch version".
  *   [TE-3509]   TransformerEngine PR "[PyTorch] Fuse MoE chunk sorting and
  *               padding": Description, Changes, Validation, Diagram.
@@ -273,6 +273,84 @@ MOE_PERM_API int moe_topk_softmax_bwd(const void *d_probs, const void *probs, in
                                       const int32_t *topk_idx, int num_tokens, int num_experts,
                                       int topk, void *d_logits, int logit_bytes,
                                       int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * TransformerEngine mask-map form (interop for callers holding a routing
+ * mask instead of top-k indices).
+ *
+ * [TE-mask] make_row_id_map: routing_map [num_tokens][num_experts], entry !=
+ * 0 routes the token to the expert (mask_bytes 1: bool / uint8, or 4:
+ * int32).  Destination rows are the same counting sort as
+ * moe_make_row_id_map: expert-major, tokens ascending inside an expert.
+ * [TE-mask] moe_permute_with_probs, num_out_tokens (the count of rows not
+ * dropped): a row >= num_out_tokens is dropped; -1 keeps every row.
+ * row_id_map [num_tokens][2*num_experts+1], per token t:
+ *   [0, n)            its kept destination rows in descending order,
+ *   [E, E + n)        the expert of each of those rows,
+ *   [2E]              n;
+ * every other entry is left unwritten (the page leaves them unused).
+ * expert_offsets [E+1] (optional): kept rows of the experts below e; the
+ * last entry is the number of kept rows.  Workspace as for the top-k map:
+ * moe_make_mask_row_id_map_workspace_bytes(), 256-byte aligned.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API size_t moe_make_mask_row_id_map_workspace_bytes(int num_tokens, int num_experts);
+MOE_PERM_API int moe_make_mask_row_id_map(const void *routing_map, int mask_bytes,
+                                          int num_tokens, int num_experts, int num_out_tokens,
+                                          int32_t *row_id_map, int32_t *expert_offsets,
+                                          void *workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+/*
+ * [TE-mask] _permute_kernel: out[row] = x[t] for each slot of token t's map
+ * row.  With probs ([num_tokens][num_experts] fp32): out_probs[row] =
+ * probs[t][e], and a prob equal to zero (+0 or -0) marks a padded slot
+ * whose out row is written as zeros instead of x[t].  Rows of out that no
+ * map entry names are not written.  Also the backward of the unpermute
+ * without merging probs (d_in = this gather-copy of d_out).
+ *   x [num_tokens][hidden] bf16 (any 2-byte type without probs),
+ *   out [num_out_rows][hidden], out_probs [num_out_rows] (optional).
+ *   dev_status: MOE_DEV_BAD_EXPERT, MOE_DEV_BAD_ROW (a row outside
+ *   [0, num_out_rows), or a count outside [0, E]).
+ */
+MOE_PERM_API int moe_permute_mask(const void *x, const float *probs, const int32_t *row_id_map,
+                                  int num_tokens, int hidden, int num_experts, int num_out_rows,
+                                  void *out, float *out_probs, int32_t *dev_status,
+                                  hipStream_t stream);
+
+/*
+ * [TE-mask] _unpermute_kernel: per token and element, an fp32 accumulator
+ * from +0 visits the token's rows in map order (descending rows); each row
+ * is widened to fp32, multiplied by merging_probs[t][e] when given (one
+ * fp32 rounding), then added (a second rounding); the sum is rounded to
+ * nearest-even bf16.  This is TE's arithmetic, not the fused slot-order
+ * combine of moe_unpermute.  With unpermuted_probs ([num_tokens][num_experts]
+ * fp32, optional): permuted_probs[row] at each routed expert (0 when
+ * permuted_probs is NULL), 0 elsewhere.  Without merging probs this is also
+ * the backward of moe_permute_mask: d_x = this sum of d_out rows, and the
+ * probs gradient is the unpermuted_probs of d_out_probs.
+ *   in [num_in_rows][hidden] bf16, out [num_tokens][hidden] bf16.
+ *   dev_status: MOE_DEV_BAD_EXPERT, MOE_DEV_BAD_ROW.
+ */
+MOE_PERM_API int moe_unpermute_mask(const void *in, const float *merging_probs,
+                                    const float *permuted_probs, const int32_t *row_id_map,
+                                    int num_tokens, int hidden, int num_experts, int num_in_rows,
+                                    void *out, float *unpermuted_probs, int32_t *dev_status,
+                                    hipStream_t stream);
+
+/*
+ * [TE-mask] _unpermute_bwd_with_merging_probs_kernel: for each slot of
+ * token t (row, expert e), d_in[row] = bf16(fp32(d_out[t] * merging_probs
+ * [t][e])), and d_merging_probs[t][e] = sum_h fwd_in[row][h] * d_out[t][h]
+ * (fp32; its summation order is the kernel's own); the other experts of
+ * the row get 0.  d_merging_probs (optional) needs fwd_in.  Rows of d_in no
+ * map entry names are not written.
+ *   dev_status: MOE_DEV_BAD_EXPERT, MOE_DEV_BAD_ROW.
+ */
+MOE_PERM_API int moe_unpermute_mask_bwd(const void *d_out, const void *fwd_in,
+                                        const float *merging_probs, const int32_t *row_id_map,
+                                        int num_tokens, int hidden, int num_experts,
+                                        int num_rows, void *d_in, float *d_merging_probs,
+                                        int32_t *dev_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * (3) Fused chunk sort-and-pad.

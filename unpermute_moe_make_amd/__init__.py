@@ -8,6 +8,8 @@ with a thin ctypes binding whose functions carry the C names:
   moe_unpermute / moe_unpermute_bwd   fixed slot-order FMA combine, gradient
   moe_unpermute_ep                    the combine with EP rank-ordered partials
   moe_topk_softmax(_bwd)              fused top-k softmax router, gradient
+  moe_make_mask_row_id_map            TE mask-map form: [T, 2E+1] map from a mask
+  moe_permute_mask / moe_unpermute_mask(_bwd)  TE-order copies and combine
   moe_sort_chunks_and_pad(_bwd)       fused chunk regroup + zero padding
   moe_unpad_and_restore_chunks(_bwd)  the matching restore
 
@@ -26,6 +28,11 @@ from ._binding import (  # noqa: F401
     library_path,
     moe_make_row_id_map,
     moe_make_row_id_map_workspace_bytes,
+    moe_make_mask_row_id_map,
+    moe_make_mask_row_id_map_workspace_bytes,
+    moe_permute_mask,
+    moe_unpermute_mask,
+    moe_unpermute_mask_bwd,
     moe_permute,
     moe_permute_bwd,
     moe_sort_chunks_and_pad,

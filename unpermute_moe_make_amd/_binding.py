@@ -38,6 +38,11 @@ _SIGS = {
     "moe_unpermute_ep": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_unpermute_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_permute_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+    "moe_make_mask_row_id_map_workspace_bytes": ([_I, _I], _Z),
+    "moe_make_mask_row_id_map": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "moe_permute_mask": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+    "moe_unpermute_mask": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+    "moe_unpermute_mask_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_topk_softmax": ([_P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
     "moe_topk_softmax_bwd": ([_P, _P, _I, _P, _I, _I, _I, _P, _I, _P, _P], _I),
     "moe_sort_chunks_and_pad": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P,
@@ -284,6 +289,124 @@ def moe_permute_bwd(d_out: torch.Tensor, topk_idx: torch.Tensor, row_id_map: tor
                                 _ptr(_status_arg(dev_status)), _stream(stream)),
            "moe_permute_bwd")
     return d_x, d_probs
+
+
+# ---------------------------------------------------------------------------
+# TransformerEngine mask-map form
+# ---------------------------------------------------------------------------
+
+def moe_make_mask_row_id_map_workspace_bytes(num_tokens: int, num_experts: int) -> int:
+    return int(_lib.moe_make_mask_row_id_map_workspace_bytes(num_tokens, num_experts))
+
+
+def moe_make_mask_row_id_map(routing_map: torch.Tensor, *, num_out_tokens: int = -1,
+                             row_id_map=None, expert_offsets=None, workspace=None, stream=None):
+    """[T, E] routing mask (bool / uint8 / int8 / int32) -> (row_id_map [T, 2E+1],
+    expert_offsets [E+1]); rows at or past num_out_tokens are dropped."""
+    _need(routing_map, "routing_map")
+    if routing_map.dim() != 2:
+        raise ValueError("routing_map must be [num_tokens, num_experts]")
+    if routing_map.dtype in (torch.bool, torch.uint8, torch.int8):
+        mb = 1
+    elif routing_map.dtype == torch.int32:
+        mb = 4
+    else:
+        raise TypeError("routing_map must be bool, uint8, int8 or int32")
+    T, E = routing_map.shape
+    dev = routing_map.device
+    row_id_map = (torch.empty((T, 2 * E + 1), dtype=torch.int32, device=dev)
+                  if row_id_map is None else
+                  _need(row_id_map, "row_id_map", torch.int32, (T, 2 * E + 1)))
+    expert_offsets = (torch.empty(E + 1, dtype=torch.int32, device=dev)
+                      if expert_offsets is None else
+                      _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,)))
+    need = moe_make_mask_row_id_map_workspace_bytes(T, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace")
+    _check(_lib.moe_make_mask_row_id_map(
+        _ptr(routing_map), mb, T, E, num_out_tokens, _ptr(row_id_map), _ptr(expert_offsets),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "moe_make_mask_row_id_map")
+    return row_id_map, expert_offsets
+
+
+def _mask_map(row_id_map):
+    _need(row_id_map, "row_id_map", torch.int32)
+    if row_id_map.dim() != 2 or row_id_map.shape[1] % 2 != 1:
+        raise ValueError("row_id_map must be [num_tokens, 2 * num_experts + 1]")
+    return row_id_map.shape[0], (row_id_map.shape[1] - 1) // 2
+
+
+def moe_permute_mask(x: torch.Tensor, row_id_map: torch.Tensor, num_out_rows: int,
+                     probs: Optional[torch.Tensor] = None, *, out=None, out_probs=None,
+                     dev_status=None, stream=None):
+    """out[row] = x[t] per map slot; with probs [T, E]: out_probs[row] = probs[t, e]
+    and a zero prob writes a zero row.  Returns (out, out_probs)."""
+    T, E = _mask_map(row_id_map)
+    _bf16_like_2d(x, "x")
+    if x.shape[0] != T:
+        raise ValueError("x must have num_tokens rows")
+    H = x.shape[1]
+    _opt(probs, "probs", torch.float32, (T, E))
+    out = torch.empty((num_out_rows, H), dtype=x.dtype, device=x.device) if out is None else \
+        _need(out, "out", x.dtype, (num_out_rows, H))
+    if probs is not None and out_probs is None:
+        out_probs = torch.empty(num_out_rows, dtype=torch.float32, device=x.device)
+    _opt(out_probs, "out_probs", torch.float32, (num_out_rows,))
+    _check(_lib.moe_permute_mask(_ptr(x), _ptr(probs), _ptr(row_id_map), T, H, E, num_out_rows,
+                                 _ptr(out), _ptr(out_probs), _ptr(_status_arg(dev_status)),
+                                 _stream(stream)), "moe_permute_mask")
+    return out, out_probs
+
+
+def moe_unpermute_mask(inp: torch.Tensor, row_id_map: torch.Tensor,
+                       merging_probs: Optional[torch.Tensor] = None,
+                       permuted_probs: Optional[torch.Tensor] = None, *, out=None,
+                       unpermuted_probs=None, dev_status=None, stream=None):
+    """TE-order combine: rows in map order, times merging_probs[t, e], added in
+    fp32.  Returns (out [T, H], unpermuted_probs [T, E] or None)."""
+    T, E = _mask_map(row_id_map)
+    _bf16_like_2d(inp, "inp")
+    n, H = inp.shape
+    _opt(merging_probs, "merging_probs", torch.float32, (T, E))
+    _opt(permuted_probs, "permuted_probs", torch.float32, (n,))
+    out = torch.empty((T, H), dtype=inp.dtype, device=inp.device) if out is None else \
+        _need(out, "out", inp.dtype, (T, H))
+    if permuted_probs is not None and unpermuted_probs is None:
+        unpermuted_probs = torch.empty((T, E), dtype=torch.float32, device=inp.device)
+    _opt(unpermuted_probs, "unpermuted_probs", torch.float32, (T, E))
+    _check(_lib.moe_unpermute_mask(_ptr(inp), _ptr(merging_probs), _ptr(permuted_probs),
+                                   _ptr(row_id_map), T, H, E, n, _ptr(out),
+                                   _ptr(unpermuted_probs), _ptr(_status_arg(dev_status)),
+                                   _stream(stream)), "moe_unpermute_mask")
+    return out, unpermuted_probs
+
+
+def moe_unpermute_mask_bwd(d_out: torch.Tensor, fwd_in: torch.Tensor,
+                           merging_probs: torch.Tensor, row_id_map: torch.Tensor, *,
+                           d_in=None, d_merging_probs=None, want_probs_grad: bool = True,
+                           dev_status=None, stream=None):
+    """d_in[row] = bf16(d_out[t] * p) per slot; d_merging_probs[t, e] = fp32 dot of
+    fwd_in[row] and d_out[t].  Returns (d_in, d_merging_probs or None)."""
+    T, E = _mask_map(row_id_map)
+    _bf16_like_2d(d_out, "d_out")
+    _bf16_like_2d(fwd_in, "fwd_in")
+    n, H = fwd_in.shape
+    if d_out.shape != (T, H):
+        raise ValueError("d_out must be [num_tokens, hidden]")
+    _need(merging_probs, "merging_probs", torch.float32, (T, E))
+    d_in = torch.empty((n, H), dtype=d_out.dtype, device=d_out.device) if d_in is None else \
+        _need(d_in, "d_in", d_out.dtype, (n, H))
+    if want_probs_grad and d_merging_probs is None:
+        d_merging_probs = torch.empty((T, E), dtype=torch.float32, device=d_out.device)
+    _opt(d_merging_probs, "d_merging_probs", torch.float32, (T, E))
+    _check(_lib.moe_unpermute_mask_bwd(_ptr(d_out), _ptr(fwd_in), _ptr(merging_probs),
+                                       _ptr(row_id_map), T, H, E, n, _ptr(d_in),
+                                       _ptr(d_merging_probs), _ptr(_status_arg(dev_status)),
+                                       _stream(stream)), "moe_unpermute_mask_bwd")
+    return d_in, d_merging_probs
 
 
 # ---------------------------------------------------------------------------

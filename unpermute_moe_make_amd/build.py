@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoeperm.so")
-SOURCES = ["api.hip", "row_map.hip", "permute.hip", "chunks.hip", "router.hip"]
+SOURCES = ["api.hip", "row_map.hip", "permute.hip", "chunks.hip", "router.hip", "mask.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -202,6 +202,104 @@ MOE_PERM_API int moe_permute_bwd(const void *d_out, const float *d_out_probs,
                                         dev_status, vec_ok(H, d_out, d_x), stream));
 }
 
+MOE_PERM_API size_t moe_make_mask_row_id_map_workspace_bytes(int num_tokens, int num_experts) {
+  if (num_tokens < 0 || num_experts < 1) return 0;
+  return moe::maskmap_workspace_bytes(num_tokens, num_experts);
+}
+
+MOE_PERM_API int moe_make_mask_row_id_map(const void *routing_map, int mask_bytes,
+                                          int num_tokens, int num_experts, int num_out_tokens,
+                                          int32_t *row_id_map, int32_t *expert_offsets,
+                                          void *workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  const int T = num_tokens, E = num_experts;
+  if (T < 0 || E < 1 || num_out_tokens < -1) return MOE_ERR_SHAPE;
+  if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (mask_bytes != 1 && mask_bytes != 4) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * E > INT32_MAX || (int64_t)T * (2 * (int64_t)E + 1) > INT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (routing_map == nullptr || row_id_map == nullptr)) return MOE_ERR_NULL;
+  if (!aligned(routing_map, (uintptr_t)mask_bytes) || !aligned(row_id_map, 4) ||
+      !aligned(expert_offsets, 4))
+    return MOE_ERR_ALIGN;
+  if (T > 0) {
+    const size_t need = moe::maskmap_workspace_bytes(T, E);
+    if (workspace == nullptr || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  }
+  return hip_status(moe::launch_maskmap(routing_map, mask_bytes, T, E, num_out_tokens,
+                                        row_id_map, expert_offsets, workspace, stream));
+}
+
+// Checks shared by the mask-map row calls.
+static int check_mask_rows(int T, int H, int E, int n_rows) {
+  if (T < 0 || H < 1 || E < 1 || n_rows < 0) return MOE_ERR_SHAPE;
+  if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * E > INT32_MAX || (int64_t)T * (2 * (int64_t)E + 1) > INT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+MOE_PERM_API int moe_permute_mask(const void *x, const float *probs, const int32_t *row_id_map,
+                                  int num_tokens, int hidden, int num_experts, int num_out_rows,
+                                  void *out, float *out_probs, int32_t *dev_status,
+                                  hipStream_t stream) {
+  const int T = num_tokens, H = hidden, E = num_experts;
+  int st = check_mask_rows(T, H, E, num_out_rows);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !row_id_map || (num_out_rows > 0 && !out)) return MOE_ERR_NULL;
+  if (out_probs != nullptr && probs == nullptr) return MOE_ERR_NULL;
+  if (!aligned(x, 2) || !aligned(out, 2) || !aligned(probs, 4) || !aligned(out_probs, 4) ||
+      !aligned(row_id_map, 4) || !aligned(dev_status, 4))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_mask_permute(x, probs, row_id_map, T, H, E, num_out_rows, out,
+                                             out_probs, dev_status, vec_ok(H, x, out), stream));
+}
+
+MOE_PERM_API int moe_unpermute_mask(const void *in, const float *merging_probs,
+                                    const float *permuted_probs, const int32_t *row_id_map,
+                                    int num_tokens, int hidden, int num_experts, int num_in_rows,
+                                    void *out, float *unpermuted_probs, int32_t *dev_status,
+                                    hipStream_t stream) {
+  const int T = num_tokens, H = hidden, E = num_experts;
+  int st = check_mask_rows(T, H, E, num_in_rows);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (!row_id_map || !out || (num_in_rows > 0 && !in)) return MOE_ERR_NULL;
+  if (permuted_probs != nullptr && unpermuted_probs == nullptr) return MOE_ERR_NULL;
+  if (!aligned(in, 2) || !aligned(out, 2) || !aligned(merging_probs, 4) ||
+      !aligned(permuted_probs, 4) || !aligned(unpermuted_probs, 4) ||
+      !aligned(row_id_map, 4) || !aligned(dev_status, 4))
+    return MOE_ERR_ALIGN;
+  const bool vec = in != nullptr ? vec_ok(H, in, out) : vec_ok(H, out, out);
+  return hip_status(moe::launch_mask_unpermute(in, merging_probs, permuted_probs, row_id_map, T,
+                                               H, E, num_in_rows, out, unpermuted_probs,
+                                               dev_status, vec, stream));
+}
+
+MOE_PERM_API int moe_unpermute_mask_bwd(const void *d_out, const void *fwd_in,
+                                        const float *merging_probs, const int32_t *row_id_map,
+                                        int num_tokens, int hidden, int num_experts,
+                                        int num_rows, void *d_in, float *d_merging_probs,
+                                        int32_t *dev_status, hipStream_t stream) {
+  const int T = num_tokens, H = hidden, E = num_experts;
+  int st = check_mask_rows(T, H, E, num_rows);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (!d_out || !merging_probs || !row_id_map || (num_rows > 0 && !d_in)) return MOE_ERR_NULL;
+  if (d_merging_probs != nullptr && num_rows > 0 && fwd_in == nullptr) return MOE_ERR_NULL;
+  if (!aligned(d_out, 2) || !aligned(fwd_in, 2) || !aligned(d_in, 2) ||
+      !aligned(merging_probs, 4) || !aligned(d_merging_probs, 4) || !aligned(row_id_map, 4) ||
+      !aligned(dev_status, 4))
+    return MOE_ERR_ALIGN;
+  const void *d_in_or = d_in != nullptr ? d_in : d_out;
+  const bool vec = vec_ok(H, d_out, d_in_or, d_merging_probs ? fwd_in : nullptr);
+  return hip_status(moe::launch_mask_unpermute_bwd(d_out, fwd_in, merging_probs, row_id_map, T,
+                                                   H, E, num_rows, d_in, d_merging_probs,
+                                                   dev_status, vec, stream));
+}
+
 MOE_PERM_API int moe_topk_softmax(const void *logits, int logit_bytes, int num_tokens,
                                   int num_experts, int topk, int32_t *topk_idx, void *probs,
                                   int prob_bytes, hipStream_t stream) {

@@ -33,6 +33,23 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
                               int k, int E, int n_rows, void *d_in, float *d_probs,
                               int32_t *dev_status, bool vec, hipStream_t s);
 
+// TransformerEngine mask-map form: map builder and its row kernels.
+size_t maskmap_workspace_bytes(int T, int E);
+hipError_t launch_maskmap(const void *routing_map, int mask_bytes, int T, int E, int num_out,
+                          int32_t *map, int32_t *expert_offsets, void *ws, hipStream_t s);
+hipError_t launch_mask_permute(const void *x, const float *probs, const int32_t *map, int T,
+                               int H, int E, int n_rows, void *out, float *out_probs,
+                               int32_t *dev_status, bool vec, hipStream_t s);
+hipError_t launch_mask_unpermute(const void *in, const float *merging_probs,
+                                 const float *permuted_probs, const int32_t *map, int T, int H,
+                                 int E, int n_rows, void *out, float *unpermuted_probs,
+                                 int32_t *dev_status, bool vec, hipStream_t s);
+hipError_t launch_mask_unpermute_bwd(const void *d_out, const void *fwd_in,
+                                     const float *merging_probs, const int32_t *map, int T,
+                                     int H, int E, int n_rows, void *d_in,
+                                     float *d_merging_probs, int32_t *dev_status, bool vec,
+                                     hipStream_t s);
+
 // Fused top-k softmax router and its gradient.
 hipError_t launch_topk_softmax(const void *logits, int logit_bytes, int T, int E, int k,
                                int32_t *topk_idx, void *probs, int prob_bytes, hipStream_t s);

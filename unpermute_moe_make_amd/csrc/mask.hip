@@ -1,0 +1,421 @@
+// Token-row kernels on the TransformerEngine mask-map form (d9d
+// permute_with_probs.py): the permute (_permute_kernel, with the prob == 0
+// padding rule), the unpermute (_unpermute_kernel: rows visited in map
+// order, each multiplied by its merging prob and then added in fp32, one
+// bf16 rounding; optional [T][E] unpermuted probs) and the unpermute
+// backward with merging probs (_unpermute_bwd_with_merging_probs_kernel).
+//
+// The map row of token t is [rows (n) | unused | experts (n) | unused | n],
+// width 2E+1.  A token may be routed to any number of experts, so the
+// kernels resolve its slots into LDS 64 at a time.  Otherwise the design is
+// that of the top-k row kernels: one workgroup per token row (slice), 16-byte
+// units, every load of a batch in flight before the arithmetic.
+#include "common.h"
+#include "launch.h"
+#include "rows.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSlotChunk = 64;   // slots resolved into LDS at a time
+constexpr int kBatch = 8;        // rows loaded together in the combine
+
+// The token's slot count; bad counts become 0 and set a status bit.
+__device__ __forceinline__ int mask_count(const int32_t *__restrict__ mrow, int E, int *bad) {
+  const int n = mrow[2 * E];
+  if (n < 0 || n > E) {
+    *bad |= MOE_DEV_BAD_ROW;
+    return 0;
+  }
+  return n;
+}
+
+// Slot i of the token: its row (or -1 with a status bit) and expert.
+__device__ __forceinline__ int64_t mask_slot(const int32_t *__restrict__ mrow, int E, int n_rows,
+                                             int i, int *expert, int *bad) {
+  const int e = mrow[E + i];
+  const int r = mrow[i];
+  *expert = e;
+  if ((unsigned)e >= (unsigned)E) {
+    *bad |= MOE_DEV_BAD_EXPERT;
+    return -1;
+  }
+  if ((unsigned)r >= (unsigned)n_rows) {
+    *bad |= MOE_DEV_BAD_ROW;
+    return -1;
+  }
+  return r;
+}
+
+// out[row] = x[t] for each slot; with probs, out_probs[row] = probs[t][e]
+// and a zero prob writes a zero row.
+template <typename U, int VPT>
+__global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
+    const U *__restrict__ x, const float *__restrict__ probs, const int32_t *__restrict__ map,
+    int T, int64_t V, int E, int n_rows, U *__restrict__ out, float *__restrict__ out_probs,
+    int32_t *__restrict__ dev_status) {
+  __shared__ int64_t srow[kSlotChunk];
+  __shared__ int szero[kSlotChunk];
+  const int t = blockIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
+  const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
+
+  U v[VPT];
+  const U *xr = x + (int64_t)t * V;
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = c0 + (int64_t)i * blockDim.x;
+    if (c < V) v[i] = ld_row<false>(xr + c);
+  }
+  U zero;
+  zero = U{};
+  int bad = 0;
+  const int n = mask_count(mrow, E, &bad);
+  for (int j0 = 0; j0 < n; j0 += kSlotChunk) {
+    const int nj = min(kSlotChunk, n - j0);
+    if ((int)threadIdx.x < nj) {
+      int e;
+      const int64_t r = mask_slot(mrow, E, n_rows, j0 + threadIdx.x, &e, &bad);
+      int z = 0;
+      if (probs != nullptr && r >= 0) {
+        const float p = probs[(int64_t)t * E + e];
+        z = p == 0.0f;
+        if (blockIdx.y == 0 && out_probs != nullptr) out_probs[r] = p;
+      }
+      srow[threadIdx.x] = r;
+      szero[threadIdx.x] = z;
+    }
+    __syncthreads();
+    for (int j = 0; j < nj; j++) {
+      const int64_t r = srow[j];
+      if (r < 0) continue;
+      const bool z = szero[j] != 0;
+      U *orow = out + r * V;
+#pragma unroll
+      for (int i = 0; i < VPT; i++) {
+        const int64_t c = c0 + (int64_t)i * blockDim.x;
+        if (c < V) st_row<false>(z ? zero : v[i], orow + c);
+      }
+    }
+    __syncthreads();
+  }
+  if (blockIdx.y == 0) report(dev_status, bad);
+}
+
+// out[t] = bf16(sum over slots in map order of (in[row] * p)), the product
+// and the sum each rounded in fp32 (MERGE), or of in[row] alone.  With
+// unpermuted_probs, row t of it gets permuted_probs[row] at each routed
+// expert (0 when permuted_probs is NULL) and 0 elsewhere.
+template <int EPV, int VPT, bool NT, bool MERGE>
+__global__ __launch_bounds__(kRowThreads) void mask_unpermute_kernel(
+    const typename Bf16Unit<EPV>::T *__restrict__ in, const float *__restrict__ merging_probs,
+    const float *__restrict__ permuted_probs, const int32_t *__restrict__ map, int T, int64_t V,
+    int E, int n_rows, typename Bf16Unit<EPV>::T *__restrict__ out,
+    float *__restrict__ unpermuted_probs, int32_t *__restrict__ dev_status) {
+  using Unit = Bf16Unit<EPV>;
+  using U = typename Unit::T;
+  __shared__ int64_t srow[kSlotChunk];
+  __shared__ float sp[kSlotChunk];
+  __shared__ float sup[MOE_MAX_EXPERTS];
+  const int t = blockIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
+  const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
+  const bool scatter = unpermuted_probs != nullptr && blockIdx.y == 0;
+  if (scatter)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) sup[e] = 0.0f;
+  __syncthreads();
+
+  float acc[VPT][EPV];
+#pragma unroll
+  for (int i = 0; i < VPT; i++)
+#pragma unroll
+    for (int e = 0; e < EPV; e++) acc[i][e] = 0.0f;
+
+  int bad = 0;
+  const int n = mask_count(mrow, E, &bad);
+  for (int j0 = 0; j0 < n; j0 += kSlotChunk) {
+    const int nj = min(kSlotChunk, n - j0);
+    if ((int)threadIdx.x < nj) {
+      int e;
+      const int64_t r = mask_slot(mrow, E, n_rows, j0 + threadIdx.x, &e, &bad);
+      srow[threadIdx.x] = r;
+      if (MERGE) sp[threadIdx.x] = r >= 0 ? merging_probs[(int64_t)t * E + e] : 0.0f;
+      if (scatter && r >= 0) sup[e] = permuted_probs != nullptr ? permuted_probs[r] : 0.0f;
+    }
+    __syncthreads();
+    for (int jb = 0; jb < nj; jb += kBatch) {
+      U vals[kBatch][VPT];
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) {
+        const int64_t r = jb + jj < nj ? srow[jb + jj] : -1;
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+          const int64_t c = c0 + (int64_t)i * blockDim.x;
+          vals[jj][i] = (r >= 0 && c < V) ? ld_row<NT>(in + r * V + c) : Unit::zero();
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) {
+        if (jb + jj >= nj) break;
+        const float p = MERGE ? sp[jb + jj] : 1.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+          float f[EPV];
+          Unit::unpack(vals[jj][i], f);
+#pragma unroll
+          for (int e = 0; e < EPV; e++) {
+            const float term = MERGE ? f[e] * p : f[e];   // rounded before the add
+            acc[i][e] = acc[i][e] + term;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  U *orow = out + (int64_t)t * V;
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = c0 + (int64_t)i * blockDim.x;
+    if (c < V) st_row<NT>(Unit::pack(acc[i]), orow + c);
+  }
+  if (scatter)
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      unpermuted_probs[(int64_t)t * E + e] = sup[e];
+  if (blockIdx.y == 0) report(dev_status, bad);
+}
+
+// d_in[row] = bf16(d_out[t] * p) per slot (one fp32 rounding, then bf16);
+// d_merging_probs[t][e] = sum_h fwd_in[row][h] * d_out[t][h] at routed
+// experts (a fixed per-lane fmaf chain, then a fixed tree), 0 elsewhere.
+// With the probs gradient the workgroup walks the whole row in passes.
+template <int EPV, int VPT, bool NT>
+__global__ __launch_bounds__(kRowThreads) void mask_unpermute_bwd_kernel(
+    const typename Bf16Unit<EPV>::T *__restrict__ d_out,
+    const typename Bf16Unit<EPV>::T *__restrict__ fwd_in,
+    const float *__restrict__ merging_probs, const int32_t *__restrict__ map, int T, int64_t V,
+    int E, int n_rows, typename Bf16Unit<EPV>::T *__restrict__ d_in,
+    float *__restrict__ d_merging_probs, int32_t *__restrict__ dev_status) {
+  using Unit = Bf16Unit<EPV>;
+  using U = typename Unit::T;
+  __shared__ int64_t srow[kSlotChunk];
+  __shared__ float sp[kSlotChunk];
+  __shared__ int se[kSlotChunk];
+  __shared__ float sred[kRowThreads / kWave][kBatch];
+  __shared__ float sdp[MOE_MAX_EXPERTS];
+  const int t = blockIdx.x;
+  const int64_t pass = (int64_t)blockDim.x * VPT;
+  const int64_t stride = pass * gridDim.y;
+  const int64_t cfirst = (int64_t)blockIdx.y * pass + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
+  const U *grow = d_out + (int64_t)t * V;
+  const bool want_dot = d_merging_probs != nullptr;
+  if (want_dot)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) sdp[e] = 0.0f;
+  __syncthreads();
+
+  int bad = 0;
+  const int n = mask_count(mrow, E, &bad);
+  for (int j0 = 0; j0 < n; j0 += kSlotChunk) {
+    const int nj = min(kSlotChunk, n - j0);
+    if ((int)threadIdx.x < nj) {
+      int e;
+      const int64_t r = mask_slot(mrow, E, n_rows, j0 + threadIdx.x, &e, &bad);
+      srow[threadIdx.x] = r;
+      se[threadIdx.x] = r >= 0 ? e : -1;
+      sp[threadIdx.x] = r >= 0 ? merging_probs[(int64_t)t * E + e] : 0.0f;
+    }
+    __syncthreads();
+    for (int jb = 0; jb < nj; jb += kBatch) {
+      float part[kBatch];
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) part[jj] = 0.0f;
+      for (int64_t cb = cfirst; cb < V; cb += stride) {
+        U graw[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+          const int64_t c = cb + (int64_t)i * blockDim.x;
+          graw[i] = c < V ? ld_row<NT>(grow + c) : Unit::zero();
+        }
+        U fin[kBatch][VPT];
+        if (want_dot) {
+#pragma unroll
+          for (int jj = 0; jj < kBatch; jj++) {
+            const int64_t r = jb + jj < nj ? srow[jb + jj] : -1;
+#pragma unroll
+            for (int i = 0; i < VPT; i++) {
+              const int64_t c = cb + (int64_t)i * blockDim.x;
+              fin[jj][i] = (r >= 0 && c < V) ? ld_row<NT>(fwd_in + r * V + c) : Unit::zero();
+            }
+          }
+        }
+        float g[VPT][EPV];
+#pragma unroll
+        for (int i = 0; i < VPT; i++) Unit::unpack(graw[i], g[i]);
+#pragma unroll
+        for (int jj = 0; jj < kBatch; jj++) {
+          if (jb + jj >= nj) break;
+          const int64_t r = srow[jb + jj];
+          const float p = sp[jb + jj];
+#pragma unroll
+          for (int i = 0; i < VPT; i++) {
+            const int64_t c = cb + (int64_t)i * blockDim.x;
+            float prod[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; e++) prod[e] = g[i][e] * p;
+            if (r >= 0 && c < V) st_row<NT>(Unit::pack(prod), d_in + r * V + c);
+            if (want_dot) {
+              float f[EPV];
+              Unit::unpack(fin[jj][i], f);
+#pragma unroll
+              for (int e = 0; e < EPV; e++) part[jj] = __builtin_fmaf(f[e], g[i][e], part[jj]);
+            }
+          }
+        }
+      }
+      if (want_dot) {
+#pragma unroll
+        for (int jj = 0; jj < kBatch; jj++) {
+          const float s = wave_sum(part[jj]);
+          if (lane == 0) sred[wv][jj] = s;
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < kBatch && jb + (int)threadIdx.x < nj) {
+          const int e = se[jb + threadIdx.x];
+          float s = 0.0f;
+          for (int w = 0; w < nwaves; w++) s += sred[w][threadIdx.x];
+          if (e >= 0) sdp[e] = s;
+        }
+        __syncthreads();
+      }
+    }
+    __syncthreads();
+  }
+  if (want_dot)
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      d_merging_probs[(int64_t)t * E + e] = sdp[e];
+  if (blockIdx.y == 0) report(dev_status, bad);
+}
+
+template <typename U>
+void mask_permute_dispatch(const void *x, const float *probs, const int32_t *map, int T,
+                           int64_t V, int E, int n_rows, void *out, float *out_probs,
+                           int32_t *st, hipStream_t s) {
+  const RowShape sh = row_shape(V, true);
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const U *xp = static_cast<const U *>(x);
+  U *op = static_cast<U *>(out);
+#define MOE_MASK_PERMUTE(VPTV)                                                              \
+  hipLaunchKernelGGL((mask_permute_kernel<U, VPTV>), grid, block, 0, s, xp, probs, map, T, V, \
+                     E, n_rows, op, out_probs, st)
+  switch (sh.vpt) {
+    case 1: MOE_MASK_PERMUTE(1); break;
+    case 2: MOE_MASK_PERMUTE(2); break;
+    default: MOE_MASK_PERMUTE(4); break;
+  }
+#undef MOE_MASK_PERMUTE
+}
+
+template <int EPV, bool NT>
+void mask_unpermute_dispatch(const void *in, const float *mp, const float *pp,
+                             const int32_t *map, int T, int64_t V, int E, int n_rows, void *out,
+                             float *up, int32_t *st, hipStream_t s) {
+  using U = typename Bf16Unit<EPV>::T;
+  const RowShape sh = row_shape(V, true);
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const U *ip = static_cast<const U *>(in);
+  U *op = static_cast<U *>(out);
+#define MOE_MASK_UNPERMUTE(VPTV, MERGE)                                                        \
+  hipLaunchKernelGGL((mask_unpermute_kernel<EPV, VPTV, NT, MERGE>), grid, block, 0, s, ip, mp, \
+                     pp, map, T, V, E, n_rows, op, up, st)
+  if (mp != nullptr) {
+    switch (sh.vpt) {
+      case 1: MOE_MASK_UNPERMUTE(1, true); break;
+      case 2: MOE_MASK_UNPERMUTE(2, true); break;
+      default: MOE_MASK_UNPERMUTE(4, true); break;
+    }
+  } else {
+    switch (sh.vpt) {
+      case 1: MOE_MASK_UNPERMUTE(1, false); break;
+      case 2: MOE_MASK_UNPERMUTE(2, false); break;
+      default: MOE_MASK_UNPERMUTE(4, false); break;
+    }
+  }
+#undef MOE_MASK_UNPERMUTE
+}
+
+template <int EPV, bool NT>
+void mask_unpermute_bwd_dispatch(const void *d_out, const void *fwd_in, const float *mp,
+                                 const int32_t *map, int T, int64_t V, int E, int n_rows,
+                                 void *d_in, float *dmp, int32_t *st, hipStream_t s) {
+  using U = typename Bf16Unit<EPV>::T;
+  const RowShape sh = row_shape(V, dmp == nullptr);
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const U *gp = static_cast<const U *>(d_out);
+  const U *fp = static_cast<const U *>(fwd_in);
+  U *dp = static_cast<U *>(d_in);
+#define MOE_MASK_BWD(VPTV)                                                                     \
+  hipLaunchKernelGGL((mask_unpermute_bwd_kernel<EPV, VPTV, NT>), grid, block, 0, s, gp, fp, mp, \
+                     map, T, V, E, n_rows, dp, dmp, st)
+  switch (sh.vpt) {
+    case 1: MOE_MASK_BWD(1); break;
+    case 2: MOE_MASK_BWD(2); break;
+    default: MOE_MASK_BWD(4); break;
+  }
+#undef MOE_MASK_BWD
+}
+
+}  // namespace
+
+hipError_t launch_mask_permute(const void *x, const float *probs, const int32_t *map, int T,
+                               int H, int E, int n_rows, void *out, float *out_probs,
+                               int32_t *dev_status, bool vec, hipStream_t s) {
+  if (vec)
+    mask_permute_dispatch<v4u>(x, probs, map, T, H / 8, E, n_rows, out, out_probs, dev_status,
+                               s);
+  else
+    mask_permute_dispatch<uint16_t>(x, probs, map, T, H, E, n_rows, out, out_probs, dev_status,
+                                    s);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_unpermute(const void *in, const float *merging_probs,
+                                 const float *permuted_probs, const int32_t *map, int T, int H,
+                                 int E, int n_rows, void *out, float *unpermuted_probs,
+                                 int32_t *dev_status, bool vec, hipStream_t s) {
+  const bool stream = 2ll * H * ((int64_t)n_rows + T) > kStreamBytes;
+  if (vec && stream)
+    mask_unpermute_dispatch<8, true>(in, merging_probs, permuted_probs, map, T, H / 8, E, n_rows,
+                                     out, unpermuted_probs, dev_status, s);
+  else if (vec)
+    mask_unpermute_dispatch<8, false>(in, merging_probs, permuted_probs, map, T, H / 8, E,
+                                      n_rows, out, unpermuted_probs, dev_status, s);
+  else
+    mask_unpermute_dispatch<1, false>(in, merging_probs, permuted_probs, map, T, H, E, n_rows,
+                                      out, unpermuted_probs, dev_status, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_unpermute_bwd(const void *d_out, const void *fwd_in,
+                                     const float *merging_probs, const int32_t *map, int T,
+                                     int H, int E, int n_rows, void *d_in,
+                                     float *d_merging_probs, int32_t *dev_status, bool vec,
+                                     hipStream_t s) {
+  const bool stream =
+      2ll * H * ((int64_t)n_rows * (d_merging_probs ? 2 : 1) + T) > kStreamBytes;
+  if (vec && stream)
+    mask_unpermute_bwd_dispatch<8, true>(d_out, fwd_in, merging_probs, map, T, H / 8, E, n_rows,
+                                         d_in, d_merging_probs, dev_status, s);
+  else if (vec)
+    mask_unpermute_bwd_dispatch<8, false>(d_out, fwd_in, merging_probs, map, T, H / 8, E,
+                                          n_rows, d_in, d_merging_probs, dev_status, s);
+  else
+    mask_unpermute_bwd_dispatch<1, false>(d_out, fwd_in, merging_probs, map, T, H, E, n_rows,
+                                          d_in, d_merging_probs, dev_status, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -20,20 +20,12 @@
 
 #include "common.h"
 #include "launch.h"
+#include "rows.h"
 
 namespace moe {
 namespace {
 
 constexpr int kMaxTopk = MOE_MAX_TOPK;
-// Largest row workgroup (512 keeps 256 VGPRs per lane available) and the
-// units per lane (0: chosen per row length); build-time tuning constants.
-#ifndef MOE_ROW_MAX_THREADS
-#define MOE_ROW_MAX_THREADS 512
-#endif
-#ifndef MOE_ROW_VPT
-#define MOE_ROW_VPT 0
-#endif
-constexpr int kRowThreads = MOE_ROW_MAX_THREADS;
 
 // Resolve the token's slots into LDS.  Returns status bits of this lane.
 __device__ __forceinline__ int resolve_slots(const int32_t *__restrict__ topk_idx,
@@ -401,44 +393,6 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
       __syncthreads();
     }
   }
-}
-
-// ------------------------------------------------------------ launch shape --
-
-struct RowShape {
-  int threads;  // workgroup size, multiple of 64
-  int vpt;      // units per lane per row slice
-  int ysplit;   // row slices per token (grid.y)
-};
-
-// One workgroup per token row (slice): cover V units with `threads` lanes of
-// `vpt` units each, preferring the least idle lanes, then mid-size groups.
-RowShape row_shape(int64_t V, bool allow_split) {
-  const int kMaxThreads = kRowThreads;
-  int ysplit = 1;
-  if (allow_split && V > (int64_t)kMaxThreads * 4)
-    ysplit = (int)((V + (int64_t)kMaxThreads * 4 - 1) / ((int64_t)kMaxThreads * 4));
-  const int64_t Vs = (V + ysplit - 1) / ysplit;
-  // Fallback for an unsplit row longer than one full-size pass.
-  RowShape best{kMaxThreads, 4, ysplit};
-  int64_t best_waste = -1;
-  int best_score = 0;
-  const int vpts[] = {1, 2, 4};
-  for (int vpt : vpts) {
-    if (MOE_ROW_VPT != 0 && vpt != MOE_ROW_VPT) continue;
-    int64_t th = (Vs + vpt - 1) / vpt;
-    th = ((th + kWave - 1) / kWave) * kWave;
-    if (th > kMaxThreads) continue;
-    const int64_t waste = th * vpt - Vs;
-    // prefer 256..512 threads, then fewer units per lane
-    const int score = (th >= 256 && th <= 512 ? 0 : (th < 256 ? 1 : 2)) * 8 + vpt;
-    if (best_waste < 0 || waste < best_waste || (waste == best_waste && score < best_score)) {
-      best = RowShape{(int)th, vpt, ysplit};
-      best_waste = waste;
-      best_score = score;
-    }
-  }
-  return best;
 }
 
 template <typename U>

@@ -24,6 +24,8 @@
 //   earlier blocks would grow quadratically, so a column-scan kernel (one
 //   workgroup per expert, a parallel scan over the blocks) computes the
 //   bases once and the write kernel reads them: three launches.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -206,6 +208,151 @@ __global__ __launch_bounds__(kTokPerBlock) void rowmap_write_kernel(
   }
 }
 
+// ----------------------------------------------------- mask-map (TE) form --
+//
+// d9d permute_with_probs.py (TransformerEngine mask-map permutation),
+// make_row_id_map: a [T][E] routing mask instead of top-k indices, and a
+// per-token map [T][2E+1]: the token's destination rows in descending
+// order, then their experts, then their count.  The rows are the same
+// counting sort as above; only the input and the final layout differ.  For a
+// fixed token the rows grow with the expert (expert-major), so descending
+// rows are simply the routed experts walked from E-1 down to 0.
+
+// Masks from a [T][E] routing mask: lane l of wave w holds V experts and
+// builds their 64-bit token masks over the wave's 64 tokens, one coalesced
+// row segment per token.  MB: bytes per mask entry; V: experts per lane
+// (one vector load of V entries).
+template <int MB, int V>
+__global__ __launch_bounds__(kTokPerBlock) void maskmap_count_kernel(
+    const void *__restrict__ routing_map, int T, int E, unsigned long long *__restrict__ masks,
+    int32_t *__restrict__ counts) {
+  extern __shared__ int s_cnt[];  // [4][E]
+  using Vec = typename std::conditional<
+      MB * V == 16, v4u,
+      typename std::conditional<MB * V == 4, uint32_t,
+                                typename std::conditional<MB * V == 2, uint16_t,
+                                                          uint8_t>::type>::type>::type;
+  static_assert(sizeof(Vec) == MB * V, "one load per lane and token");
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int tw = b * kTokPerBlock + w * kWave;   // first token of the wave tile
+  const int ntw = max(0, min(kWave, T - tw));
+  for (int e0 = lane * V; e0 < E; e0 += kWave * V) {
+    unsigned long long bits[V];
+#pragma unroll
+    for (int c = 0; c < V; c++) bits[c] = 0ull;
+    const char *base = static_cast<const char *>(routing_map) + ((int64_t)tw * E + e0) * MB;
+#pragma unroll 8
+    for (int i = 0; i < ntw; i++) {
+      const Vec raw = *reinterpret_cast<const Vec *>(base + (int64_t)i * E * MB);
+      const uint8_t *bytes = reinterpret_cast<const uint8_t *>(&raw);
+#pragma unroll
+      for (int c = 0; c < V; c++) {
+        bool on;
+        if constexpr (MB == 4)
+          on = reinterpret_cast<const uint32_t *>(bytes)[c] != 0u;
+        else
+          on = bytes[c] != 0;
+        bits[c] |= (unsigned long long)on << i;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < V; c++) {
+      masks[((int64_t)b * kWavesPerBlock + w) * E + e0 + c] = bits[c];
+      s_cnt[w * E + e0 + c] = __popcll(bits[c]);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kTokPerBlock)
+    counts[(int64_t)b * E + e] =
+        s_cnt[e] + s_cnt[E + e] + s_cnt[2 * E + e] + s_cnt[3 * E + e];
+}
+
+constexpr int kMaskChunk = kTokPerBlock;   // experts staged in LDS at a time
+
+// Per-token map rows.  FUSED as for rowmap_write_kernel.  Each lane owns
+// one token and walks the experts from the top down, chunk by chunk,
+// appending its kept rows; entries past the token's count are not written.
+template <bool FUSED>
+__global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
+    const unsigned long long *__restrict__ masks, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ totals, int T, int E, int nb, int num_out,
+    int32_t *__restrict__ map, int32_t *__restrict__ expert_offsets) {
+  __shared__ int s_off[MOE_MAX_EXPERTS];
+  __shared__ unsigned long long s_mask[kWavesPerBlock][kMaskChunk];
+  __shared__ int s_base[kWavesPerBlock][kMaskChunk];
+  __shared__ int wave_tot[kTokPerBlock / kWave];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  for (int e = tid; e < E; e += kTokPerBlock) {
+    int tot = 0;
+    if (FUSED) {
+#pragma unroll 8
+      for (int b2 = 0; b2 < nb; b2++) tot += counts[(int64_t)b2 * E + e];
+    } else {
+      tot = totals[e];
+    }
+    s_off[e] = tot;
+  }
+  __syncthreads();
+  const int total = block_scan_lds(s_off, E, wave_tot);
+  const int kept = num_out >= 0 ? min(total, num_out) : total;
+  if (b == 0 && expert_offsets != nullptr) {
+    for (int e = tid; e < E; e += kTokPerBlock) expert_offsets[e] = min(s_off[e], kept);
+    if (tid == 0) expert_offsets[E] = kept;
+  }
+
+  const int w = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int t = b * kTokPerBlock + tid;
+  const int64_t W = 2 * (int64_t)E + 1;
+  int32_t *mrow = map + (int64_t)t * W;
+  int n = 0;
+  const int nchunks = (E + kMaskChunk - 1) / kMaskChunk;
+  for (int ch = nchunks - 1; ch >= 0; ch--) {
+    const int c0 = ch * kMaskChunk;
+    const int nc = min(kMaskChunk, E - c0);
+    __syncthreads();   // the previous chunk's readers are done
+    if (tid < nc) {
+      const int e = c0 + tid;
+      int pre = 0;
+      if (FUSED) {
+#pragma unroll 8
+        for (int b2 = 0; b2 < b; b2++) pre += counts[(int64_t)b2 * E + e];
+      } else {
+        pre = counts[(int64_t)b * E + e];
+      }
+      int run = s_off[e] + pre;
+#pragma unroll
+      for (int ww = 0; ww < kWavesPerBlock; ww++) {
+        const unsigned long long m = masks[((int64_t)b * kWavesPerBlock + ww) * E + e];
+        s_mask[ww][tid] = m;
+        s_base[ww][tid] = run;
+        run += __popcll(m);
+      }
+    }
+    __syncthreads();
+    if (t < T) {
+      for (int i = nc - 1; i >= 0; i--) {
+        const unsigned long long m = s_mask[w][i];
+        if ((m >> lane) & 1ull) {
+          const int row = s_base[w][i] + (int)__builtin_amdgcn_mbcnt_hi(
+                                             (unsigned)(m >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+          if (row < kept) {
+            mrow[n] = row;
+            mrow[E + n] = c0 + i;
+            n++;
+          }
+        }
+      }
+    }
+  }
+  if (t < T) mrow[2 * E] = n;
+}
+
 __global__ void fill_kernel(int32_t *__restrict__ p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -262,6 +409,43 @@ hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *
                        E, w.totals);
     hipLaunchKernelGGL(rowmap_write_kernel<false>, wgrid, dim3(kTokPerBlock), lds_write, s,
                        w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
+  }
+  return hipGetLastError();
+}
+
+size_t maskmap_workspace_bytes(int T, int E) { return rowmap_workspace_bytes(T, 1, E); }
+
+hipError_t launch_maskmap(const void *routing_map, int mask_bytes, int T, int E, int num_out,
+                          int32_t *map, int32_t *expert_offsets, void *ws, hipStream_t s) {
+  if (T == 0) {
+    if (expert_offsets == nullptr) return hipSuccess;
+    hipLaunchKernelGGL(fill_kernel, dim3((E + 1 + 255) / 256), dim3(256), 0, s, expert_offsets,
+                       E + 1, 0);
+    return hipGetLastError();
+  }
+  const int nb = (T + kTokPerBlock - 1) / kTokPerBlock;
+  const Workspace w = carve(ws, nb, E);
+  const size_t lds_count = (size_t)kWavesPerBlock * E * sizeof(int);
+  // Vector loads of 4 entries when rows allow them.
+  const uintptr_t a = reinterpret_cast<uintptr_t>(routing_map);
+  const bool vec = E % 4 == 0 && a % (4 * (uintptr_t)mask_bytes) == 0;
+#define MOE_MASK_COUNT(MB, V)                                                                 \
+  hipLaunchKernelGGL((maskmap_count_kernel<MB, V>), dim3(nb), dim3(kTokPerBlock), lds_count, s, \
+                     routing_map, T, E, w.masks, w.counts)
+  if (mask_bytes == 4) {
+    if (vec) MOE_MASK_COUNT(4, 4); else MOE_MASK_COUNT(4, 1);
+  } else {
+    if (vec) MOE_MASK_COUNT(1, 4); else MOE_MASK_COUNT(1, 1);
+  }
+#undef MOE_MASK_COUNT
+  if (nb <= kFusedMaxBlocks) {
+    hipLaunchKernelGGL(maskmap_write_kernel<true>, dim3(nb), dim3(kTokPerBlock), 0, s, w.masks,
+                       w.counts, w.totals, T, E, nb, num_out, map, expert_offsets);
+  } else {
+    hipLaunchKernelGGL(rowmap_colscan_kernel, dim3(E), dim3(kScanThreads), 0, s, w.counts, nb,
+                       E, w.totals);
+    hipLaunchKernelGGL(maskmap_write_kernel<false>, dim3(nb), dim3(kTokPerBlock), 0, s, w.masks,
+                       w.counts, w.totals, T, E, nb, num_out, map, expert_offsets);
   }
   return hipGetLastError();
 }
