@@ -68,6 +68,19 @@ def routed_bytes(T, H, E, k):
     }
 
 
+def mask_bytes(T, H, E, k):
+    """Algorithmic bytes of the mask-map ops on a routing with k experts per
+    token (bool mask; each slot reads two map entries and its [T, E] prob)."""
+    row = 2 * H
+    look = 8 * T * k + 4 * T
+    return {
+        "mask_row_map": T * E + 4 * T * (2 * k + 1) + 4 * (E + 1),
+        "mask_permute": T * row + T * k * row + look + 4 * T * k + 4 * T * k,
+        "mask_unpermute": T * k * row + T * row + look + 4 * T * k,
+        "mask_unpermute_bwd": T * row + 2 * T * k * row + look + 4 * T * k + 4 * T * E,
+    }
+
+
 def chunk_bytes(N, H, cap, eb=2):
     row = eb * H
     return {
@@ -227,6 +240,33 @@ def build_routed(m, w):
          (p(logits), eb, T, E, k, p(r_idx), p(r_probs), 4)),
         ("topk_softmax_bwd", T * k * 12 + T * E * 4, lib.moe_topk_softmax_bwd,
          (p(dprob), p(probs), 4, p(idx), T, E, k, p(d_logits), 4, None)),
+    ]
+    # TransformerEngine mask-map form on the same routing.
+    mask = torch.zeros((T, E), dtype=torch.bool, device=dev)
+    mask.scatter_(1, idx.long(), True)
+    probs_te = torch.zeros((T, E), dtype=torch.float32, device=dev)
+    probs_te.scatter_(1, idx.long(), probs)
+    mmap = torch.empty((T, 2 * E + 1), dtype=torch.int32, device=dev)
+    moff = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    mws_n = m.moe_make_mask_row_id_map_workspace_bytes(T, E)
+    mws = torch.empty(mws_n, dtype=torch.uint8, device=dev)
+    m.moe_make_mask_row_id_map(mask, row_id_map=mmap, expert_offsets=moff, workspace=mws)
+    mP = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+    mpp = torch.empty(n, dtype=torch.float32, device=dev)
+    my = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    mdP = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+    mdp = torch.empty((T, E), dtype=torch.float32, device=dev)
+    step.keep += [mask, probs_te, mmap, moff, mws, mP, mpp, my, mdP, mdp]
+    mb = mask_bytes(T, H, E, k)
+    step.extra += [
+        ("mask_row_map", mb["mask_row_map"], lib.moe_make_mask_row_id_map,
+         (p(mask), 1, T, E, -1, p(mmap), p(moff), p(mws), mws_n)),
+        ("mask_permute", mb["mask_permute"], lib.moe_permute_mask,
+         (p(x), p(probs_te), p(mmap), T, H, E, n, p(mP), p(mpp), None)),
+        ("mask_unpermute", mb["mask_unpermute"], lib.moe_unpermute_mask,
+         (p(mP), p(probs_te), None, p(mmap), T, H, E, n, p(my), None, None)),
+        ("mask_unpermute_bwd", mb["mask_unpermute_bwd"], lib.moe_unpermute_mask_bwd,
+         (p(dy), p(mP), p(probs_te), p(mmap), T, H, E, n, p(mdP), p(mdp), None)),
     ]
     return step, routed_bytes(T, H, E, k)
 

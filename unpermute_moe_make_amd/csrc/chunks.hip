@@ -23,9 +23,24 @@
 namespace moe {
 namespace {
 
+// Build-time tuning: units in flight per lane, and the streaming policy of
+// calls larger than kStreamBytes (bit 0: non-temporal loads, bit 1:
+// non-temporal stores).
+#ifndef MOE_PAD_ILP
+#define MOE_PAD_ILP 2
+#endif
+#ifndef MOE_RESTORE_ILP
+#define MOE_RESTORE_ILP 4
+#endif
+#ifndef MOE_PAD_STREAM
+#define MOE_PAD_STREAM 2
+#endif
+#ifndef MOE_RESTORE_STREAM
+#define MOE_RESTORE_STREAM 1
+#endif
 constexpr int kCopyThreads = 256;
-constexpr int kCopyIlp = 4;
-constexpr int kUnitsPerIter = kCopyThreads * kCopyIlp;
+constexpr int kPadIlp = MOE_PAD_ILP;
+constexpr int kRestoreIlp = MOE_RESTORE_ILP;
 constexpr int kMapRows = 256;         // row_map entries per map workgroup (one per lane)
 
 // ----------------------------------------------------------- chunk tables --
@@ -222,18 +237,18 @@ __global__ __launch_bounds__(kCopyThreads) void chunk_map_kernel(
 }
 
 // Pad copy driven by the row map: out[d] = in[row_map[d]] or zeros.
-// NTS: stream the (dense, sequential) destination rows.
-template <typename U, bool NTS>
+// NTL / NTS: stream the source / the (dense, sequential) destination rows.
+template <typename U, bool NTL, bool NTS>
 __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
     const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, int64_t W,
     int n_cap, const int32_t *__restrict__ row_map, int out_cap, U *__restrict__ out,
     uint8_t *__restrict__ out_probs, int32_t *__restrict__ dev_status) {
   const int64_t total = (int64_t)out_cap * W;
-  const int64_t base = (int64_t)blockIdx.x * kUnitsPerIter + threadIdx.x;
-  U v[kCopyIlp];
+  const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kPadIlp + threadIdx.x;
+  U v[kPadIlp];
   int bad = 0;
 #pragma unroll
-  for (int i = 0; i < kCopyIlp; i++) {
+  for (int i = 0; i < kPadIlp; i++) {
     const int64_t u = base + (int64_t)i * kCopyThreads;
     v[i] = zero_unit<U>();
     if (u < total) {
@@ -244,12 +259,12 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
         bad |= MOE_DEV_BAD_ROW;
         s = -1;
       }
-      if (s >= 0) v[i] = ld_row<false>(in + s * W + c);
+      if (s >= 0) v[i] = ld_row<NTL>(in + s * W + c);
       if (c == 0 && out_probs != nullptr) copy_prob(probs, s, out_probs, d, prob_bytes);
     }
   }
 #pragma unroll
-  for (int i = 0; i < kCopyIlp; i++) {
+  for (int i = 0; i < kPadIlp; i++) {
     const int64_t u = base + (int64_t)i * kCopyThreads;
     if (u < total) st_row<NTS>(v[i], out + u);
   }
@@ -270,8 +285,9 @@ __device__ __forceinline__ int64_t wave_total(const int32_t *__restrict__ sizes,
 
 // Flat index over [0, max(out_cap, n_cap)) x W: unit (i, c) scatters padded
 // row i (if mapped) and zero-fills restored row i (if past the token total).
-// NTL: stream the (dense, sequential) padded source rows.
-template <typename U, bool NTL>
+// NTL / NTS: stream the (dense, sequential) padded source rows / the
+// restored rows.
+template <typename U, bool NTL, bool NTS>
 __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
     const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, int64_t W,
     const int32_t *__restrict__ row_map, const int32_t *__restrict__ split_sizes, int C,
@@ -279,12 +295,12 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
     int32_t *__restrict__ dev_status) {
   const int64_t rows = max(out_cap, n_cap);
   const int64_t total = rows * W;
-  const int64_t base = (int64_t)blockIdx.x * kUnitsPerIter + threadIdx.x;
-  U v[kCopyIlp];
-  int32_t dst[kCopyIlp];
+  const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kRestoreIlp + threadIdx.x;
+  U v[kRestoreIlp];
+  int32_t dst[kRestoreIlp];
   int bad = 0;
 #pragma unroll
-  for (int i = 0; i < kCopyIlp; i++) {
+  for (int i = 0; i < kRestoreIlp; i++) {
     const int64_t u = base + (int64_t)i * kCopyThreads;
     dst[i] = -1;
     if (u < total) {
@@ -304,14 +320,14 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
   const int64_t n_act = wave_total(split_sizes, C);
   if (n_act > n_cap) bad |= MOE_DEV_OVERFLOW;
 #pragma unroll
-  for (int i = 0; i < kCopyIlp; i++) {
+  for (int i = 0; i < kRestoreIlp; i++) {
     const int64_t u = base + (int64_t)i * kCopyThreads;
     if (u < total) {
       const int64_t d = u / W;
       const int64_t c = u - d * W;
-      if (dst[i] >= 0) st_row<false>(v[i], out + (int64_t)dst[i] * W + c);
+      if (dst[i] >= 0) st_row<NTS>(v[i], out + (int64_t)dst[i] * W + c);
       if (d >= n_act && d < n_cap) {
-        st_row<false>(zero_unit<U>(), out + u);
+        st_row<NTS>(zero_unit<U>(), out + u);
         if (c == 0 && out_probs != nullptr) copy_prob(probs, -1, out_probs, d, prob_bytes);
       }
     }
@@ -319,8 +335,9 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
   report(dev_status, bad);
 }
 
-inline unsigned copy_blocks(int64_t units) {
-  return (unsigned)((units + kUnitsPerIter - 1) / kUnitsPerIter);
+inline unsigned copy_blocks(int64_t units, int ilp) {
+  const int64_t per = (int64_t)kCopyThreads * ilp;
+  return (unsigned)((units + per - 1) / per);
 }
 
 }  // namespace
@@ -341,28 +358,30 @@ hipError_t launch_pad_copy(const void *in, const void *probs, int prob_bytes, in
                            void *out, void *out_probs, int32_t *dev_status, hipStream_t s) {
   const int64_t units = (int64_t)out_cap * row_units;
   if (units == 0) return hipSuccess;
-  const dim3 grid(copy_blocks(units)), block(kCopyThreads);
+  const dim3 grid(copy_blocks(units, kPadIlp)), block(kCopyThreads);
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
   const bool stream = units * unit_bytes * 2 > kStreamBytes;
   switch (unit_bytes) {
     case 16:
       if (stream)
-        hipLaunchKernelGGL((pad_copy_kernel<v4u, true>), grid, block, 0, s,
-                           static_cast<const v4u *>(in), pp, prob_bytes, row_units, n_cap,
-                           row_map, out_cap, static_cast<v4u *>(out), op, dev_status);
+        hipLaunchKernelGGL((pad_copy_kernel<v4u, (MOE_PAD_STREAM & 1) != 0,
+                                            (MOE_PAD_STREAM & 2) != 0>),
+                           grid, block, 0, s, static_cast<const v4u *>(in), pp, prob_bytes,
+                           row_units, n_cap, row_map, out_cap, static_cast<v4u *>(out), op,
+                           dev_status);
       else
-        hipLaunchKernelGGL((pad_copy_kernel<v4u, false>), grid, block, 0, s,
+        hipLaunchKernelGGL((pad_copy_kernel<v4u, false, false>), grid, block, 0, s,
                            static_cast<const v4u *>(in), pp, prob_bytes, row_units, n_cap,
                            row_map, out_cap, static_cast<v4u *>(out), op, dev_status);
       break;
     case 4:
-      hipLaunchKernelGGL((pad_copy_kernel<uint32_t, false>), grid, block, 0, s,
+      hipLaunchKernelGGL((pad_copy_kernel<uint32_t, false, false>), grid, block, 0, s,
                          static_cast<const uint32_t *>(in), pp, prob_bytes, row_units, n_cap,
                          row_map, out_cap, static_cast<uint32_t *>(out), op, dev_status);
       break;
     default:
-      hipLaunchKernelGGL((pad_copy_kernel<uint16_t, false>), grid, block, 0, s,
+      hipLaunchKernelGGL((pad_copy_kernel<uint16_t, false, false>), grid, block, 0, s,
                          static_cast<const uint16_t *>(in), pp, prob_bytes, row_units, n_cap,
                          row_map, out_cap, static_cast<uint16_t *>(out), op, dev_status);
       break;
@@ -376,31 +395,32 @@ hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes
                                void *out, void *out_probs, int32_t *dev_status, hipStream_t s) {
   const int64_t units = (int64_t)(out_cap > n_cap ? out_cap : n_cap) * row_units;
   if (units == 0) return hipSuccess;
-  const dim3 grid(copy_blocks(units)), block(kCopyThreads);
+  const dim3 grid(copy_blocks(units, kRestoreIlp)), block(kCopyThreads);
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
   const bool stream = ((int64_t)out_cap + n_cap) * row_units * unit_bytes > kStreamBytes;
   switch (unit_bytes) {
     case 16:
       if (stream)
-        hipLaunchKernelGGL((restore_copy_kernel<v4u, true>), grid, block, 0, s,
-                           static_cast<const v4u *>(in), pp, prob_bytes, row_units, row_map,
-                           split_sizes, C, out_cap, n_cap, static_cast<v4u *>(out), op,
-                           dev_status);
+        hipLaunchKernelGGL((restore_copy_kernel<v4u, (MOE_RESTORE_STREAM & 1) != 0,
+                                                (MOE_RESTORE_STREAM & 2) != 0>),
+                           grid, block, 0, s, static_cast<const v4u *>(in), pp, prob_bytes,
+                           row_units, row_map, split_sizes, C, out_cap, n_cap,
+                           static_cast<v4u *>(out), op, dev_status);
       else
-        hipLaunchKernelGGL((restore_copy_kernel<v4u, false>), grid, block, 0, s,
+        hipLaunchKernelGGL((restore_copy_kernel<v4u, false, false>), grid, block, 0, s,
                            static_cast<const v4u *>(in), pp, prob_bytes, row_units, row_map,
                            split_sizes, C, out_cap, n_cap, static_cast<v4u *>(out), op,
                            dev_status);
       break;
     case 4:
-      hipLaunchKernelGGL((restore_copy_kernel<uint32_t, false>), grid, block, 0, s,
+      hipLaunchKernelGGL((restore_copy_kernel<uint32_t, false, false>), grid, block, 0, s,
                          static_cast<const uint32_t *>(in), pp, prob_bytes, row_units, row_map,
                          split_sizes, C, out_cap, n_cap, static_cast<uint32_t *>(out), op,
                          dev_status);
       break;
     default:
-      hipLaunchKernelGGL((restore_copy_kernel<uint16_t, false>), grid, block, 0, s,
+      hipLaunchKernelGGL((restore_copy_kernel<uint16_t, false, false>), grid, block, 0, s,
                          static_cast<const uint16_t *>(in), pp, prob_bytes, row_units, row_map,
                          split_sizes, C, out_cap, n_cap, static_cast<uint16_t *>(out), op,
                          dev_status);

@@ -27,9 +27,12 @@ template <bool NT, typename U> __device__ __forceinline__ void st_row(U v, U *p)
 // A call that moves more bytes than the MI355X Infinity Cache (256 MiB)
 // holds streams its rows; a smaller call keeps plain accesses so the next
 // call on the same buffers can still hit the cache.  Which accesses of a
-// kernel stream was measured per kernel (non-temporal stores help dense,
-// sequential row writes and hurt scattered ones).
-constexpr int64_t kStreamBytes = 256ll << 20;
+// kernel stream (loads, stores or both) was measured per kernel and is set
+// beside each kernel's launcher.
+#ifndef MOE_STREAM_MIB
+#define MOE_STREAM_MIB 256
+#endif
+constexpr int64_t kStreamBytes = (int64_t)MOE_STREAM_MIB << 20;
 
 // bf16 -> fp32 is exact: the bf16 pattern is the top half of the binary32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

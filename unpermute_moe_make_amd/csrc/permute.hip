@@ -26,6 +26,17 @@ namespace moe {
 namespace {
 
 constexpr int kMaxTopk = MOE_MAX_TOPK;
+// Streaming policy of calls larger than kStreamBytes, per kernel (bit 0:
+// non-temporal loads, bit 1: non-temporal stores); build-time tuning.
+#ifndef MOE_PERMUTE_STREAM
+#define MOE_PERMUTE_STREAM 2
+#endif
+#ifndef MOE_COMBINE_STREAM
+#define MOE_COMBINE_STREAM 3
+#endif
+#ifndef MOE_COMBINE_BWD_STREAM
+#define MOE_COMBINE_BWD_STREAM 3
+#endif
 
 // Resolve the token's slots into LDS.  Returns status bits of this lane.
 __device__ __forceinline__ int resolve_slots(const int32_t *__restrict__ topk_idx,
@@ -53,7 +64,7 @@ __device__ __forceinline__ int resolve_slots(const int32_t *__restrict__ topk_id
 
 // ---------------------------------------------------------------- permute --
 
-template <typename U, int VPT>
+template <typename U, int VPT, int NTM>
 __global__ __launch_bounds__(kRowThreads) void permute_kernel(
     const U *__restrict__ x, const float *__restrict__ probs,
     const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
@@ -69,7 +80,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = c0 + (int64_t)i * blockDim.x;
-    if (c < V) v[i] = ld_row<false>(xr + c);
+    if (c < V) v[i] = ld_row<(NTM & 1) != 0>(xr + c);
   }
   const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
   if (blockIdx.y == 0 && threadIdx.x < k) {
@@ -86,7 +97,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
 #pragma unroll
     for (int i = 0; i < VPT; i++) {
       const int64_t c = c0 + (int64_t)i * blockDim.x;
-      if (c < V) st_row<false>(v[i], orow + c);
+      if (c < V) st_row<(NTM & 2) != 0>(v[i], orow + c);
     }
   }
 }
@@ -96,7 +107,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
 // out[t] = bf16(fma chain over slots of p_j * in[r_j]); probs == NULL -> 1.
 // KB = slots loaded per batch (all of them when k <= 8).  Optionally gathers
 // gather_dst[t][j] = gather_src[r_j] (permute backward of the probs).
-template <int EPV, int VPT, int KB, bool NT>
+template <int EPV, int VPT, int KB, int NTM>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     const typename Bf16Unit<EPV>::T *__restrict__ in, const float *__restrict__ probs,
     const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
@@ -139,7 +150,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 #pragma unroll
       for (int i = 0; i < VPT; i++) {
         const int64_t c = c0 + (int64_t)i * blockDim.x;
-        vals[jj][i] = (r >= 0 && c < V) ? ld_row<NT>(in + r * V + c) : Unit::zero();
+        vals[jj][i] = (r >= 0 && c < V) ? ld_row<(NTM & 1) != 0>(in + r * V + c) : Unit::zero();
       }
     }
     // Then the fused multiply-adds, strictly in slot order.
@@ -163,7 +174,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = c0 + (int64_t)i * blockDim.x;
-    if (c < V) st_row<NT>(Unit::pack(acc[i]), orow + c);
+    if (c < V) st_row<(NTM & 2) != 0>(Unit::pack(acc[i]), orow + c);
   }
 }
 
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_ep_kernel(
 // A workgroup walks its row slice in passes of blockDim*VPT units.  When
 // d_probs is written the grid must not split rows (gridDim.y == 1), so the
 // workgroup sees the whole row and reduces each slot's dot product itself.
-template <int EPV, int VPT, int KB, bool NT>
+template <int EPV, int VPT, int KB, int NTM>
 __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
     const typename Bf16Unit<EPV>::T *__restrict__ d_out,
     const typename Bf16Unit<EPV>::T *__restrict__ fwd_in, const float *__restrict__ probs,
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = cfirst + (int64_t)i * blockDim.x;
-    graw[i] = c < V ? ld_row<NT>(grow + c) : Unit::zero();
+    graw[i] = c < V ? ld_row<(NTM & 1) != 0>(grow + c) : Unit::zero();
   }
   const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
   if (threadIdx.x < k) {
@@ -336,7 +347,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
 #pragma unroll
         for (int i = 0; i < VPT; i++) {
           const int64_t c = cb + (int64_t)i * blockDim.x;
-          graw[i] = c < V ? ld_row<NT>(grow + c) : Unit::zero();
+          graw[i] = c < V ? ld_row<(NTM & 1) != 0>(grow + c) : Unit::zero();
         }
       }
       U fin[KB][VPT];
@@ -348,7 +359,8 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
 #pragma unroll
           for (int i = 0; i < VPT; i++) {
             const int64_t c = cb + (int64_t)i * blockDim.x;
-            fin[jj][i] = (r >= 0 && c < V) ? ld_row<NT>(fwd_in + r * V + c) : Unit::zero();
+            fin[jj][i] = (r >= 0 && c < V) ? ld_row<(NTM & 1) != 0>(fwd_in + r * V + c)
+                                           : Unit::zero();
           }
         }
       }
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
           float prod[EPV];
 #pragma unroll
           for (int e = 0; e < EPV; e++) prod[e] = g[i][e] * p;  // one fp32 rounding
-          if (r >= 0 && c < V) st_row<NT>(Unit::pack(prod), d_in + r * V + c);
+          if (r >= 0 && c < V) st_row<(NTM & 2) != 0>(Unit::pack(prod), d_in + r * V + c);
           if (want_dot) {
             float f[EPV];
             Unit::unpack(fin[jj][i], f);
@@ -395,7 +407,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
   }
 }
 
-template <typename U>
+template <typename U, int NTM>
 hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *topk_idx,
                             const int32_t *row_id_map, int T, int64_t V, int k, int E,
                             int n_rows, void *out, float *out_probs, int32_t *dev_status,
@@ -406,22 +418,22 @@ hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *to
   U *op = static_cast<U *>(out);
   switch (sh.vpt) {
     case 1:
-      hipLaunchKernelGGL((permute_kernel<U, 1>), grid, block, 0, s, xp, probs, topk_idx,
+      hipLaunchKernelGGL((permute_kernel<U, 1, NTM>), grid, block, 0, s, xp, probs, topk_idx,
                          row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
       break;
     case 2:
-      hipLaunchKernelGGL((permute_kernel<U, 2>), grid, block, 0, s, xp, probs, topk_idx,
+      hipLaunchKernelGGL((permute_kernel<U, 2, NTM>), grid, block, 0, s, xp, probs, topk_idx,
                          row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
       break;
     default:
-      hipLaunchKernelGGL((permute_kernel<U, 4>), grid, block, 0, s, xp, probs, topk_idx,
+      hipLaunchKernelGGL((permute_kernel<U, 4, NTM>), grid, block, 0, s, xp, probs, topk_idx,
                          row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
       break;
   }
   return hipGetLastError();
 }
 
-template <int EPV, int VPT, bool NT>
+template <int EPV, int VPT, int NTM>
 void combine_k(const RowShape &sh, int T, const void *in, const float *probs,
                const int32_t *topk_idx, const int32_t *row_id_map, int64_t V, int k, int E,
                int n_rows, void *out, const float *gsrc, float *gdst, int32_t *st,
@@ -431,7 +443,7 @@ void combine_k(const RowShape &sh, int T, const void *in, const float *probs,
   const U *ip = static_cast<const U *>(in);
   U *op = static_cast<U *>(out);
 #define MOE_COMBINE(KBV)                                                                     \
-  hipLaunchKernelGGL((combine_kernel<EPV, VPT, KBV, NT>), grid, block, 0, s, ip, probs, topk_idx, \
+  hipLaunchKernelGGL((combine_kernel<EPV, VPT, KBV, NTM>), grid, block, 0, s, ip, probs, topk_idx, \
                      row_id_map, T, V, k, E, n_rows, op, gsrc, gdst, st)
   switch (k) {
     case 1: MOE_COMBINE(1); break;
@@ -446,7 +458,7 @@ void combine_k(const RowShape &sh, int T, const void *in, const float *probs,
 #undef MOE_COMBINE
 }
 
-template <int EPV, int VPT, bool NT>
+template <int EPV, int VPT, int NTM>
 void combine_bwd_k(const RowShape &sh, int T, const void *d_out, const void *fwd_in,
                    const float *probs, const int32_t *topk_idx, const int32_t *row_id_map,
                    int64_t V, int k, int E, int n_rows, void *d_in, float *d_probs, int32_t *st,
@@ -457,7 +469,7 @@ void combine_bwd_k(const RowShape &sh, int T, const void *d_out, const void *fwd
   const U *fp = static_cast<const U *>(fwd_in);
   U *dp = static_cast<U *>(d_in);
 #define MOE_COMBINE_BWD(KBV)                                                                  \
-  hipLaunchKernelGGL((combine_bwd_kernel<EPV, VPT, KBV, NT>), grid, block, 0, s, gp, fp, probs,   \
+  hipLaunchKernelGGL((combine_bwd_kernel<EPV, VPT, KBV, NTM>), grid, block, 0, s, gp, fp, probs,  \
                      topk_idx, row_id_map, T, V, k, E, n_rows, dp, d_probs, st)
   switch (k) {
     case 1: MOE_COMBINE_BWD(1); break;
@@ -472,19 +484,19 @@ void combine_bwd_k(const RowShape &sh, int T, const void *d_out, const void *fwd
 #undef MOE_COMBINE_BWD
 }
 
-template <int EPV, bool NT>
+template <int EPV, int NTM>
 void combine_dispatch(const void *in, const float *probs, const int32_t *topk_idx,
                       const int32_t *row_id_map, int T, int64_t V, int k, int E, int n_rows,
                       void *out, const float *gsrc, float *gdst, int32_t *st, hipStream_t s) {
   const RowShape sh = row_shape(V, true);
   switch (sh.vpt) {
-    case 1: combine_k<EPV, 1, NT>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
-    case 2: combine_k<EPV, 2, NT>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
-    default: combine_k<EPV, 4, NT>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+    case 1: combine_k<EPV, 1, NTM>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+    case 2: combine_k<EPV, 2, NTM>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
+    default: combine_k<EPV, 4, NTM>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
   }
 }
 
-template <int EPV, bool NT>
+template <int EPV, int NTM>
 void combine_bwd_dispatch(const void *d_out, const void *fwd_in, const float *probs,
                           const int32_t *topk_idx, const int32_t *row_id_map, int T, int64_t V,
                           int k, int E, int n_rows, void *d_in, float *d_probs, int32_t *st,
@@ -493,9 +505,9 @@ void combine_bwd_dispatch(const void *d_out, const void *fwd_in, const float *pr
   // longer than one pass are then walked in several passes.
   const RowShape sh = row_shape(V, d_probs == nullptr);
   switch (sh.vpt) {
-    case 1: combine_bwd_k<EPV, 1, NT>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
-    case 2: combine_bwd_k<EPV, 2, NT>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
-    default: combine_bwd_k<EPV, 4, NT>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+    case 1: combine_bwd_k<EPV, 1, NTM>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+    case 2: combine_bwd_k<EPV, 2, NTM>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
+    default: combine_bwd_k<EPV, 4, NTM>(sh, T, d_out, fwd_in, probs, topk_idx, row_id_map, V, k, E, n_rows, d_in, d_probs, st, s); break;
   }
 }
 
@@ -534,11 +546,16 @@ hipError_t launch_permute(const void *x, const float *probs, const int32_t *topk
                           const int32_t *row_id_map, int T, int H, int k, int E, int n_rows,
                           void *out, float *out_probs, int32_t *dev_status, bool vec,
                           hipStream_t s) {
+  const int64_t bytes = 2ll * H * ((int64_t)n_rows + T);
+  if (vec && bytes > kStreamBytes)
+    return permute_dispatch<v4u, MOE_PERMUTE_STREAM>(x, probs, topk_idx, row_id_map, T, H / 8,
+                                                     k, E, n_rows, out, out_probs, dev_status,
+                                                     s);
   if (vec)
-    return permute_dispatch<v4u>(x, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
-                                   out_probs, dev_status, s);
-  return permute_dispatch<uint16_t>(x, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out,
-                                    out_probs, dev_status, s);
+    return permute_dispatch<v4u, 0>(x, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows,
+                                    out, out_probs, dev_status, s);
+  return permute_dispatch<uint16_t, 0>(x, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out,
+                                       out_probs, dev_status, s);
 }
 
 hipError_t launch_combine(const void *in, const float *probs, const int32_t *topk_idx,
@@ -548,13 +565,13 @@ hipError_t launch_combine(const void *in, const float *probs, const int32_t *top
   // Gathered rows in, dense rows out: both stream when the call is large.
   const int64_t bytes = 2ll * H * ((int64_t)n_rows + T);
   if (vec && bytes > kStreamBytes)
-    combine_dispatch<8, true>(in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
+    combine_dispatch<8, MOE_COMBINE_STREAM>(in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
                               gather_src, gather_dst, dev_status, s);
   else if (vec)
-    combine_dispatch<8, false>(in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
+    combine_dispatch<8, 0>(in, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows, out,
                                gather_src, gather_dst, dev_status, s);
   else
-    combine_dispatch<1, false>(in, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out,
+    combine_dispatch<1, 0>(in, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out,
                                gather_src, gather_dst, dev_status, s);
   return hipGetLastError();
 }
@@ -565,13 +582,13 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
                               int32_t *dev_status, bool vec, hipStream_t s) {
   const int64_t bytes = 2ll * H * ((int64_t)n_rows * (d_probs ? 2 : 1) + T);
   if (vec && bytes > kStreamBytes)
-    combine_bwd_dispatch<8, true>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
+    combine_bwd_dispatch<8, MOE_COMBINE_BWD_STREAM>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
                                   n_rows, d_in, d_probs, dev_status, s);
   else if (vec)
-    combine_bwd_dispatch<8, false>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
+    combine_bwd_dispatch<8, 0>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
                                    n_rows, d_in, d_probs, dev_status, s);
   else
-    combine_bwd_dispatch<1, false>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H, k, E,
+    combine_bwd_dispatch<1, 0>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H, k, E,
                                    n_rows, d_in, d_probs, dev_status, s);
   return hipGetLastError();
 }
