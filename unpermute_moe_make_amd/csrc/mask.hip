@@ -17,6 +17,12 @@
 namespace moe {
 namespace {
 
+// Streaming policy of the permute on calls larger than kStreamBytes (bit 0:
+// non-temporal loads, bit 1: non-temporal stores), as for the top-k permute.
+#ifndef MOE_MASK_PERMUTE_STREAM
+#define MOE_MASK_PERMUTE_STREAM 2
+#endif
+
 constexpr int kSlotChunk = 64;   // slots resolved into LDS at a time
 constexpr int kBatch = 8;        // rows loaded together in the combine
 
@@ -49,7 +55,7 @@ __device__ __forceinline__ int64_t mask_slot(const int32_t *__restrict__ mrow, i
 
 // out[row] = x[t] for each slot; with probs, out_probs[row] = probs[t][e]
 // and a zero prob writes a zero row.
-template <typename U, int VPT>
+template <typename U, int VPT, int NTM>
 __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
     const U *__restrict__ x, const float *__restrict__ probs, const int32_t *__restrict__ map,
     int T, int64_t V, int E, int n_rows, U *__restrict__ out, float *__restrict__ out_probs,
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = c0 + (int64_t)i * blockDim.x;
-    if (c < V) v[i] = ld_row<false>(xr + c);
+    if (c < V) v[i] = ld_row<(NTM & 1) != 0>(xr + c);
   }
   U zero;
   zero = U{};
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
 #pragma unroll
       for (int i = 0; i < VPT; i++) {
         const int64_t c = c0 + (int64_t)i * blockDim.x;
-        if (c < V) st_row<false>(z ? zero : v[i], orow + c);
+        if (c < V) st_row<(NTM & 2) != 0>(z ? zero : v[i], orow + c);
       }
     }
     __syncthreads();
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(kRowThreads) void mask_unpermute_bwd_kernel(
   if (blockIdx.y == 0) report(dev_status, bad);
 }
 
-template <typename U>
+template <typename U, int NTM>
 void mask_permute_dispatch(const void *x, const float *probs, const int32_t *map, int T,
                            int64_t V, int E, int n_rows, void *out, float *out_probs,
                            int32_t *st, hipStream_t s) {
@@ -309,8 +315,8 @@ void mask_permute_dispatch(const void *x, const float *probs, const int32_t *map
   const U *xp = static_cast<const U *>(x);
   U *op = static_cast<U *>(out);
 #define MOE_MASK_PERMUTE(VPTV)                                                              \
-  hipLaunchKernelGGL((mask_permute_kernel<U, VPTV>), grid, block, 0, s, xp, probs, map, T, V, \
-                     E, n_rows, op, out_probs, st)
+  hipLaunchKernelGGL((mask_permute_kernel<U, VPTV, NTM>), grid, block, 0, s, xp, probs, map, T, \
+                     V, E, n_rows, op, out_probs, st)
   switch (sh.vpt) {
     case 1: MOE_MASK_PERMUTE(1); break;
     case 2: MOE_MASK_PERMUTE(2); break;
@@ -373,12 +379,16 @@ void mask_unpermute_bwd_dispatch(const void *d_out, const void *fwd_in, const fl
 hipError_t launch_mask_permute(const void *x, const float *probs, const int32_t *map, int T,
                                int H, int E, int n_rows, void *out, float *out_probs,
                                int32_t *dev_status, bool vec, hipStream_t s) {
-  if (vec)
-    mask_permute_dispatch<v4u>(x, probs, map, T, H / 8, E, n_rows, out, out_probs, dev_status,
-                               s);
+  const bool stream = 2ll * H * ((int64_t)n_rows + T) > kStreamBytes;
+  if (vec && stream)
+    mask_permute_dispatch<v4u, MOE_MASK_PERMUTE_STREAM>(x, probs, map, T, H / 8, E, n_rows, out,
+                                                        out_probs, dev_status, s);
+  else if (vec)
+    mask_permute_dispatch<v4u, 0>(x, probs, map, T, H / 8, E, n_rows, out, out_probs,
+                                  dev_status, s);
   else
-    mask_permute_dispatch<uint16_t>(x, probs, map, T, H, E, n_rows, out, out_probs, dev_status,
-                                    s);
+    mask_permute_dispatch<uint16_t, 0>(x, probs, map, T, H, E, n_rows, out, out_probs,
+                                       dev_status, s);
   return hipGetLastError();
 }
 
