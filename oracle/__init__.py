@@ -75,6 +75,8 @@ def _load():
             "oracle_topk_softmax": [P, I, I, I, I, P, P, I],
             "oracle_topk_softmax_bwd": [P, P, I, P, I, I, I, P, I],
             "oracle_mask_row_id_map": [P, I, I, I, I, P, P],
+            "oracle_permute_scaled": [P, L, P, L, P, P, P, I, I, I, L, P, P, P],
+            "oracle_mask_permute_scaled": [P, L, P, L, P, P, I, I, I, P, P, P],
             "oracle_mask_permute": [P, P, P, I, I, I, I, P, P],
             "oracle_mask_unpermute": [P, P, P, P, I, I, I, I, P, P],
             "oracle_mask_unpermute_bwd": [P, P, P, P, I, I, I, I, P, P],
@@ -326,6 +328,55 @@ def mask_unpermute_bwd(d_out, fwd_in, merging_probs, row_map, d_in=None):
     _check(_load().oracle_mask_unpermute_bwd(_p(d_out), _p(fwd_in), _p(mp), _p(rm), T, H, E,
                                              n_rows, _p(d_in), _p(dmp)), "mask_unpermute_bwd")
     return d_in, dmp
+
+
+# ---- quantized rows ----------------------------------------------------------
+
+def _byte_rows(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint8).reshape(a.shape[0], -1)
+
+
+def permute_scaled(x, scale, probs, topk_idx, row_map, n_rows=None):
+    """x: [T][...] rows of any dtype (copied as bytes); scale: [T][...] or None.
+    Returns (out bytes [n_rows][row_bytes], out_scale bytes or None, out_probs)."""
+    xb = _byte_rows(x)
+    T, rb = xb.shape
+    sb = None if scale is None else _byte_rows(scale)
+    srb = 0 if sb is None else sb.shape[1]
+    idx = _arr(topk_idx, np.int32)
+    rm = _arr(row_map, np.int32)
+    probs = _arr(probs, np.float32)
+    k = idx.shape[1]
+    E = rm.shape[0]
+    n = T * k if n_rows is None else n_rows
+    out = np.zeros((n, rb), np.uint8)
+    out_s = None if sb is None else np.zeros((n, srb), np.uint8)
+    out_p = None if probs is None else np.zeros(n, np.float32)
+    _check(_load().oracle_permute_scaled(_p(xb), rb, _p(sb), srb, _p(probs), _p(idx), _p(rm),
+                                         T, k, E, n, _p(out), _p(out_s), _p(out_p)),
+           "permute_scaled")
+    return out, out_s, out_p
+
+
+def mask_permute_scaled(x, scale, probs, row_map, n_rows, out=None, out_scale=None):
+    """Mask-map form of permute_scaled; rows no map entry names keep `out` /
+    `out_scale` (zeros by default)."""
+    xb = _byte_rows(x)
+    T, rb = xb.shape
+    sb = None if scale is None else _byte_rows(scale)
+    srb = 0 if sb is None else sb.shape[1]
+    rm = _arr(row_map, np.int32)
+    probs = _arr(probs, np.float32)
+    E = (rm.shape[1] - 1) // 2
+    out = np.zeros((n_rows, rb), np.uint8) if out is None else np.array(out, np.uint8)
+    out_s = None if sb is None else (np.zeros((n_rows, srb), np.uint8) if out_scale is None
+                                     else np.array(out_scale, np.uint8))
+    out_p = None if probs is None else np.zeros(n_rows, np.float32)
+    _check(_load().oracle_mask_permute_scaled(_p(xb), rb, _p(sb), srb, _p(probs), _p(rm), T, E,
+                                              n_rows, _p(out), _p(out_s), _p(out_p)),
+           "mask_permute_scaled")
+    return out, out_s, out_p
 
 
 # ---- (3) chunk sort-and-pad / unpad-and-restore ------------------------------

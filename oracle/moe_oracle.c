@@ -31,6 +31,8 @@
  *                              from a [T][E] routing mask, with dropping.
  *   oracle_mask_permute / oracle_mask_unpermute(_bwd)
  *                           -- the TE-order copies and combine on that map.
+ *   oracle_permute_scaled / oracle_mask_permute_scaled
+ *                           -- quantized (e.g. FP8) rows with their scale rows.
  *   oracle_chunk_map        -- padded destination -> source row map.
  *   oracle_sort_chunks_and_pad / oracle_unpad_and_restore_chunks
  *                           -- the two copies driven by that map.
@@ -732,6 +734,79 @@ int oracle_mask_unpermute_bwd(const uint16_t *d_out, const uint16_t *fwd_in,
                 dot += (double)bf16_to_f32(fwd_in[(int64_t)row * H + h]) * (double)g;
             }
             if (d_merging_probs) d_merging_probs[(int64_t)t * E + e] = (float)dot;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- quantized rows: data rows of any element size, scale rows alongside -- */
+
+/*
+ * d9d permute_with_probs.py, _permute_kernel with PERMUTE_SCALE and
+ * permute_with_mask_map (scale, scale_hidden_dim): next to each token's data
+ * row, the token's scale row is stored to the same destination index of a
+ * permuted scale tensor.  Data rows are row_bytes bytes (an FP8 row of H
+ * elements is H bytes) and are copied bitwise, so the FP8 encoding does not
+ * enter; scale rows are scale_row_bytes bytes (0: no scales).
+ * The top-k form routes by topk_idx / row_id_map[E][T] as oracle_permute;
+ * the mask-map form by the per-token map, and with probs ([T][E] fp32) a zero
+ * prob writes a zero data row while the scale row is still copied.  Rows no
+ * route names are left as they were.
+ */
+static void copy_bytes(uint8_t *dst, const uint8_t *src, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) dst[i] = src[i];
+}
+
+int oracle_permute_scaled(const uint8_t *x, int64_t row_bytes, const uint8_t *scale,
+                          int64_t scale_row_bytes, const float *probs, const int32_t *topk_idx,
+                          const int32_t *row_id_map, int T, int k, int E, int64_t n_rows,
+                          uint8_t *out, uint8_t *out_scale, float *out_probs)
+{
+    if (T < 0 || row_bytes < 1 || scale_row_bytes < 0 || k < 1 || E < 1 || n_rows < 0)
+        return ORC_BAD_ARG;
+    for (int t = 0; t < T; t++) {
+        for (int j = 0; j < k; j++) {
+            int64_t r;
+            int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
+            if (s) return s;
+            copy_bytes(out + r * row_bytes, x + (int64_t)t * row_bytes, row_bytes);
+            if (scale && out_scale && scale_row_bytes > 0)
+                copy_bytes(out_scale + r * scale_row_bytes, scale + (int64_t)t * scale_row_bytes,
+                           scale_row_bytes);
+            if (probs && out_probs) out_probs[r] = probs[(int64_t)t * k + j];
+        }
+    }
+    return ORC_OK;
+}
+
+int oracle_mask_permute_scaled(const uint8_t *x, int64_t row_bytes, const uint8_t *scale,
+                               int64_t scale_row_bytes, const float *probs, const int32_t *map,
+                               int T, int E, int n_rows, uint8_t *out, uint8_t *out_scale,
+                               float *out_probs)
+{
+    if (T < 0 || row_bytes < 1 || scale_row_bytes < 0 || E < 1 || n_rows < 0)
+        return ORC_BAD_ARG;
+    for (int t = 0; t < T; t++) {
+        int n, s = mask_count(map, E, t, &n);
+        if (s) return s;
+        for (int i = 0; i < n; i++) {
+            int row, e;
+            s = mask_slot(map, E, n_rows, t, i, &row, &e);
+            if (s) return s;
+            int zero_row = 0;
+            if (probs) {
+                float p = probs[(int64_t)t * E + e];
+                if (out_probs) out_probs[row] = p;
+                zero_row = p == 0.0f;
+            }
+            if (zero_row)
+                for (int64_t b = 0; b < row_bytes; b++) out[(int64_t)row * row_bytes + b] = 0;
+            else
+                copy_bytes(out + (int64_t)row * row_bytes, x + (int64_t)t * row_bytes, row_bytes);
+            if (scale && out_scale && scale_row_bytes > 0)
+                copy_bytes(out_scale + (int64_t)row * scale_row_bytes,
+                           scale + (int64_t)t * scale_row_bytes, scale_row_bytes);
         }
     }
     return ORC_OK;

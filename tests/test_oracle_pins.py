@@ -875,3 +875,75 @@ def test_mask_unpermute_bwd_against_direct_products():
             np.testing.assert_array_equal(d_in[r], _to_bf16_torch(gv[t] * mp[t, e]))
             ref = float(np.dot(fv[r].astype(np.float64), gv[t].astype(np.float64)))
             assert abs(dmp[t, e] - ref) <= 2.0 ** -24 * abs(ref) + 1e-45
+
+
+# --------------------------------------------- quantized rows with scales ---
+
+def _route_rows(idx, rm):
+    T, k = idx.shape
+    return rm[idx.astype(np.int64), np.arange(T)[:, None]]      # [T][k] destination rows
+
+
+@pytest.mark.parametrize("H,block,sdt", [(256, 128, "f32"), (200, 64, "f32"), (384, 128, "e8m0"),
+                                         (16, 16, "f32")])
+def test_permute_scaled_moves_fp8_rows_and_scales(H, block, sdt):
+    """FP8 rows and their scale rows land at the destinations of the (pinned)
+    row map, byte for byte; the dequantized rows are the source's."""
+    rng = np.random.default_rng(H)
+    T, E, k = 45, 11, 3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32))
+    q, sc = workloads.quantize_fp8_rows(x, block, torch.float32 if sdt == "f32"
+                                        else torch.float8_e8m0fnu)
+    qb = q.view(torch.uint8).numpy()
+    sb = sc.view(torch.uint8).numpy().reshape(T, -1) if sdt == "e8m0" else sc.numpy()
+    probs = rng.random((T, k)).astype(np.float32)
+    rm, _ = oracle.row_id_map(idx, E)
+    out, out_s, out_p = oracle.permute_scaled(qb, sb, probs, idx, rm)
+    rows = _route_rows(idx, rm)
+    for t in range(T):
+        for j in range(k):
+            r = rows[t, j]
+            np.testing.assert_array_equal(out[r], qb[t])
+            np.testing.assert_array_equal(out_s[r], np.ascontiguousarray(sb[t]).view(np.uint8))
+            assert out_p[r] == probs[t, j]
+    # dequantized: the permuted FP8 rows times their permuted scales equal the source's
+    src = q.float() * sc.float().repeat_interleave(block, dim=1)[:, :H]
+    outq = torch.from_numpy(out).view(torch.float8_e4m3fn).float()
+    outs = (torch.from_numpy(out_s).view(torch.float8_e8m0fnu) if sdt == "e8m0"
+            else torch.from_numpy(out_s.view(np.float32))).float()
+    dst = outq * outs.repeat_interleave(block, dim=1)[:, :H]
+    torch.testing.assert_close(dst[torch.from_numpy(rows.ravel())],
+                               src.repeat_interleave(k, dim=0), rtol=0, atol=0)
+
+
+def test_permute_scaled_on_bf16_rows_is_the_permute():
+    rng = np.random.default_rng(2)
+    T, E, k, H = 30, 8, 2, 24
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = _to_bf16_torch(rng.standard_normal((T, H)).astype(np.float32))
+    probs = rng.random((T, k)).astype(np.float32)
+    rm, _ = oracle.row_id_map(idx, E)
+    out, out_s, out_p = oracle.permute_scaled(x, None, probs, idx, rm)
+    ref, ref_p = oracle.permute(x, probs, idx, rm)
+    np.testing.assert_array_equal(out.view(np.uint16), ref)
+    np.testing.assert_array_equal(out_p, ref_p)
+    assert out_s is None
+
+
+def test_mask_permute_scaled_zero_prob_keeps_scale():
+    """The padding rule zeroes the data row only; the scale row still moves."""
+    x = np.array([[1, 2, 3, 4], [5, 6, 7, 8]], np.uint8)
+    sc = np.array([[0.5], [2.0]], np.float32)
+    mask = np.array([[1, 1], [1, 0]], np.int32)        # rows: e0: t0=0, t1=1; e1: t0=2
+    probs = np.array([[0.3, 0.0], [0.7, 0.0]], np.float32)
+    mm, _ = oracle.mask_row_id_map(mask)
+    out, out_s, out_p = oracle.mask_permute_scaled(x, sc, probs, mm, 3)
+    np.testing.assert_array_equal(out, [[1, 2, 3, 4], [5, 6, 7, 8], [0, 0, 0, 0]])
+    np.testing.assert_array_equal(out_s.view(np.float32).ravel(), [0.5, 2.0, 0.5])
+    np.testing.assert_array_equal(out_p, np.array([0.3, 0.7, 0.0], np.float32))
+    # bf16 rows, no scales: the same as the mask-map permute
+    xb = _to_bf16_torch(np.random.default_rng(1).standard_normal((2, 6)).astype(np.float32))
+    o1, _, _ = oracle.mask_permute_scaled(xb, None, probs, mm, 3)
+    o2, _ = oracle.mask_permute(xb, probs, mm, 3)
+    np.testing.assert_array_equal(o1.view(np.uint16), o2)

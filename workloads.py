@@ -186,6 +186,25 @@ ROUTED = {"tiny": tiny, "finegrain": finegrain, "skewed": skewed}
 CHUNKED = {"chunks8k": chunks8k, "chunks32k": chunks32k}
 
 
+def quantize_fp8_rows(x: torch.Tensor, block: int = 128, scale_dtype=torch.float32):
+    """FP8 (OCP E4M3FN) rows with one scale per `block` elements of a row:
+    scale = amax / 448 (the format's largest finite value; 1 for an all-zero
+    block), q = fp8(x / scale) by torch's round-to-nearest cast.  Returns
+    (q [T][H] float8_e4m3fn, scale [T][ceil(H / block)] of scale_dtype).  With
+    scale_dtype torch.float8_e8m0fnu the scale is rounded up to a power of two
+    first (an MX-style exponent scale).  The quantization happens upstream of
+    the path: the permute moves the bytes it is given."""
+    T, H = x.shape
+    nb = (H + block - 1) // block
+    xf = torch.nn.functional.pad(x.float(), (0, nb * block - H)).view(T, nb, block)
+    amax = xf.abs().amax(dim=2)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    if scale_dtype == torch.float8_e8m0fnu:
+        scale = torch.exp2(torch.ceil(torch.log2(scale)))
+    q = (xf / scale[:, :, None]).view(T, nb * block)[:, :H].to(torch.float8_e4m3fn)
+    return q.contiguous(), scale.to(scale_dtype).contiguous()
+
+
 def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bf16 CPU tensor's bit patterns."""
     return t.contiguous().view(torch.int16).numpy().view("uint16")
