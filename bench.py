@@ -257,7 +257,20 @@ def build_routed(m, w):
     mdP = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
     mdp = torch.empty((T, E), dtype=torch.float32, device=dev)
     step.keep += [mask, probs_te, mmap, moff, mws, mP, mpp, my, mdP, mdp]
+    # Quantized rows: FP8 (E4M3FN) tokens with fp32 scales per 128 elements.
+    q8, sc8 = workloads.quantize_fp8_rows(w.x, 128)
+    q8, sc8 = q8.to(dev), sc8.to(dev)
+    S = sc8.shape[1]
+    qP = torch.empty((n, H), dtype=q8.dtype, device=dev)
+    qS = torch.empty((n, S), dtype=torch.float32, device=dev)
+    step.keep += [q8, sc8, qP, qS]
+    fp8_bytes = T * H + n * H + 4 * S * (T + n) + 8 * n + 4 * n + 4 * n
     mb = mask_bytes(T, H, E, k)
+    step.extra += [
+        ("permute_fp8_scaled", fp8_bytes, lib.moe_permute_scaled,
+         (p(q8), 1, p(sc8), 4 * S, p(probs), p(idx), p(rm), T, H, k, E, n, p(qP), p(qS), p(pp),
+          None)),
+    ]
     step.extra += [
         ("mask_row_map", mb["mask_row_map"], lib.moe_make_mask_row_id_map,
          (p(mask), 1, T, E, -1, p(mmap), p(moff), p(mws), mws_n)),

@@ -353,6 +353,36 @@ MOE_PERM_API int moe_unpermute_mask_bwd(const void *d_out, const void *fwd_in,
                                         int32_t *dev_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Quantized rows (e.g. FP8) with per-row scale vectors moved alongside.
+ *
+ * [TE-mask] _permute_kernel with PERMUTE_SCALE, permute_with_mask_map
+ * (scale, scale_hidden_dim): each token's scale row goes to the same
+ * destination index of a permuted scale tensor as its data row.  Data rows
+ * are `hidden` elements of elem_bytes (1: any FP8 encoding, 2, or 4) and
+ * are copied bitwise, so the encoding does not enter; the routing, probs,
+ * status bits and the mask-map form's zero-prob padding rule are those of
+ * moe_permute / moe_permute_mask (the padding rule zeroes the data row only;
+ * the scale row still moves).  The inputs this library is tested with are
+ * OCP FP8 E4M3FN rows (gfx950's native FP8) with fp32 or E8M0 block scales.
+ *   scale [num_tokens][scale_row_bytes bytes] (optional; NULL: no scales),
+ *   out_scale [num_out_rows][scale_row_bytes bytes] (required with scale).
+ * The backward of these permutes acts on bf16 gradients: moe_permute_bwd /
+ * moe_unpermute_mask apply unchanged, and scales carry no gradient.
+ * ------------------------------------------------------------------------ */
+MOE_PERM_API int moe_permute_scaled(const void *x, int elem_bytes, const void *scale,
+                                    int scale_row_bytes, const float *probs,
+                                    const int32_t *topk_idx, const int32_t *row_id_map,
+                                    int num_tokens, int hidden, int topk, int num_experts,
+                                    int num_out_rows, void *out, void *out_scale,
+                                    float *out_probs, int32_t *dev_status, hipStream_t stream);
+MOE_PERM_API int moe_permute_mask_scaled(const void *x, int elem_bytes, const void *scale,
+                                         int scale_row_bytes, const float *probs,
+                                         const int32_t *row_id_map, int num_tokens, int hidden,
+                                         int num_experts, int num_out_rows, void *out,
+                                         void *out_scale, float *out_probs, int32_t *dev_status,
+                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * (3) Fused chunk sort-and-pad.
  *
  * [TE-3509] Description / Changes / Diagram: rank chunks are regrouped into

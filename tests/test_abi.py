@@ -31,7 +31,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 21
     dyn = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in dyn.splitlines() if " T " in line}

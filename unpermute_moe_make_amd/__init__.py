@@ -10,6 +10,7 @@ with a thin ctypes binding whose functions carry the C names:
   moe_topk_softmax(_bwd)              fused top-k softmax router, gradient
   moe_make_mask_row_id_map            TE mask-map form: [T, 2E+1] map from a mask
   moe_permute_mask / moe_unpermute_mask(_bwd)  TE-order copies and combine
+  moe_permute_scaled / moe_permute_mask_scaled quantized (FP8) rows + scales
   moe_sort_chunks_and_pad(_bwd)       fused chunk regroup + zero padding
   moe_unpad_and_restore_chunks(_bwd)  the matching restore
 
@@ -31,6 +32,8 @@ from ._binding import (  # noqa: F401
     moe_make_mask_row_id_map,
     moe_make_mask_row_id_map_workspace_bytes,
     moe_permute_mask,
+    moe_permute_mask_scaled,
+    moe_permute_scaled,
     moe_unpermute_mask,
     moe_unpermute_mask_bwd,
     moe_permute,

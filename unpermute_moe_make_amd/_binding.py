@@ -38,6 +38,10 @@ _SIGS = {
     "moe_unpermute_ep": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_unpermute_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_permute_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+    "moe_permute_scaled": ([_P, _I, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P],
+                           _I),
+    "moe_permute_mask_scaled": ([_P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P],
+                                _I),
     "moe_make_mask_row_id_map_workspace_bytes": ([_I, _I], _Z),
     "moe_make_mask_row_id_map": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "moe_permute_mask": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
@@ -289,6 +293,90 @@ def moe_permute_bwd(d_out: torch.Tensor, topk_idx: torch.Tensor, row_id_map: tor
                                 _ptr(_status_arg(dev_status)), _stream(stream)),
            "moe_permute_bwd")
     return d_x, d_probs
+
+
+# ---------------------------------------------------------------------------
+# quantized rows with scales
+# ---------------------------------------------------------------------------
+
+def _rows_any(t, name):
+    _need(t, name)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.element_size() not in (1, 2, 4):
+        raise TypeError(f"{name} must have 1-, 2- or 4-byte elements")
+    return t
+
+
+def _scale_rows(scale, T):
+    if scale is None:
+        return None, 0
+    _need(scale, "scale")
+    if scale.dim() != 2 or scale.shape[0] != T:
+        raise ValueError("scale must be [num_tokens, n]")
+    return scale, scale.shape[1] * scale.element_size()
+
+
+def moe_permute_scaled(x: torch.Tensor, topk_idx: torch.Tensor, row_id_map: torch.Tensor,
+                       scale: Optional[torch.Tensor] = None, probs: Optional[torch.Tensor] = None,
+                       *, out=None, out_scale=None, out_probs=None, dev_status=None,
+                       stream=None):
+    """Permute rows of any 1/2/4-byte dtype (e.g. float8_e4m3fn) with their scale
+    rows moved alongside.  Returns (out, out_scale, out_probs)."""
+    T, k, E = _routing(topk_idx, row_id_map)
+    _rows_any(x, "x")
+    if x.shape[0] != T:
+        raise ValueError("x must have num_tokens rows")
+    H = x.shape[1]
+    n = T * k
+    scale, srb = _scale_rows(scale, T)
+    _opt(probs, "probs", torch.float32, (T, k))
+    out = torch.empty((n, H), dtype=x.dtype, device=x.device) if out is None else \
+        _need(out, "out", x.dtype, (n, H))
+    if scale is not None and out_scale is None:
+        out_scale = torch.empty((n, scale.shape[1]), dtype=scale.dtype, device=x.device)
+    if scale is not None:
+        _need(out_scale, "out_scale", scale.dtype, (n, scale.shape[1]))
+    if probs is not None and out_probs is None:
+        out_probs = torch.empty(n, dtype=torch.float32, device=x.device)
+    _opt(out_probs, "out_probs", torch.float32, (n,))
+    _check(_lib.moe_permute_scaled(_ptr(x), x.element_size(), _ptr(scale), srb, _ptr(probs),
+                                   _ptr(topk_idx), _ptr(row_id_map), T, H, k, E, n, _ptr(out),
+                                   _ptr(out_scale), _ptr(out_probs),
+                                   _ptr(_status_arg(dev_status)), _stream(stream)),
+           "moe_permute_scaled")
+    return out, out_scale, out_probs
+
+
+def moe_permute_mask_scaled(x: torch.Tensor, row_id_map: torch.Tensor, num_out_rows: int,
+                            scale: Optional[torch.Tensor] = None,
+                            probs: Optional[torch.Tensor] = None, *, out=None, out_scale=None,
+                            out_probs=None, dev_status=None, stream=None):
+    """Mask-map form of moe_permute_scaled (probs [T, E]; a zero prob zeroes the
+    data row, the scale row still moves).  Returns (out, out_scale, out_probs)."""
+    T, E = _mask_map(row_id_map)
+    _rows_any(x, "x")
+    if x.shape[0] != T:
+        raise ValueError("x must have num_tokens rows")
+    H = x.shape[1]
+    n = num_out_rows
+    scale, srb = _scale_rows(scale, T)
+    _opt(probs, "probs", torch.float32, (T, E))
+    out = torch.empty((n, H), dtype=x.dtype, device=x.device) if out is None else \
+        _need(out, "out", x.dtype, (n, H))
+    if scale is not None and out_scale is None:
+        out_scale = torch.empty((n, scale.shape[1]), dtype=scale.dtype, device=x.device)
+    if scale is not None:
+        _need(out_scale, "out_scale", scale.dtype, (n, scale.shape[1]))
+    if probs is not None and out_probs is None:
+        out_probs = torch.empty(n, dtype=torch.float32, device=x.device)
+    _opt(out_probs, "out_probs", torch.float32, (n,))
+    _check(_lib.moe_permute_mask_scaled(_ptr(x), x.element_size(), _ptr(scale), srb,
+                                        _ptr(probs), _ptr(row_id_map), T, H, E, n, _ptr(out),
+                                        _ptr(out_scale), _ptr(out_probs),
+                                        _ptr(_status_arg(dev_status)), _stream(stream)),
+           "moe_permute_mask_scaled")
+    return out, out_scale, out_probs
 
 
 # ---------------------------------------------------------------------------

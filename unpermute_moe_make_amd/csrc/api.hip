@@ -53,6 +53,26 @@ int chunk_unit(int elem_bytes, int H, const void *a, const void *b) {
   return elem_bytes;
 }
 
+// Largest unit (16, 4, 2 or 1 bytes) that divides a row and aligns both bases.
+int row_unit(int64_t row_bytes, const void *a, const void *b) {
+  for (int u : {16, 4, 2}) {
+    if (row_bytes % u == 0 && aligned(a, (uintptr_t)u) && aligned(b, (uintptr_t)u)) return u;
+  }
+  return 1;
+}
+
+// Side rows (scales) of a scaled permute; 0 on success.
+int side_rows(const void *scale, int scale_row_bytes, void *out_scale, moe::SideRows *side) {
+  side->src = static_cast<const uint8_t *>(scale);
+  side->dst = static_cast<uint8_t *>(out_scale);
+  side->bytes = scale != nullptr ? scale_row_bytes : 0;
+  side->words = scale_row_bytes % 4 == 0 && aligned(scale, 4) && aligned(out_scale, 4);
+  if (scale == nullptr) return MOE_OK;
+  if (scale_row_bytes < 1) return MOE_ERR_SHAPE;
+  if (out_scale == nullptr) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +222,32 @@ MOE_PERM_API int moe_permute_bwd(const void *d_out, const float *d_out_probs,
                                         dev_status, vec_ok(H, d_out, d_x), stream));
 }
 
+MOE_PERM_API int moe_permute_scaled(const void *x, int elem_bytes, const void *scale,
+                                    int scale_row_bytes, const float *probs,
+                                    const int32_t *topk_idx, const int32_t *row_id_map,
+                                    int num_tokens, int hidden, int topk, int num_experts,
+                                    int num_out_rows, void *out, void *out_scale,
+                                    float *out_probs, int32_t *dev_status, hipStream_t stream) {
+  const int T = num_tokens, H = hidden, k = topk, E = num_experts;
+  int st = check_rows(T, H, k, E, num_out_rows);
+  if (st) return st;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_idx || !row_id_map || !out) return MOE_ERR_NULL;
+  if (out_probs != nullptr && probs == nullptr) return MOE_ERR_NULL;
+  moe::SideRows side;
+  st = side_rows(scale, scale_row_bytes, out_scale, &side);
+  if (st) return st;
+  if (!aligned(x, (uintptr_t)elem_bytes) || !aligned(out, (uintptr_t)elem_bytes) ||
+      !aligned(probs, 4) || !aligned(out_probs, 4) || !aligned(topk_idx, 4) ||
+      !aligned(row_id_map, 4) || !aligned(dev_status, 4))
+    return MOE_ERR_ALIGN;
+  const int64_t row_bytes = (int64_t)H * elem_bytes;
+  return hip_status(moe::launch_permute_rows(x, row_bytes, row_unit(row_bytes, x, out), probs,
+                                             topk_idx, row_id_map, T, k, E, num_out_rows, out,
+                                             out_probs, side, dev_status, stream));
+}
+
 MOE_PERM_API size_t moe_make_mask_row_id_map_workspace_bytes(int num_tokens, int num_experts) {
   if (num_tokens < 0 || num_experts < 1) return 0;
   return moe::maskmap_workspace_bytes(num_tokens, num_experts);
@@ -255,6 +301,32 @@ MOE_PERM_API int moe_permute_mask(const void *x, const float *probs, const int32
     return MOE_ERR_ALIGN;
   return hip_status(moe::launch_mask_permute(x, probs, row_id_map, T, H, E, num_out_rows, out,
                                              out_probs, dev_status, vec_ok(H, x, out), stream));
+}
+
+MOE_PERM_API int moe_permute_mask_scaled(const void *x, int elem_bytes, const void *scale,
+                                         int scale_row_bytes, const float *probs,
+                                         const int32_t *row_id_map, int num_tokens, int hidden,
+                                         int num_experts, int num_out_rows, void *out,
+                                         void *out_scale, float *out_probs, int32_t *dev_status,
+                                         hipStream_t stream) {
+  const int T = num_tokens, H = hidden, E = num_experts;
+  int st = check_mask_rows(T, H, E, num_out_rows);
+  if (st) return st;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !row_id_map || (num_out_rows > 0 && !out)) return MOE_ERR_NULL;
+  if (out_probs != nullptr && probs == nullptr) return MOE_ERR_NULL;
+  moe::SideRows side;
+  st = side_rows(scale, scale_row_bytes, out_scale, &side);
+  if (st) return st;
+  if (!aligned(x, (uintptr_t)elem_bytes) || !aligned(out, (uintptr_t)elem_bytes) ||
+      !aligned(probs, 4) || !aligned(out_probs, 4) || !aligned(row_id_map, 4) ||
+      !aligned(dev_status, 4))
+    return MOE_ERR_ALIGN;
+  const int64_t row_bytes = (int64_t)H * elem_bytes;
+  return hip_status(moe::launch_mask_permute_rows(x, row_bytes, row_unit(row_bytes, x, out),
+                                                  probs, row_id_map, T, E, num_out_rows, out,
+                                                  out_probs, side, dev_status, stream));
 }
 
 MOE_PERM_API int moe_unpermute_mask(const void *in, const float *merging_probs,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
 #include "moe_perm.h"
 
 namespace moe {
@@ -109,6 +110,20 @@ template <> __device__ __forceinline__ uint16_t zero_unit<uint16_t>() { return 0
 // OR status bits into the caller's device status word (vector atomic).
 __device__ __forceinline__ void report(int32_t *status, int bits) {
   if (status != nullptr && bits != 0) atomicOr(status, bits);
+}
+
+// Row `from` of a side tensor to row `to`, by the whole workgroup.
+__device__ __forceinline__ void copy_side_row(const SideRows &s, int64_t from, int64_t to) {
+  if (s.words) {
+    const int64_t n = s.bytes / 4;
+    const uint32_t *a = reinterpret_cast<const uint32_t *>(s.src) + from * n;
+    uint32_t *b = reinterpret_cast<uint32_t *>(s.dst) + to * n;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) b[i] = a[i];
+  } else {
+    const uint8_t *a = s.src + from * s.bytes;
+    uint8_t *b = s.dst + to * s.bytes;
+    for (int64_t i = threadIdx.x; i < s.bytes; i += blockDim.x) b[i] = a[i];
+  }
 }
 
 // Wave-wide fp32 sum by butterfly exchanges; every lane gets the total.

@@ -8,6 +8,14 @@
 
 namespace moe {
 
+// A per-row side vector (quantization scales) moved along with its data row.
+struct SideRows {
+  const uint8_t *src;   // [rows][bytes]
+  uint8_t *dst;         // [out rows][bytes]
+  int64_t bytes;        // bytes per row
+  int words;            // 1: copy 4-byte words (bytes % 4 == 0, both bases aligned)
+};
+
 // Row map (stable counting sort).
 size_t rowmap_workspace_bytes(int T, int k, int E);
 hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *row_id_map,
@@ -32,6 +40,18 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
                               const int32_t *topk_idx, const int32_t *row_id_map, int T, int H,
                               int k, int E, int n_rows, void *d_in, float *d_probs,
                               int32_t *dev_status, bool vec, hipStream_t s);
+
+// Rows of any element size (quantized rows) with optional side rows
+// (their scales): row_bytes per data row, moved in unit_bytes units.
+hipError_t launch_permute_rows(const void *x, int64_t row_bytes, int unit_bytes,
+                               const float *probs, const int32_t *topk_idx,
+                               const int32_t *row_id_map, int T, int k, int E, int n_rows,
+                               void *out, float *out_probs, const SideRows &side,
+                               int32_t *dev_status, hipStream_t s);
+hipError_t launch_mask_permute_rows(const void *x, int64_t row_bytes, int unit_bytes,
+                                    const float *probs, const int32_t *map, int T, int E,
+                                    int n_rows, void *out, float *out_probs,
+                                    const SideRows &side, int32_t *dev_status, hipStream_t s);
 
 // TransformerEngine mask-map form: map builder and its row kernels.
 size_t maskmap_workspace_bytes(int T, int E);

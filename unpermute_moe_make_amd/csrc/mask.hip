@@ -55,11 +55,13 @@ __device__ __forceinline__ int64_t mask_slot(const int32_t *__restrict__ mrow, i
 
 // out[row] = x[t] for each slot; with probs, out_probs[row] = probs[t][e]
 // and a zero prob writes a zero row.
-template <typename U, int VPT, int NTM>
+// SIDE: also move each token's side row (quantization scales) to the same
+// destinations, padded slots included.
+template <typename U, int VPT, int NTM, bool SIDE>
 __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
     const U *__restrict__ x, const float *__restrict__ probs, const int32_t *__restrict__ map,
     int T, int64_t V, int E, int n_rows, U *__restrict__ out, float *__restrict__ out_probs,
-    int32_t *__restrict__ dev_status) {
+    SideRows side, int32_t *__restrict__ dev_status) {
   __shared__ int64_t srow[kSlotChunk];
   __shared__ int szero[kSlotChunk];
   const int t = blockIdx.x;
@@ -102,6 +104,7 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
         const int64_t c = c0 + (int64_t)i * blockDim.x;
         if (c < V) st_row<(NTM & 2) != 0>(z ? zero : v[i], orow + c);
       }
+      if (SIDE && blockIdx.y == 0) copy_side_row(side, t, r);
     }
     __syncthreads();
   }
@@ -306,17 +309,17 @@ __global__ __launch_bounds__(kRowThreads) void mask_unpermute_bwd_kernel(
   if (blockIdx.y == 0) report(dev_status, bad);
 }
 
-template <typename U, int NTM>
+template <typename U, int NTM, bool SIDE>
 void mask_permute_dispatch(const void *x, const float *probs, const int32_t *map, int T,
                            int64_t V, int E, int n_rows, void *out, float *out_probs,
-                           int32_t *st, hipStream_t s) {
+                           const SideRows &side, int32_t *st, hipStream_t s) {
   const RowShape sh = row_shape(V, true);
   const dim3 grid(T, sh.ysplit), block(sh.threads);
   const U *xp = static_cast<const U *>(x);
   U *op = static_cast<U *>(out);
-#define MOE_MASK_PERMUTE(VPTV)                                                              \
-  hipLaunchKernelGGL((mask_permute_kernel<U, VPTV, NTM>), grid, block, 0, s, xp, probs, map, T, \
-                     V, E, n_rows, op, out_probs, st)
+#define MOE_MASK_PERMUTE(VPTV)                                                                 \
+  hipLaunchKernelGGL((mask_permute_kernel<U, VPTV, NTM, SIDE>), grid, block, 0, s, xp, probs, \
+                     map, T, V, E, n_rows, op, out_probs, side, st)
   switch (sh.vpt) {
     case 1: MOE_MASK_PERMUTE(1); break;
     case 2: MOE_MASK_PERMUTE(2); break;
@@ -379,16 +382,43 @@ void mask_unpermute_bwd_dispatch(const void *d_out, const void *fwd_in, const fl
 hipError_t launch_mask_permute(const void *x, const float *probs, const int32_t *map, int T,
                                int H, int E, int n_rows, void *out, float *out_probs,
                                int32_t *dev_status, bool vec, hipStream_t s) {
+  const SideRows none{nullptr, nullptr, 0, 0};
   const bool stream = 2ll * H * ((int64_t)n_rows + T) > kStreamBytes;
   if (vec && stream)
-    mask_permute_dispatch<v4u, MOE_MASK_PERMUTE_STREAM>(x, probs, map, T, H / 8, E, n_rows, out,
-                                                        out_probs, dev_status, s);
+    mask_permute_dispatch<v4u, MOE_MASK_PERMUTE_STREAM, false>(x, probs, map, T, H / 8, E, n_rows,
+                                                               out, out_probs, none, dev_status,
+                                                               s);
   else if (vec)
-    mask_permute_dispatch<v4u, 0>(x, probs, map, T, H / 8, E, n_rows, out, out_probs,
-                                  dev_status, s);
+    mask_permute_dispatch<v4u, 0, false>(x, probs, map, T, H / 8, E, n_rows, out, out_probs,
+                                         none, dev_status, s);
   else
-    mask_permute_dispatch<uint16_t, 0>(x, probs, map, T, H, E, n_rows, out, out_probs,
-                                       dev_status, s);
+    mask_permute_dispatch<uint16_t, 0, false>(x, probs, map, T, H, E, n_rows, out, out_probs,
+                                              none, dev_status, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_permute_rows(const void *x, int64_t row_bytes, int unit_bytes,
+                                    const float *probs, const int32_t *map, int T, int E,
+                                    int n_rows, void *out, float *out_probs,
+                                    const SideRows &side, int32_t *dev_status, hipStream_t s) {
+  const int64_t V = row_bytes / unit_bytes;
+  const bool stream = row_bytes * ((int64_t)n_rows + T) > kStreamBytes;
+#define MOE_MASK_ROWS(UT)                                                                      \
+  if (stream)                                                                                  \
+    mask_permute_dispatch<UT, MOE_MASK_PERMUTE_STREAM, true>(x, probs, map, T, V, E, n_rows,   \
+                                                             out, out_probs, side, dev_status, \
+                                                             s);                               \
+  else                                                                                         \
+    mask_permute_dispatch<UT, 0, true>(x, probs, map, T, V, E, n_rows, out, out_probs, side,   \
+                                       dev_status, s);                                         \
+  break
+  switch (unit_bytes) {
+    case 16: MOE_MASK_ROWS(v4u);
+    case 4: MOE_MASK_ROWS(uint32_t);
+    case 2: MOE_MASK_ROWS(uint16_t);
+    default: MOE_MASK_ROWS(uint8_t);
+  }
+#undef MOE_MASK_ROWS
   return hipGetLastError();
 }
 

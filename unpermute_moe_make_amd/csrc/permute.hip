@@ -64,12 +64,14 @@ __device__ __forceinline__ int resolve_slots(const int32_t *__restrict__ topk_id
 
 // ---------------------------------------------------------------- permute --
 
-template <typename U, int VPT, int NTM>
+// SIDE: also move each token's side row (quantization scales) to the same
+// destinations.
+template <typename U, int VPT, int NTM, bool SIDE>
 __global__ __launch_bounds__(kRowThreads) void permute_kernel(
     const U *__restrict__ x, const float *__restrict__ probs,
     const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
     int64_t V, int k, int E, int n_rows, U *__restrict__ out, float *__restrict__ out_probs,
-    int32_t *__restrict__ dev_status) {
+    SideRows side, int32_t *__restrict__ dev_status) {
   __shared__ int64_t srow[kMaxTopk];
   const int t = blockIdx.x;
   const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
@@ -99,6 +101,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
       const int64_t c = c0 + (int64_t)i * blockDim.x;
       if (c < V) st_row<(NTM & 2) != 0>(v[i], orow + c);
     }
+    if (SIDE && blockIdx.y == 0) copy_side_row(side, t, r);
   }
 }
 
@@ -407,29 +410,24 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
   }
 }
 
-template <typename U, int NTM>
+template <typename U, int NTM, bool SIDE>
 hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *topk_idx,
                             const int32_t *row_id_map, int T, int64_t V, int k, int E,
-                            int n_rows, void *out, float *out_probs, int32_t *dev_status,
-                            hipStream_t s) {
+                            int n_rows, void *out, float *out_probs, const SideRows &side,
+                            int32_t *dev_status, hipStream_t s) {
   const RowShape sh = row_shape(V, true);
   const dim3 grid(T, sh.ysplit), block(sh.threads);
   const U *xp = static_cast<const U *>(x);
   U *op = static_cast<U *>(out);
+#define MOE_PERMUTE(VPTV)                                                                     \
+  hipLaunchKernelGGL((permute_kernel<U, VPTV, NTM, SIDE>), grid, block, 0, s, xp, probs,       \
+                     topk_idx, row_id_map, T, V, k, E, n_rows, op, out_probs, side, dev_status)
   switch (sh.vpt) {
-    case 1:
-      hipLaunchKernelGGL((permute_kernel<U, 1, NTM>), grid, block, 0, s, xp, probs, topk_idx,
-                         row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
-      break;
-    case 2:
-      hipLaunchKernelGGL((permute_kernel<U, 2, NTM>), grid, block, 0, s, xp, probs, topk_idx,
-                         row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
-      break;
-    default:
-      hipLaunchKernelGGL((permute_kernel<U, 4, NTM>), grid, block, 0, s, xp, probs, topk_idx,
-                         row_id_map, T, V, k, E, n_rows, op, out_probs, dev_status);
-      break;
+    case 1: MOE_PERMUTE(1); break;
+    case 2: MOE_PERMUTE(2); break;
+    default: MOE_PERMUTE(4); break;
   }
+#undef MOE_PERMUTE
   return hipGetLastError();
 }
 
@@ -546,16 +544,39 @@ hipError_t launch_permute(const void *x, const float *probs, const int32_t *topk
                           const int32_t *row_id_map, int T, int H, int k, int E, int n_rows,
                           void *out, float *out_probs, int32_t *dev_status, bool vec,
                           hipStream_t s) {
+  const SideRows none{nullptr, nullptr, 0, 0};
   const int64_t bytes = 2ll * H * ((int64_t)n_rows + T);
   if (vec && bytes > kStreamBytes)
-    return permute_dispatch<v4u, MOE_PERMUTE_STREAM>(x, probs, topk_idx, row_id_map, T, H / 8,
-                                                     k, E, n_rows, out, out_probs, dev_status,
-                                                     s);
+    return permute_dispatch<v4u, MOE_PERMUTE_STREAM, false>(x, probs, topk_idx, row_id_map, T,
+                                                            H / 8, k, E, n_rows, out, out_probs,
+                                                            none, dev_status, s);
   if (vec)
-    return permute_dispatch<v4u, 0>(x, probs, topk_idx, row_id_map, T, H / 8, k, E, n_rows,
-                                    out, out_probs, dev_status, s);
-  return permute_dispatch<uint16_t, 0>(x, probs, topk_idx, row_id_map, T, H, k, E, n_rows, out,
-                                       out_probs, dev_status, s);
+    return permute_dispatch<v4u, 0, false>(x, probs, topk_idx, row_id_map, T, H / 8, k, E,
+                                           n_rows, out, out_probs, none, dev_status, s);
+  return permute_dispatch<uint16_t, 0, false>(x, probs, topk_idx, row_id_map, T, H, k, E,
+                                              n_rows, out, out_probs, none, dev_status, s);
+}
+
+hipError_t launch_permute_rows(const void *x, int64_t row_bytes, int unit_bytes,
+                               const float *probs, const int32_t *topk_idx,
+                               const int32_t *row_id_map, int T, int k, int E, int n_rows,
+                               void *out, float *out_probs, const SideRows &side,
+                               int32_t *dev_status, hipStream_t s) {
+  const int64_t V = row_bytes / unit_bytes;
+  const bool stream = row_bytes * ((int64_t)n_rows + T) > kStreamBytes;
+#define MOE_PERMUTE_ROWS(UT)                                                                  \
+  return stream ? permute_dispatch<UT, MOE_PERMUTE_STREAM, true>(                             \
+                      x, probs, topk_idx, row_id_map, T, V, k, E, n_rows, out, out_probs,     \
+                      side, dev_status, s)                                                    \
+                : permute_dispatch<UT, 0, true>(x, probs, topk_idx, row_id_map, T, V, k, E,   \
+                                                n_rows, out, out_probs, side, dev_status, s)
+  switch (unit_bytes) {
+    case 16: MOE_PERMUTE_ROWS(v4u);
+    case 4: MOE_PERMUTE_ROWS(uint32_t);
+    case 2: MOE_PERMUTE_ROWS(uint16_t);
+    default: MOE_PERMUTE_ROWS(uint8_t);
+  }
+#undef MOE_PERMUTE_ROWS
 }
 
 hipError_t launch_combine(const void *in, const float *probs, const int32_t *topk_idx,
