@@ -573,7 +573,8 @@ def test_chunks_configs(m, name):
 
 
 @pytest.mark.parametrize("case", ["fp32_tokens", "fp16_probs", "odd_hidden", "align1_identity",
-                                  "empty_group", "short_total", "big_cap", "all_empty"])
+                                  "empty_group", "short_total", "big_cap", "all_empty",
+                                  "h1536", "h7168", "h7000_fp32"])
 def test_chunk_edges(m, case):
     say(f"chunk edge {case}")
     kw = dict(N=3000, seed=50, H=256, num_ranks=4, num_experts=6, align=16, num_empty=5)
@@ -581,6 +582,11 @@ def test_chunk_edges(m, case):
         kw["dtype"] = torch.float32
     if case == "odd_hidden":
         kw["H"] = 37
+    if case in ("h1536", "h7168"):     # rows of 192 and 896 16-byte units
+        kw["H"] = int(case[1:])
+    if case == "h7000_fp32":           # 1750 units per row
+        kw["H"] = 7000
+        kw["dtype"] = torch.float32
     cw = workloads.chunked(**kw)
     sizes = cw.split_sizes.clone()
     if case == "align1_identity":

@@ -43,6 +43,36 @@ constexpr int kPadIlp = MOE_PAD_ILP;
 constexpr int kRestoreIlp = MOE_RESTORE_ILP;
 constexpr int kMapRows = 256;         // row_map entries per map workgroup (one per lane)
 
+// Row / unit split of a flat unit index u over rows of W units without a
+// hardware divide: q = floor(u / W) = (umulhi(m, u) + u) >> l, with
+// l = ceil(log2 W) and m = floor(2^32 (2^l - W) / W) + 1 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", the
+// unsigned N-bit case), exact for every u < 2^32.  The host computes (m, l)
+// and falls back to 64-bit division when the flat index can reach 2^32.
+struct RowDiv {
+  uint32_t m;
+  int l;
+  int64_t W;
+};
+
+inline RowDiv row_div(int64_t W) {
+  int l = 0;
+  while (((int64_t)1 << l) < W) l++;
+  const uint64_t num = ((uint64_t)1 << 32) * (((uint64_t)1 << l) - (uint64_t)W);
+  return RowDiv{(uint32_t)(num / (uint64_t)W + 1), l, W};
+}
+
+template <bool IDX64>
+__device__ __forceinline__ void split_unit(int64_t u, const RowDiv &dv, int64_t &d, int64_t &c) {
+  if constexpr (IDX64) {
+    d = u / dv.W;
+  } else {
+    const uint32_t x = (uint32_t)u;
+    d = (int64_t)(((uint64_t)__umulhi(dv.m, x) + x) >> dv.l);
+  }
+  c = u - d * dv.W;
+}
+
 // ----------------------------------------------------------- chunk tables --
 
 // Tables in LDS.  int32 entries are exact whenever the metadata is valid
@@ -238,11 +268,12 @@ __global__ __launch_bounds__(kCopyThreads) void chunk_map_kernel(
 
 // Pad copy driven by the row map: out[d] = in[row_map[d]] or zeros.
 // NTL / NTS: stream the source / the (dense, sequential) destination rows.
-template <typename U, bool NTL, bool NTS>
+template <typename U, bool NTL, bool NTS, bool IDX64>
 __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
-    const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, int64_t W,
+    const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, RowDiv dv,
     int n_cap, const int32_t *__restrict__ row_map, int out_cap, U *__restrict__ out,
     uint8_t *__restrict__ out_probs, int32_t *__restrict__ dev_status) {
+  const int64_t W = dv.W;
   const int64_t total = (int64_t)out_cap * W;
   const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kPadIlp + threadIdx.x;
   U v[kPadIlp];
@@ -252,8 +283,8 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
     const int64_t u = base + (int64_t)i * kCopyThreads;
     v[i] = zero_unit<U>();
     if (u < total) {
-      const int64_t d = u / W;
-      const int64_t c = u - d * W;
+      int64_t d, c;
+      split_unit<IDX64>(u, dv, d, c);
       int64_t s = row_map[d];
       if (s >= n_cap) {
         bad |= MOE_DEV_BAD_ROW;
@@ -287,25 +318,31 @@ __device__ __forceinline__ int64_t wave_total(const int32_t *__restrict__ sizes,
 // row i (if mapped) and zero-fills restored row i (if past the token total).
 // NTL / NTS: stream the (dense, sequential) padded source rows / the
 // restored rows.
-template <typename U, bool NTL, bool NTS>
+template <typename U, bool NTL, bool NTS, bool IDX64>
 __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
-    const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, int64_t W,
+    const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, RowDiv dv,
     const int32_t *__restrict__ row_map, const int32_t *__restrict__ split_sizes, int C,
     int out_cap, int n_cap, U *__restrict__ out, uint8_t *__restrict__ out_probs,
     int32_t *__restrict__ dev_status) {
+  const int64_t W = dv.W;
   const int64_t rows = max(out_cap, n_cap);
   const int64_t total = rows * W;
   const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kRestoreIlp + threadIdx.x;
   U v[kRestoreIlp];
   int32_t dst[kRestoreIlp];
+  int64_t dd[kRestoreIlp], cc[kRestoreIlp];
   int bad = 0;
 #pragma unroll
   for (int i = 0; i < kRestoreIlp; i++) {
     const int64_t u = base + (int64_t)i * kCopyThreads;
     dst[i] = -1;
+    dd[i] = -1;
+    cc[i] = 0;
     if (u < total) {
-      const int64_t d = u / W;
-      const int64_t c = u - d * W;
+      int64_t d, c;
+      split_unit<IDX64>(u, dv, d, c);
+      dd[i] = d;
+      cc[i] = c;
       if (d < out_cap) {
         const int32_t s = row_map[d];
         if (s >= n_cap) bad |= MOE_DEV_BAD_ROW;
@@ -323,8 +360,8 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
   for (int i = 0; i < kRestoreIlp; i++) {
     const int64_t u = base + (int64_t)i * kCopyThreads;
     if (u < total) {
-      const int64_t d = u / W;
-      const int64_t c = u - d * W;
+      const int64_t d = dd[i];
+      const int64_t c = cc[i];
       if (dst[i] >= 0) st_row<NTS>(v[i], out + (int64_t)dst[i] * W + c);
       if (d >= n_act && d < n_cap) {
         st_row<NTS>(zero_unit<U>(), out + u);
@@ -362,30 +399,31 @@ hipError_t launch_pad_copy(const void *in, const void *probs, int prob_bytes, in
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
   const bool stream = units * unit_bytes * 2 > kStreamBytes;
+  const RowDiv dv = row_div(row_units);
+  // flat indices of the last workgroup stay below 2^32 on the fast path
+  const bool idx64 = (int64_t)grid.x * kCopyThreads * kPadIlp >= ((int64_t)1 << 32);
+#define MOE_PAD(UT, NTL, NTS)                                                                  \
+  do {                                                                                         \
+    if (idx64)                                                                                 \
+      hipLaunchKernelGGL((pad_copy_kernel<UT, NTL, NTS, true>), grid, block, 0, s,             \
+                         static_cast<const UT *>(in), pp, prob_bytes, dv, n_cap, row_map,      \
+                         out_cap, static_cast<UT *>(out), op, dev_status);                     \
+    else                                                                                       \
+      hipLaunchKernelGGL((pad_copy_kernel<UT, NTL, NTS, false>), grid, block, 0, s,            \
+                         static_cast<const UT *>(in), pp, prob_bytes, dv, n_cap, row_map,      \
+                         out_cap, static_cast<UT *>(out), op, dev_status);                     \
+  } while (0)
   switch (unit_bytes) {
     case 16:
       if (stream)
-        hipLaunchKernelGGL((pad_copy_kernel<v4u, (MOE_PAD_STREAM & 1) != 0,
-                                            (MOE_PAD_STREAM & 2) != 0>),
-                           grid, block, 0, s, static_cast<const v4u *>(in), pp, prob_bytes,
-                           row_units, n_cap, row_map, out_cap, static_cast<v4u *>(out), op,
-                           dev_status);
+        MOE_PAD(v4u, (MOE_PAD_STREAM & 1) != 0, (MOE_PAD_STREAM & 2) != 0);
       else
-        hipLaunchKernelGGL((pad_copy_kernel<v4u, false, false>), grid, block, 0, s,
-                           static_cast<const v4u *>(in), pp, prob_bytes, row_units, n_cap,
-                           row_map, out_cap, static_cast<v4u *>(out), op, dev_status);
+        MOE_PAD(v4u, false, false);
       break;
-    case 4:
-      hipLaunchKernelGGL((pad_copy_kernel<uint32_t, false, false>), grid, block, 0, s,
-                         static_cast<const uint32_t *>(in), pp, prob_bytes, row_units, n_cap,
-                         row_map, out_cap, static_cast<uint32_t *>(out), op, dev_status);
-      break;
-    default:
-      hipLaunchKernelGGL((pad_copy_kernel<uint16_t, false, false>), grid, block, 0, s,
-                         static_cast<const uint16_t *>(in), pp, prob_bytes, row_units, n_cap,
-                         row_map, out_cap, static_cast<uint16_t *>(out), op, dev_status);
-      break;
+    case 4: MOE_PAD(uint32_t, false, false); break;
+    default: MOE_PAD(uint16_t, false, false); break;
   }
+#undef MOE_PAD
   return hipGetLastError();
 }
 
@@ -399,33 +437,30 @@ hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
   const bool stream = ((int64_t)out_cap + n_cap) * row_units * unit_bytes > kStreamBytes;
+  const RowDiv dv = row_div(row_units);
+  const bool idx64 = (int64_t)grid.x * kCopyThreads * kRestoreIlp >= ((int64_t)1 << 32);
+#define MOE_RESTORE(UT, NTL, NTS)                                                              \
+  do {                                                                                         \
+    if (idx64)                                                                                 \
+      hipLaunchKernelGGL((restore_copy_kernel<UT, NTL, NTS, true>), grid, block, 0, s,         \
+                         static_cast<const UT *>(in), pp, prob_bytes, dv, row_map, split_sizes, \
+                         C, out_cap, n_cap, static_cast<UT *>(out), op, dev_status);           \
+    else                                                                                       \
+      hipLaunchKernelGGL((restore_copy_kernel<UT, NTL, NTS, false>), grid, block, 0, s,        \
+                         static_cast<const UT *>(in), pp, prob_bytes, dv, row_map, split_sizes, \
+                         C, out_cap, n_cap, static_cast<UT *>(out), op, dev_status);           \
+  } while (0)
   switch (unit_bytes) {
     case 16:
       if (stream)
-        hipLaunchKernelGGL((restore_copy_kernel<v4u, (MOE_RESTORE_STREAM & 1) != 0,
-                                                (MOE_RESTORE_STREAM & 2) != 0>),
-                           grid, block, 0, s, static_cast<const v4u *>(in), pp, prob_bytes,
-                           row_units, row_map, split_sizes, C, out_cap, n_cap,
-                           static_cast<v4u *>(out), op, dev_status);
+        MOE_RESTORE(v4u, (MOE_RESTORE_STREAM & 1) != 0, (MOE_RESTORE_STREAM & 2) != 0);
       else
-        hipLaunchKernelGGL((restore_copy_kernel<v4u, false, false>), grid, block, 0, s,
-                           static_cast<const v4u *>(in), pp, prob_bytes, row_units, row_map,
-                           split_sizes, C, out_cap, n_cap, static_cast<v4u *>(out), op,
-                           dev_status);
+        MOE_RESTORE(v4u, false, false);
       break;
-    case 4:
-      hipLaunchKernelGGL((restore_copy_kernel<uint32_t, false, false>), grid, block, 0, s,
-                         static_cast<const uint32_t *>(in), pp, prob_bytes, row_units, row_map,
-                         split_sizes, C, out_cap, n_cap, static_cast<uint32_t *>(out), op,
-                         dev_status);
-      break;
-    default:
-      hipLaunchKernelGGL((restore_copy_kernel<uint16_t, false, false>), grid, block, 0, s,
-                         static_cast<const uint16_t *>(in), pp, prob_bytes, row_units, row_map,
-                         split_sizes, C, out_cap, n_cap, static_cast<uint16_t *>(out), op,
-                         dev_status);
-      break;
+    case 4: MOE_RESTORE(uint32_t, false, false); break;
+    default: MOE_RESTORE(uint16_t, false, false); break;
   }
+#undef MOE_RESTORE
   return hipGetLastError();
 }
 
