@@ -36,10 +36,10 @@ constexpr int kTokPerBlock = 256;  // 4 waves x 64 tokens
 constexpr int kWavesPerBlock = kTokPerBlock / kWave;
 constexpr int kFusedMaxBlocks = 64;  // up to 16384 tokens: write derives bases itself
 constexpr int kScanThreads = 256;
-#ifndef MOE_MAP_EXPERTS_PER_WRITE
-#define MOE_MAP_EXPERTS_PER_WRITE 32
-#endif
-constexpr int kExpertsPerWrite = MOE_MAP_EXPERTS_PER_WRITE;  // experts per write workgroup
+// Experts per write workgroup: 8 while there are few token blocks (more
+// workgroups to spread the map stores), 16 beyond (less repeated base
+// derivation); chosen by measurement.
+constexpr int kSmallBlocks = 32;
 
 __global__ __launch_bounds__(kTokPerBlock) void rowmap_count_kernel(
     const int32_t *__restrict__ topk_idx, int T, int k, int E,
@@ -141,28 +141,35 @@ __global__ __launch_bounds__(kScanThreads) void rowmap_colscan_kernel(
 
 // FUSED: derive totals and the earlier-block prefix from counts[nb][E];
 // otherwise counts already holds the prefix and totals the expert totals.
-// Grid (nb, ceil(E / kExpertsPerWrite)): block (b, y) writes the entries of
-// experts [y*G, y*G+G), G = kExpertsPerWrite, for the block's 256 tokens.
-template <bool FUSED>
+// Grid (nb, ceil(E / EPW)): block (b, y) writes the entries of experts
+// [y*EPW, y*EPW+EPW) for the block's 256 tokens.
+template <bool FUSED, int EPW>
 __global__ __launch_bounds__(kTokPerBlock) void rowmap_write_kernel(
     const unsigned long long *__restrict__ masks, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ totals, int T, int E, int nb, int32_t *__restrict__ row_id_map,
     int32_t *__restrict__ expert_offsets) {
   extern __shared__ int s_off[];                         // [E] expert offsets
-  __shared__ int s_pre[kExpertsPerWrite];                // rows of earlier blocks
-  __shared__ int s_base[kWavesPerBlock][kExpertsPerWrite];
-  __shared__ unsigned long long s_mask[kWavesPerBlock][kExpertsPerWrite];
+  __shared__ int s_pre[EPW];                             // rows of earlier blocks
+  __shared__ int s_base[kWavesPerBlock][EPW];
+  __shared__ unsigned long long s_mask[kWavesPerBlock][EPW];
   __shared__ int wave_tot[kTokPerBlock / kWave];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int e0 = blockIdx.y * kExpertsPerWrite;
-  const int ne = min(kExpertsPerWrite, E - e0);
+  const int e0 = blockIdx.y * EPW;
+  const int ne = min(EPW, E - e0);
 
+  // The block's own masks do not depend on the scan: load them first.
+  unsigned long long mk[kWavesPerBlock];
+  if (tid < ne) {
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; w++)
+      mk[w] = masks[((int64_t)b * kWavesPerBlock + w) * E + e0 + tid];
+  }
   for (int e = tid; e < E; e += kTokPerBlock) {
     int tot = 0, pre = 0;
     const bool mine = e >= e0 && e < e0 + ne;
     if (FUSED) {
-#pragma unroll 8
+#pragma unroll 16
       for (int b2 = 0; b2 < nb; b2++) {
         const int c = counts[(int64_t)b2 * E + e];
         tot += c;
@@ -186,10 +193,9 @@ __global__ __launch_bounds__(kTokPerBlock) void rowmap_write_kernel(
     int run = s_off[e] + s_pre[tid];
 #pragma unroll
     for (int w = 0; w < kWavesPerBlock; w++) {
-      const unsigned long long m = masks[((int64_t)b * kWavesPerBlock + w) * E + e];
-      s_mask[w][tid] = m;
+      s_mask[w][tid] = mk[w];
       s_base[w][tid] = run;
-      run += __popcll(m);
+      run += __popcll(mk[w]);
     }
   }
   __syncthreads();
@@ -289,8 +295,12 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
   for (int e = tid; e < E; e += kTokPerBlock) {
     int tot = 0;
     if (FUSED) {
-#pragma unroll 8
-      for (int b2 = 0; b2 < nb; b2++) tot += counts[(int64_t)b2 * E + e];
+      int c[kFusedMaxBlocks];
+#pragma unroll
+      for (int b2 = 0; b2 < kFusedMaxBlocks; b2++)
+        c[b2] = b2 < nb ? counts[(int64_t)b2 * E + e] : 0;
+#pragma unroll
+      for (int b2 = 0; b2 < kFusedMaxBlocks; b2++) tot += c[b2];
     } else {
       tot = totals[e];
     }
@@ -319,8 +329,12 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
       const int e = c0 + tid;
       int pre = 0;
       if (FUSED) {
-#pragma unroll 8
-        for (int b2 = 0; b2 < b; b2++) pre += counts[(int64_t)b2 * E + e];
+        int c[kFusedMaxBlocks];
+#pragma unroll
+        for (int b2 = 0; b2 < kFusedMaxBlocks; b2++)
+          c[b2] = b2 < b ? counts[(int64_t)b2 * E + e] : 0;
+#pragma unroll
+        for (int b2 = 0; b2 < kFusedMaxBlocks; b2++) pre += c[b2];
       } else {
         pre = counts[(int64_t)b * E + e];
       }
@@ -398,16 +412,21 @@ hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *
   const Workspace w = carve(ws, nb, E);
   const size_t lds_count = (size_t)kWavesPerBlock * E * sizeof(unsigned long long);
   const size_t lds_write = (size_t)E * sizeof(int);
-  const dim3 wgrid(nb, (E + kExpertsPerWrite - 1) / kExpertsPerWrite);
+  const bool small = nb <= kSmallBlocks;
+  const dim3 wgrid(nb, (E + (small ? 8 : 16) - 1) / (small ? 8 : 16));
   hipLaunchKernelGGL(rowmap_count_kernel, dim3(nb), dim3(kTokPerBlock), lds_count, s, topk_idx,
                      T, k, E, w.masks, w.counts, dev_status);
   if (nb <= kFusedMaxBlocks) {
-    hipLaunchKernelGGL(rowmap_write_kernel<true>, wgrid, dim3(kTokPerBlock), lds_write, s,
-                       w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
+    if (small)
+      hipLaunchKernelGGL((rowmap_write_kernel<true, 8>), wgrid, dim3(kTokPerBlock), lds_write, s,
+                         w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
+    else
+      hipLaunchKernelGGL((rowmap_write_kernel<true, 16>), wgrid, dim3(kTokPerBlock), lds_write,
+                         s, w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
   } else {
     hipLaunchKernelGGL(rowmap_colscan_kernel, dim3(E), dim3(kScanThreads), 0, s, w.counts, nb,
                        E, w.totals);
-    hipLaunchKernelGGL(rowmap_write_kernel<false>, wgrid, dim3(kTokPerBlock), lds_write, s,
+    hipLaunchKernelGGL((rowmap_write_kernel<false, 16>), wgrid, dim3(kTokPerBlock), lds_write, s,
                        w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
   }
   return hipGetLastError();
