@@ -6,12 +6,13 @@
 // row, for E <= 256; G = 64, the whole wave, above).  Lane l of a group
 // holds logits l, l + G, l + 2G, ... (PER of them) as order-preserving
 // 32-bit keys, so a comparison of logits is one unsigned compare.  Each of
-// the k rounds reduces the largest untaken key over the group, then the
-// lowest expert holding that key (the tie-break), both with DPP row permutes
-// (plus two cross-row exchanges when G = 64), and the lane that owned the
-// winner clears it.  The group's k winners come out in
-// descending order with deterministic tie-breaks; the softmax over them is
-// an fp32 exp of each difference from the first and a fixed-order sum.
+// the k rounds finds the group's largest key below the previous one with a
+// subtract and a min per key and a DPP row reduction (plus two cross-row
+// exchanges when G = 64).  bf16 keys carry the expert in their low half, so
+// they are distinct and the tie-break is built in; fp32 keys fall back to an
+// exact round-by-round selection (largest key, then lowest expert) in the
+// rare wave whose top k holds equal logits.  The softmax over the k is an
+// fp32 exp of each difference from the first and a fixed-order sum.
 #include "common.h"
 #include "launch.h"
 
@@ -34,14 +35,6 @@ __device__ __forceinline__ uint32_t logit_key(float f) {
 __device__ __forceinline__ float key_logit(uint32_t key) {
   if (key <= 1u) return __uint_as_float(0x7FC00000u);
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
-template <int EB>
-__device__ __forceinline__ float load_logit(const void *p, int64_t i) {
-  if constexpr (EB == 2)
-    return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
-  else
-    return static_cast<const float *>(p)[i];
 }
 
 // DPP row permutes (gfx9 encodings): quad_perm [1,0,3,2], quad_perm
@@ -96,35 +89,77 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Every lane of the wave runs every step (tokens past T are clamped to the
-// last one and store nothing), so the DPP and cross-lane exchanges always
-// read active lanes.
-template <int EB, int G, int PER>
-__global__ __launch_bounds__(kRouterWaves * kWave) void topk_softmax_kernel(
-    const void *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ topk_idx,
-    void *__restrict__ probs, int prob_bytes) {
-  constexpr int kGroups = kRouterWaves * (kWave / G);
-  __shared__ float sval[kGroups][MOE_MAX_TOPK];
-  __shared__ int sidx[kGroups][MOE_MAX_TOPK];
-  const int grp = threadIdx.x / G;
-  const int gl = threadIdx.x % G;
-  const int t = blockIdx.x * kGroups + grp;
-  const bool live = t < T;
-  const int64_t row = (int64_t)(live ? t : T - 1) * E;
-
-  uint32_t key[PER];
-#pragma unroll
-  for (int s = 0; s < PER; s++) {
-    const int e = s * G + gl;
-    key[s] = e < E ? logit_key(load_logit<EB>(logits, row + e)) : 0u;
+template <int G>
+__device__ __forceinline__ uint32_t group_sum_u32(uint32_t v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  if constexpr (G == 64) {
+    v += (uint32_t)__shfl_xor((int)v, 16, kWave);
+    v += (uint32_t)__shfl_xor((int)v, 32, kWave);
   }
+  return v;
+}
+
+// bf16 logit -> 16-bit order-preserving key, as logit_key: -0 folded into +0,
+// NaN -> 1, real keys >= 0x7F.
+__device__ __forceinline__ uint32_t bf16_key(uint32_t b) {
+  if ((b & 0x7F80u) == 0x7F80u && (b & 0x7Fu) != 0u) return 1u;
+  if (b == 0x8000u) b = 0u;
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+
+__device__ __forceinline__ float bf16_key_logit(uint32_t key16) {
+  if (key16 <= 1u) return __uint_as_float(0x7FC00000u);
+  const uint32_t b = (key16 & 0x8000u) ? (key16 & 0x7FFFu) : (~key16 & 0xFFFFu);
+  return __uint_as_float(b << 16);
+}
+
+// The k largest keys of the group by repeated "largest key below the last
+// one": with lim = last - 1, lim - key is small for keys below the last and
+// wraps to a large value for the others, so one min over (lim - key) per
+// round finds the next key without clearing anything.  Returns whether the
+// k keys came out strictly decreasing and real (> 1 never needed: real keys
+// are >= 1); group lane 0 stores them in skey[0..k).
+// FIND: the lane holding each selected key also stores its expert in
+// sidx[j] (one holder per key when the keys are distinct; the caller
+// discards sidx otherwise).
+template <int G, int PER, bool FIND>
+__device__ __forceinline__ bool select_below(const uint32_t (&key)[PER], int k, int gl,
+                                             uint32_t *skey, int *sidx, uint32_t &last) {
+  uint32_t below = 0xFFFFFFFFu;   // above every key
+  bool strict = true;
   for (int j = 0; j < k; j++) {
-    // the group's largest untaken key ...
+    const uint32_t lim = below - 1u;
+    uint32_t dmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int s = 0; s < PER; s++) dmin = min(dmin, lim - key[s]);
+    const uint32_t m = lim - group_min<G>(dmin);
+    strict = strict && m < below && m != 0u;
+    if (gl == 0) skey[j] = m;
+    if constexpr (FIND) {
+      int fs = -1;
+#pragma unroll
+      for (int s = PER - 1; s >= 0; s--) fs = key[s] == m ? s : fs;
+      if (fs >= 0) sidx[j] = fs * G + gl;
+    }
+    below = m;
+  }
+  last = below;
+  return strict;
+}
+
+// Exact selection for keys that may repeat: per round the largest untaken
+// key, then the lowest expert holding it; the winner is cleared.
+template <int G, int PER>
+__device__ __forceinline__ void select_exact(uint32_t (&key)[PER], int k, int gl, float *sval,
+                                             int *sidx) {
+  for (int j = 0; j < k; j++) {
     uint32_t bk = 0;
 #pragma unroll
     for (int s = 0; s < PER; s++) bk = max(bk, key[s]);
     const uint32_t top_key = group_max<G>(bk);
-    // ... and the lowest expert holding it (k <= E: one always exists)
     int fs = -1;
 #pragma unroll
     for (int s = PER - 1; s >= 0; s--) fs = key[s] == top_key ? s : fs;
@@ -135,8 +170,71 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void topk_softmax_kernel(
 #pragma unroll
     for (int s = 0; s < PER; s++) key[s] = s == cs ? 0u : key[s];
     if (gl == 0) {
-      sval[grp][j] = key_logit(top_key);
-      sidx[grp][j] = (int)we;
+      sval[j] = key_logit(top_key);
+      sidx[j] = (int)we;
+    }
+  }
+}
+
+// Every lane of the wave runs every step (tokens past T are clamped to the
+// last one and store nothing), so the DPP and cross-lane exchanges always
+// read active lanes.
+//
+// bf16 logits: the key is (16-bit logit key << 16) | (0xFFFF - expert), so
+// keys are distinct, larger logits first and the lower expert first among
+// equal logits; select_below alone is exact and the expert is in the key.
+// fp32 logits: select_below on the 32-bit logit keys is exact when the k
+// keys found are distinct and exactly k elements of the group reach the
+// last of them (no ties in the top k); the lane holding each key stores its
+// expert as the key is found.  Otherwise the wave takes the exact path.
+template <int EB, int G, int PER>
+__global__ __launch_bounds__(kRouterWaves * kWave) void topk_softmax_kernel(
+    const void *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ topk_idx,
+    void *__restrict__ probs, int prob_bytes) {
+  constexpr int kGroups = kRouterWaves * (kWave / G);
+  __shared__ float sval[kGroups][MOE_MAX_TOPK];
+  __shared__ int sidx[kGroups][MOE_MAX_TOPK];
+  __shared__ uint32_t skey[kGroups][MOE_MAX_TOPK];
+  const int grp = threadIdx.x / G;
+  const int gl = threadIdx.x % G;
+  const int t = blockIdx.x * kGroups + grp;
+  const bool live = t < T;
+  const int64_t row = (int64_t)(live ? t : T - 1) * E;
+
+  uint32_t key[PER];
+  uint32_t last;
+  if constexpr (EB == 2) {
+    const uint16_t *lr = static_cast<const uint16_t *>(logits) + row;
+#pragma unroll
+    for (int s = 0; s < PER; s++) {
+      const int e = s * G + gl;
+      key[s] = e < E ? (bf16_key(lr[e]) << 16) | (0xFFFFu - (uint32_t)e) : 0u;
+    }
+    select_below<G, PER, false>(key, k, gl, skey[grp], sidx[grp], last);
+    __syncwarp();
+    for (int j = gl; j < k; j += G) {
+      const uint32_t m = skey[grp][j];
+      sidx[grp][j] = (int)(0xFFFFu - (m & 0xFFFFu));
+      sval[grp][j] = bf16_key_logit(m >> 16);
+    }
+  } else {
+    const float *lr = static_cast<const float *>(logits) + row;
+#pragma unroll
+    for (int s = 0; s < PER; s++) {
+      const int e = s * G + gl;
+      key[s] = e < E ? logit_key(lr[e]) : 0u;
+    }
+    const bool strict = select_below<G, PER, true>(key, k, gl, skey[grp], sidx[grp], last);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int s = 0; s < PER; s++) cnt += key[s] >= last ? 1u : 0u;
+    cnt = group_sum_u32<G>(cnt);
+    if (__all(strict && cnt == (uint32_t)k)) {
+      __syncwarp();
+      for (int j = gl; j < k; j += G) sval[grp][j] = key_logit(skey[grp][j]);
+    } else {
+      __syncwarp();   // the fast path's stores land before the exact path rewrites them
+      select_exact<G, PER>(key, k, gl, sval[grp], sidx[grp]);
     }
   }
   __syncwarp();
