@@ -313,7 +313,8 @@ template <typename U, int NTM, bool SIDE>
 void mask_permute_dispatch(const void *x, const float *probs, const int32_t *map, int T,
                            int64_t V, int E, int n_rows, void *out, float *out_probs,
                            const SideRows &side, int32_t *st, hipStream_t s) {
-  const RowShape sh = row_shape(V, true);
+  RowShape sh = row_shape_vpt(V, 2, kRowThreads);   // as the top-k permute
+  if (sh.threads == 0) sh = row_shape(V, true);
   const dim3 grid(T, sh.ysplit), block(sh.threads);
   const U *xp = static_cast<const U *>(x);
   U *op = static_cast<U *>(out);

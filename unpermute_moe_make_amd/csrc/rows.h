@@ -26,6 +26,15 @@ struct RowShape {
   int ysplit;   // row slices per token (grid.y)
 };
 
+// A whole row in one pass with exactly `vpt` units per lane, when that fits
+// `max_threads`; ysplit 0 when it does not.
+inline RowShape row_shape_vpt(int64_t V, int vpt, int max_threads) {
+  int64_t th = (V + vpt - 1) / vpt;
+  th = ((th + kWave - 1) / kWave) * kWave;
+  if (th > max_threads) return RowShape{0, 0, 0};
+  return RowShape{(int)th, vpt, 1};
+}
+
 // One workgroup per token row (slice): cover V units with `threads` lanes of
 // `vpt` units each, preferring the least idle lanes, then mid-size groups.
 inline RowShape row_shape(int64_t V, bool allow_split) {
