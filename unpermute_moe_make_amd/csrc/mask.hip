@@ -198,8 +198,8 @@ __global__ __launch_bounds__(kRowThreads) void mask_unpermute_kernel(
 // d_merging_probs[t][e] = sum_h fwd_in[row][h] * d_out[t][h] at routed
 // experts (a fixed per-lane fmaf chain, then a fixed tree), 0 elsewhere.
 // With the probs gradient the workgroup walks the whole row in passes.
-template <int EPV, int VPT, bool NT>
-__global__ __launch_bounds__(kRowThreads) void mask_unpermute_bwd_kernel(
+template <int EPV, int VPT, bool NT, int MAXT>
+__global__ __launch_bounds__(MAXT) void mask_unpermute_bwd_kernel(
     const typename Bf16Unit<EPV>::T *__restrict__ d_out,
     const typename Bf16Unit<EPV>::T *__restrict__ fwd_in,
     const float *__restrict__ merging_probs, const int32_t *__restrict__ map, int T, int64_t V,
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kRowThreads) void mask_unpermute_bwd_kernel(
   __shared__ int64_t srow[kSlotChunk];
   __shared__ float sp[kSlotChunk];
   __shared__ int se[kSlotChunk];
-  __shared__ float sred[kRowThreads / kWave][kBatch];
+  __shared__ float sred[MAXT / kWave][kBatch];
   __shared__ float sdp[MOE_MAX_EXPERTS];
   const int t = blockIdx.x;
   const int64_t pass = (int64_t)blockDim.x * VPT;
@@ -362,14 +362,22 @@ void mask_unpermute_bwd_dispatch(const void *d_out, const void *fwd_in, const fl
                                  const int32_t *map, int T, int64_t V, int E, int n_rows,
                                  void *d_in, float *dmp, int32_t *st, hipStream_t s) {
   using U = typename Bf16Unit<EPV>::T;
-  const RowShape sh = row_shape(V, dmp == nullptr);
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
   const U *gp = static_cast<const U *>(d_out);
   const U *fp = static_cast<const U *>(fwd_in);
   U *dp = static_cast<U *>(d_in);
-#define MOE_MASK_BWD(VPTV)                                                                     \
-  hipLaunchKernelGGL((mask_unpermute_bwd_kernel<EPV, VPTV, NT>), grid, block, 0, s, gp, fp, mp, \
-                     map, T, V, E, n_rows, dp, dmp, st)
+  // One unit per lane on up to 1024 lanes when the row fits, as the top-k
+  // unpermute backward.
+  const RowShape wide = row_shape_vpt(V, 1, 1024);
+  if (wide.threads > kRowThreads) {
+    hipLaunchKernelGGL((mask_unpermute_bwd_kernel<EPV, 1, NT, 1024>), dim3(T, 1),
+                       dim3(wide.threads), 0, s, gp, fp, mp, map, T, V, E, n_rows, dp, dmp, st);
+    return;
+  }
+  const RowShape sh = row_shape(V, dmp == nullptr);
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+#define MOE_MASK_BWD(VPTV)                                                                      \
+  hipLaunchKernelGGL((mask_unpermute_bwd_kernel<EPV, VPTV, NT, kRowThreads>), grid, block, 0, s, \
+                     gp, fp, mp, map, T, V, E, n_rows, dp, dmp, st)
   switch (sh.vpt) {
     case 1: MOE_MASK_BWD(1); break;
     case 2: MOE_MASK_BWD(2); break;

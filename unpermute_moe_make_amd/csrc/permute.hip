@@ -191,7 +191,8 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 // in rank order from zero (fp32, or fp64 when FP64), then rounded to bf16.
 // Ranks without slots contribute +0, which cannot change a sum that started
 // from +0, so only the ranks present in the token are visited.  The slots
-// are ordered by (rank, slot) once per token in LDS.
+// are ordered by (rank, slot) once per token in LDS, each slot computing its
+// own place in parallel.
 template <int EPV, int VPT, bool NT, bool FP64>
 __global__ __launch_bounds__(kRowThreads) void combine_ep_kernel(
     const typename Bf16Unit<EPV>::T *__restrict__ in, const float *__restrict__ probs,
@@ -218,16 +219,17 @@ __global__ __launch_bounds__(kRowThreads) void combine_ep_kernel(
     if (blockIdx.y == 0) report(dev_status, bad);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    // stable insertion sort of the slots by rank
-    for (int j = 0; j < k; j++) {
-      int i = j;
-      while (i > 0 && srank[sorder[i - 1]] > srank[j]) {
-        sorder[i] = sorder[i - 1];
-        i--;
-      }
-      sorder[i] = j;
+  if (threadIdx.x < k) {
+    // stable order of the slots by rank: slot j's place is the number of
+    // slots before it in (rank, slot) order -- each slot finds its own
+    const int j = threadIdx.x;
+    const int rj = srank[j];
+    int pos = 0;
+    for (int i = 0; i < k; i++) {
+      const int ri = srank[i];
+      pos += (ri < rj || (ri == rj && i < j)) ? 1 : 0;
     }
+    sorder[pos] = j;
   }
   __syncthreads();
 
@@ -528,27 +530,21 @@ void combine_ep_dispatch(const void *in, const float *probs, const int32_t *topk
                          int per_rank, int bf16_partials, void *out, int32_t *st,
                          hipStream_t s) {
   using U = typename Bf16Unit<EPV>::T;
-  const RowShape sh = row_shape(V, true);
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
   const U *ip = static_cast<const U *>(in);
   U *op = static_cast<U *>(out);
+  // (one unit per lane on up to 1024 lanes was measured slower here)
+  const RowShape sh = row_shape(V, true);
+  const dim3 grid(T, sh.ysplit), block(sh.threads);
+#define MOE_EP(VPTV)                                                                          \
+  hipLaunchKernelGGL((combine_ep_kernel<EPV, VPTV, NT, FP64>), grid, block, 0, s,             \
+                     ip, probs, topk_idx, row_id_map, T, V, k, E, n_rows, per_rank,           \
+                     bf16_partials, op, st)
   switch (sh.vpt) {
-    case 1:
-      hipLaunchKernelGGL((combine_ep_kernel<EPV, 1, NT, FP64>), grid, block, 0, s, ip, probs,
-                         topk_idx, row_id_map, T, V, k, E, n_rows, per_rank, bf16_partials, op,
-                         st);
-      break;
-    case 2:
-      hipLaunchKernelGGL((combine_ep_kernel<EPV, 2, NT, FP64>), grid, block, 0, s, ip, probs,
-                         topk_idx, row_id_map, T, V, k, E, n_rows, per_rank, bf16_partials, op,
-                         st);
-      break;
-    default:
-      hipLaunchKernelGGL((combine_ep_kernel<EPV, 4, NT, FP64>), grid, block, 0, s, ip, probs,
-                         topk_idx, row_id_map, T, V, k, E, n_rows, per_rank, bf16_partials, op,
-                         st);
-      break;
+    case 1: MOE_EP(1); break;
+    case 2: MOE_EP(2); break;
+    default: MOE_EP(4); break;
   }
+#undef MOE_EP
 }
 
 }  // namespace
