@@ -278,14 +278,37 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_count_kernel(
 
 constexpr int kMaskChunk = kTokPerBlock;   // experts staged in LDS at a time
 
-// Per-token map rows.  FUSED as for rowmap_write_kernel.  Each lane owns
-// one token and walks the experts from the top down, chunk by chunk,
-// appending its kept rows; entries past the token's count are not written.
-template <bool FUSED>
+// Bit i of the result: entry i of a 16-byte vector of routing-mask entries
+// (16 one-byte or 4 four-byte) is nonzero.
+template <int MB>
+__device__ __forceinline__ uint32_t nonzero_bits(v4u v) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint32_t w = v[q];
+    if constexpr (MB == 4) {
+      out |= (uint32_t)(w != 0u) << q;
+    } else {
+      // high bit of each byte set iff the byte is nonzero, then the four high
+      // bits gathered into a nibble by one multiply (no carries collide)
+      const uint32_t h = (((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u;
+      out |= (((h >> 7) * 0x00204081u) >> 21 & 0xFu) << (4 * q);
+    }
+  }
+  return out;
+}
+
+// Per-token map rows.  FUSED as for rowmap_write_kernel.  Each lane owns one
+// token.  Chunk by chunk from the top expert down, the block stages each
+// expert's wave-tile masks and row bases in LDS; the lane reads its own
+// routing-mask row for the chunk (VEC: 16-byte vectors), turns it into a
+// bitset and visits only its routed experts, highest first, appending the
+// kept rows.  Entries past the token's count are not written.
+template <bool FUSED, int MB, bool VEC>
 __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
-    const unsigned long long *__restrict__ masks, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ totals, int T, int E, int nb, int num_out,
-    int32_t *__restrict__ map, int32_t *__restrict__ expert_offsets) {
+    const void *__restrict__ routing_map, const unsigned long long *__restrict__ masks,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ totals, int T, int E,
+    int nb, int num_out, int32_t *__restrict__ map, int32_t *__restrict__ expert_offsets) {
   __shared__ int s_off[MOE_MAX_EXPERTS];
   __shared__ unsigned long long s_mask[kWavesPerBlock][kMaskChunk];
   __shared__ int s_base[kWavesPerBlock][kMaskChunk];
@@ -295,12 +318,8 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
   for (int e = tid; e < E; e += kTokPerBlock) {
     int tot = 0;
     if (FUSED) {
-      int c[kFusedMaxBlocks];
-#pragma unroll
-      for (int b2 = 0; b2 < kFusedMaxBlocks; b2++)
-        c[b2] = b2 < nb ? counts[(int64_t)b2 * E + e] : 0;
-#pragma unroll
-      for (int b2 = 0; b2 < kFusedMaxBlocks; b2++) tot += c[b2];
+#pragma unroll 16
+      for (int b2 = 0; b2 < nb; b2++) tot += counts[(int64_t)b2 * E + e];
     } else {
       tot = totals[e];
     }
@@ -315,26 +334,54 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
   }
 
   const int w = tid / kWave;
-  const int lane = tid & (kWave - 1);
   const int t = b * kTokPerBlock + tid;
   const int64_t W = 2 * (int64_t)E + 1;
   int32_t *mrow = map + (int64_t)t * W;
+  const uint8_t *rrow = static_cast<const uint8_t *>(routing_map) + (int64_t)t * E * MB;
   int n = 0;
   const int nchunks = (E + kMaskChunk - 1) / kMaskChunk;
   for (int ch = nchunks - 1; ch >= 0; ch--) {
     const int c0 = ch * kMaskChunk;
     const int nc = min(kMaskChunk, E - c0);
+    // this lane's routed experts of the chunk, as a bitset (loads first)
+    uint32_t bits[kMaskChunk / 32];
+#pragma unroll
+    for (int i = 0; i < kMaskChunk / 32; i++) bits[i] = 0u;
+    if (t < T) {
+      if constexpr (VEC) {
+        constexpr int kPerVec = 16 / MB;
+        const v4u *src = reinterpret_cast<const v4u *>(rrow + (int64_t)c0 * MB);
+#pragma unroll
+        for (int q = 0; q < kMaskChunk / kPerVec; q++) {
+          if (q * kPerVec < nc) {
+            const uint32_t nz = nonzero_bits<MB>(src[q]);
+            bits[q * kPerVec / 32] |= nz << ((q * kPerVec) % 32);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int word = 0; word < kMaskChunk / 32; word++) {
+          uint32_t x = 0u;
+          for (int i2 = 0; i2 < 32 && word * 32 + i2 < nc; i2++) {
+            const uint8_t *p = rrow + (int64_t)(c0 + word * 32 + i2) * MB;
+            bool on;
+            if constexpr (MB == 4)
+              on = *reinterpret_cast<const uint32_t *>(p) != 0u;
+            else
+              on = *p != 0;
+            x |= (uint32_t)on << i2;
+          }
+          bits[word] = x;
+        }
+      }
+    }
     __syncthreads();   // the previous chunk's readers are done
     if (tid < nc) {
       const int e = c0 + tid;
       int pre = 0;
       if (FUSED) {
-        int c[kFusedMaxBlocks];
-#pragma unroll
-        for (int b2 = 0; b2 < kFusedMaxBlocks; b2++)
-          c[b2] = b2 < b ? counts[(int64_t)b2 * E + e] : 0;
-#pragma unroll
-        for (int b2 = 0; b2 < kFusedMaxBlocks; b2++) pre += c[b2];
+#pragma unroll 16
+        for (int b2 = 0; b2 < b; b2++) pre += counts[(int64_t)b2 * E + e];
       } else {
         pre = counts[(int64_t)b * E + e];
       }
@@ -348,18 +395,21 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
       }
     }
     __syncthreads();
-    if (t < T) {
-      for (int i = nc - 1; i >= 0; i--) {
+#pragma unroll
+    for (int word = kMaskChunk / 32 - 1; word >= 0; word--) {
+      uint32_t x = bits[word];
+      while (x != 0u) {
+        const int hb = 31 - __clz((int)x);
+        x &= ~(1u << hb);
+        const int i = word * 32 + hb;
         const unsigned long long m = s_mask[w][i];
-        if ((m >> lane) & 1ull) {
-          const int row = s_base[w][i] + (int)__builtin_amdgcn_mbcnt_hi(
-                                             (unsigned)(m >> 32),
-                                             __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-          if (row < kept) {
-            mrow[n] = row;
-            mrow[E + n] = c0 + i;
-            n++;
-          }
+        const int row = s_base[w][i] + (int)__builtin_amdgcn_mbcnt_hi(
+                                           (unsigned)(m >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+        if (row < kept) {
+          mrow[n] = row;
+          mrow[E + n] = c0 + i;
+          n++;
         }
       }
     }
@@ -457,15 +507,25 @@ hipError_t launch_maskmap(const void *routing_map, int mask_bytes, int T, int E,
     if (vec) MOE_MASK_COUNT(1, 4); else MOE_MASK_COUNT(1, 1);
   }
 #undef MOE_MASK_COUNT
-  if (nb <= kFusedMaxBlocks) {
-    hipLaunchKernelGGL(maskmap_write_kernel<true>, dim3(nb), dim3(kTokPerBlock), 0, s, w.masks,
-                       w.counts, w.totals, T, E, nb, num_out, map, expert_offsets);
-  } else {
+  const bool fused = nb <= kFusedMaxBlocks;
+  if (!fused)
     hipLaunchKernelGGL(rowmap_colscan_kernel, dim3(E), dim3(kScanThreads), 0, s, w.counts, nb,
                        E, w.totals);
-    hipLaunchKernelGGL(maskmap_write_kernel<false>, dim3(nb), dim3(kTokPerBlock), 0, s, w.masks,
-                       w.counts, w.totals, T, E, nb, num_out, map, expert_offsets);
+  // Each lane's mask row is read in 16-byte vectors when every row starts
+  // 16-byte aligned.
+  const bool rvec = ((int64_t)E * mask_bytes) % 16 == 0 && a % 16 == 0;
+#define MOE_MASK_WRITE(F, MB, VC)                                                              \
+  hipLaunchKernelGGL((maskmap_write_kernel<F, MB, VC>), dim3(nb), dim3(kTokPerBlock), 0, s,     \
+                     routing_map, w.masks, w.counts, w.totals, T, E, nb, num_out, map,         \
+                     expert_offsets)
+  if (mask_bytes == 4) {
+    if (fused) { if (rvec) MOE_MASK_WRITE(true, 4, true); else MOE_MASK_WRITE(true, 4, false); }
+    else { if (rvec) MOE_MASK_WRITE(false, 4, true); else MOE_MASK_WRITE(false, 4, false); }
+  } else {
+    if (fused) { if (rvec) MOE_MASK_WRITE(true, 1, true); else MOE_MASK_WRITE(true, 1, false); }
+    else { if (rvec) MOE_MASK_WRITE(false, 1, true); else MOE_MASK_WRITE(false, 1, false); }
   }
+#undef MOE_MASK_WRITE
   return hipGetLastError();
 }
 
