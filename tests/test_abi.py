@@ -161,3 +161,85 @@ def test_binding_rejects_host_tensors():
     idx = torch.zeros(4, 2, dtype=torch.int32)
     with pytest.raises(ValueError):
         m.moe_make_row_id_map(idx, 8)
+
+
+def test_next_rows_host_errors(lib):
+    P = ctypes.c_void_p
+    # moe_unpermute_ep(in, probs, idx, map, T, H, k, E, n_in, ep, flags, out, st, stream)
+    f = lib.moe_unpermute_ep
+    assert f(P(FAKE), None, P(FAKE), P(FAKE), 16, 64, 4, 32, 64, 3, 1, P(FAKE), None,
+             None) == MOE_ERR_SHAPE          # ep does not divide E
+    assert f(P(FAKE), None, P(FAKE), P(FAKE), 16, 64, 4, 32, 64, 0, 1, P(FAKE), None,
+             None) == MOE_ERR_SHAPE
+    assert f(P(FAKE), None, P(FAKE), P(FAKE), 16, 64, 4, 32, 64, 4, 4, P(FAKE), None,
+             None) == MOE_ERR_UNSUPPORTED    # unknown flag bit
+    assert f(P(FAKE), None, P(FAKE), None, 16, 64, 4, 32, 64, 4, 1, P(FAKE), None,
+             None) == MOE_ERR_NULL
+    # moe_topk_softmax(logits, lb, T, E, k, idx, probs, pb, stream)
+    r = lib.moe_topk_softmax
+    assert r(P(FAKE), 4, 16, 8, 9, P(FAKE), P(FAKE), 4, None) == MOE_ERR_SHAPE      # k > E
+    assert r(P(FAKE), 4, 16, 8, 0, P(FAKE), P(FAKE), 4, None) == MOE_ERR_SHAPE
+    assert r(P(FAKE), 4, 16, 4096, 8, P(FAKE), P(FAKE), 4, None) == MOE_ERR_UNSUPPORTED
+    assert r(P(FAKE), 4, 16, 128, 65, P(FAKE), P(FAKE), 4, None) == MOE_ERR_UNSUPPORTED
+    assert r(P(FAKE), 3, 16, 8, 2, P(FAKE), P(FAKE), 4, None) == MOE_ERR_UNSUPPORTED
+    assert r(P(FAKE), 4, 16, 8, 2, P(FAKE), P(FAKE), 8, None) == MOE_ERR_UNSUPPORTED
+    assert r(None, 4, 16, 8, 2, P(FAKE), P(FAKE), 4, None) == MOE_ERR_NULL
+    assert r(P(MIS), 4, 16, 8, 2, P(FAKE), P(FAKE), 4, None) == MOE_ERR_ALIGN
+    assert r(None, 4, 0, 8, 2, None, None, 4, None) == MOE_OK                       # T == 0
+    # moe_topk_softmax_bwd(dp, p, pb, idx, T, E, k, d_logits, lb, st, stream)
+    rb = lib.moe_topk_softmax_bwd
+    assert rb(P(FAKE), P(FAKE), 4, P(FAKE), 16, 8, 9, P(FAKE), 4, None, None) == MOE_ERR_SHAPE
+    assert rb(P(FAKE), P(FAKE), 2, P(FAKE), 16, 8, 2, P(FAKE), 1, None,
+              None) == MOE_ERR_UNSUPPORTED
+    assert rb(P(FAKE), None, 4, P(FAKE), 16, 8, 2, P(FAKE), 4, None, None) == MOE_ERR_NULL
+    # moe_make_mask_row_id_map(mask, mb, T, E, num_out, map, off, ws, ws_bytes, stream)
+    g = lib.moe_make_mask_row_id_map
+    need = lib.moe_make_mask_row_id_map_workspace_bytes(16, 8)
+    assert need > 0 and lib.moe_make_mask_row_id_map_workspace_bytes(-1, 8) == 0
+    assert g(P(FAKE), 2, 16, 8, -1, P(FAKE), P(FAKE), P(FAKE), need,
+             None) == MOE_ERR_UNSUPPORTED    # 2-byte mask entries
+    assert g(P(FAKE), 1, 16, 8, -2, P(FAKE), P(FAKE), P(FAKE), need, None) == MOE_ERR_SHAPE
+    assert g(P(FAKE), 1, 16, 4096, -1, P(FAKE), P(FAKE), P(FAKE), need,
+             None) == MOE_ERR_UNSUPPORTED
+    assert g(None, 1, 16, 8, -1, P(FAKE), P(FAKE), P(FAKE), need, None) == MOE_ERR_NULL
+    assert g(P(FAKE), 1, 16, 8, -1, P(FAKE), P(FAKE), P(FAKE), need - 1,
+             None) == MOE_ERR_WORKSPACE
+    assert g(P(FAKE), 4, 16, 8, -1, P(FAKE), P(FAKE), P(FAKE + 64), need,
+             None) == MOE_ERR_ALIGN          # workspace not 256-byte aligned
+    assert g(P(MIS), 4, 16, 8, -1, P(FAKE), P(FAKE), P(FAKE), need, None) == MOE_ERR_ALIGN
+    # moe_permute_mask(x, probs, map, T, H, E, n_out, out, out_probs, st, stream)
+    pm = lib.moe_permute_mask
+    assert pm(P(FAKE), None, P(FAKE), 16, 0, 8, 10, P(FAKE), None, None, None) == MOE_ERR_SHAPE
+    assert pm(P(FAKE), None, None, 16, 64, 8, 10, P(FAKE), None, None, None) == MOE_ERR_NULL
+    assert pm(P(FAKE), None, P(FAKE), 16, 64, 8, 10, P(FAKE), P(FAKE), None,
+              None) == MOE_ERR_NULL          # out_probs without probs
+    # moe_unpermute_mask(in, mp, pp, map, T, H, E, n_in, out, up, st, stream)
+    um = lib.moe_unpermute_mask
+    assert um(P(FAKE), None, P(FAKE), P(FAKE), 16, 64, 8, 10, P(FAKE), None, None,
+              None) == MOE_ERR_NULL          # permuted probs without their output
+    assert um(P(FAKE), P(MIS), None, P(FAKE), 16, 64, 8, 10, P(FAKE), None, None,
+              None) == MOE_ERR_ALIGN
+    # moe_unpermute_mask_bwd(d_out, fwd_in, mp, map, T, H, E, n, d_in, dmp, st, stream)
+    bm = lib.moe_unpermute_mask_bwd
+    assert bm(P(FAKE), P(FAKE), None, P(FAKE), 16, 64, 8, 10, P(FAKE), None, None,
+              None) == MOE_ERR_NULL          # merging probs are required
+    assert bm(P(FAKE), None, P(FAKE), P(FAKE), 16, 64, 8, 10, P(FAKE), P(FAKE), None,
+              None) == MOE_ERR_NULL          # prob grads need fwd_in
+    # moe_permute_scaled(x, eb, scale, srb, probs, idx, map, T, H, k, E, n, out, out_s, out_p,
+    #                    st, stream)
+    ps = lib.moe_permute_scaled
+    assert ps(P(FAKE), 8, None, 0, None, P(FAKE), P(FAKE), 16, 64, 4, 32, 64, P(FAKE), None,
+              None, None, None) == MOE_ERR_UNSUPPORTED
+    assert ps(P(FAKE), 1, P(FAKE), 16, None, P(FAKE), P(FAKE), 16, 64, 4, 32, 64, P(FAKE),
+              None, None, None, None) == MOE_ERR_NULL       # scales without out_scale
+    assert ps(P(FAKE), 1, P(FAKE), 0, None, P(FAKE), P(FAKE), 16, 64, 4, 32, 64, P(FAKE),
+              P(FAKE), None, None, None) == MOE_ERR_SHAPE   # empty scale rows
+    assert ps(P(FAKE + 1), 2, None, 0, None, P(FAKE), P(FAKE), 16, 64, 4, 32, 64, P(FAKE),
+              None, None, None, None) == MOE_ERR_ALIGN
+    # moe_permute_mask_scaled(x, eb, scale, srb, probs, map, T, H, E, n, out, out_s, out_p,
+    #                         st, stream)
+    pms = lib.moe_permute_mask_scaled
+    assert pms(P(FAKE), 1, P(FAKE), 8, None, P(FAKE), 16, 64, 8, 10, P(FAKE), None, None, None,
+               None) == MOE_ERR_NULL
+    assert pms(None, 1, None, 0, None, None, 0, 64, 8, 0, None, None, None, None,
+               None) == MOE_OK             # T == 0
