@@ -311,6 +311,16 @@ def build_chunks(m, cw):
 
 # --------------------------------------------------------- CPU baseline ----
 
+def op_stats(times, nbytes):
+    """Mean, median, p10 / p90 of sorted event times (µs) and the rate."""
+    n = len(times)
+    mean = sum(times) / n
+    return {"us_mean": round(mean, 2), "us_median": round(times[n // 2], 2),
+            "us_p10": round(times[n // 10], 2), "us_p90": round(times[(9 * n) // 10], 2),
+            "bytes": nbytes, "GBps": round(nbytes / (mean * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+
+
 def cpu_baseline(name, w, target_s, step_bytes):
     """The oracle, untuned and single-threaded, on a bounded sample of the
     same workload: whole steps on a prefix of the tokens, repeated until
@@ -357,9 +367,10 @@ def cpu_baseline(name, w, target_s, step_bytes):
             break
     per_step = el / reps
     gbs = step_bytes * frac / per_step / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample}, {reps} repetitions, {el:.1f} s, single thread",
-            "seconds_per_full_step": round(per_step / frac, 4)}
+    result = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+              "sample": f"{sample}, {reps} repetitions, {el:.1f} s, single thread",
+              "seconds_per_full_step": round(per_step / frac, 4)}
+    return result
 
 
 # ----------------------------------------------------------------- main ----
@@ -408,13 +419,28 @@ def main():
     per_op = {}
     for n in names:
         times = sorted(hev.elapsed_us(evs[i][n][0], evs[i][n][1]) for i in range(K2))
-        mean = sum(times) / K2
-        per_op[n] = {"us_mean": round(mean, 2), "us_median": round(times[K2 // 2], 2),
-                     "bytes": op_bytes[n],
-                     "GBps": round(op_bytes[n] / (mean * 1e-6) / 1e9, 1),
-                     "pct_hbm_peak": round(100 * op_bytes[n] / (mean * 1e-6) / 1e9 /
-                                           HBM_PEAK_GBS, 1)}
+        per_op[n] = op_stats(times, op_bytes[n])
     dom = max(names, key=lambda n: per_op[n]["us_mean"])
+
+    # Cold pass: a 512 MiB read of an unrelated buffer before every op
+    # (outside its events) evicts the op's inputs from the Infinity Cache and
+    # writes back whatever was dirty, so the op starts from clean, unrelated
+    # cache contents.  (A write pass would leave 256 MB of dirty lines whose
+    # write-back the op would then pay.)
+    flush = torch.ones(512 << 18, dtype=torch.float32, device="cuda:0")
+    evc = [{n: (hev.create(), hev.create()) for n in names} for _ in range(K2)]
+    for i in range(K2):
+        for n, fn, a in step.ops:
+            flush.sum()
+            hev.record(evc[i][n][0], sv)
+            st = fn(*a, sv)
+            hev.record(evc[i][n][1], sv)
+            if st != 0:
+                raise RuntimeError(f"{n}: status {st}")
+    torch.cuda.synchronize()
+    del flush
+    per_op_cold = {n: op_stats(sorted(hev.elapsed_us(evc[i][n][0], evc[i][n][1])
+                                      for i in range(K2)), op_bytes[n]) for n in names}
 
     # Timed region: exactly K steps; events only around the dominant op.
     K = args.steps
@@ -454,6 +480,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "step_bytes": step_bytes,
         "per_op": per_op,
+        "per_op_cold": per_op_cold,
         "roofline": {"bound": "hbm", "kernel": dom, "kernels": OP_KERNELS[dom],
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "us_per_launch": round(dom_us, 2),
