@@ -37,6 +37,10 @@ constexpr int kMaxTopk = MOE_MAX_TOPK;
 #ifndef MOE_COMBINE_BWD_STREAM
 #define MOE_COMBINE_BWD_STREAM 3
 #endif
+// Units per lane of the permute when a row fits one pass; build-time tuning.
+#ifndef MOE_PERMUTE_VPT
+#define MOE_PERMUTE_VPT 2
+#endif
 // Largest workgroup of the unpermute backward's one-unit-per-lane shape.
 constexpr int kBwdThreads = 1024;
 
@@ -421,7 +425,7 @@ hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *to
                             int32_t *dev_status, hipStream_t s) {
   // two units per lane when a row fits one pass (measured: a 4 KiB row moves
   // faster with 128 lanes than with 256)
-  RowShape sh = row_shape_vpt(V, 2, kRowThreads);
+  RowShape sh = row_shape_vpt(V, MOE_PERMUTE_VPT, kRowThreads);
   if (sh.threads == 0) sh = row_shape(V, true);
   const dim3 grid(T, sh.ysplit), block(sh.threads);
   const U *xp = static_cast<const U *>(x);

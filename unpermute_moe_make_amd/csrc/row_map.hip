@@ -36,6 +36,7 @@ constexpr int kTokPerBlock = 256;  // 4 waves x 64 tokens
 constexpr int kWavesPerBlock = kTokPerBlock / kWave;
 constexpr int kFusedMaxBlocks = 64;  // up to 16384 tokens: write derives bases itself
 constexpr int kScanThreads = 256;
+constexpr int kCountBatch = 8;     // topk indices loaded per lane before use
 // Experts per write workgroup: 8 while there are few token blocks (more
 // workgroups to spread the map stores), 16 beyond (less repeated base
 // derivation); chosen by measurement.
@@ -56,17 +57,30 @@ __global__ __launch_bounds__(kTokPerBlock) void rowmap_count_kernel(
   const int nflat = ntok * k;
   const int32_t *src = topk_idx + (int64_t)t0 * k;
   int bad = 0;
-  // Flat, coalesced walk over the block's [ntok][k] indices.
-  for (int f = tid; f < nflat; f += kTokPerBlock) {
-    const int e = src[f];
-    const int tl = f / k;
-    if ((unsigned)e >= (unsigned)E) {
-      bad |= MOE_DEV_BAD_EXPERT;
-      continue;
+  // Flat, coalesced walk over the block's [ntok][k] indices, kCountBatch
+  // loads of a lane in flight before its first LDS atomic (one memory
+  // latency per batch rather than per index).
+  for (int f0 = tid; f0 < nflat; f0 += kTokPerBlock * kCountBatch) {
+    int ev[kCountBatch];
+#pragma unroll
+    for (int i = 0; i < kCountBatch; i++) {
+      const int f = f0 + i * kTokPerBlock;
+      ev[i] = f < nflat ? src[f] : 0;
     }
-    const unsigned long long bit = 1ull << (tl & (kWave - 1));
-    const unsigned long long old = atomicOr(&smask[(tl / kWave) * E + e], bit);
-    if (old & bit) bad |= MOE_DEV_DUP_EXPERT;
+#pragma unroll
+    for (int i = 0; i < kCountBatch; i++) {
+      const int f = f0 + i * kTokPerBlock;
+      if (f >= nflat) break;
+      const int e = ev[i];
+      const int tl = f / k;
+      if ((unsigned)e >= (unsigned)E) {
+        bad |= MOE_DEV_BAD_EXPERT;
+        continue;
+      }
+      const unsigned long long bit = 1ull << (tl & (kWave - 1));
+      const unsigned long long old = atomicOr(&smask[(tl / kWave) * E + e], bit);
+      if (old & bit) bad |= MOE_DEV_DUP_EXPERT;
+    }
   }
   report(dev_status, bad);
   __syncthreads();
