@@ -27,10 +27,10 @@ namespace {
 // calls larger than kStreamBytes (bit 0: non-temporal loads, bit 1:
 // non-temporal stores).
 #ifndef MOE_PAD_ILP
-#define MOE_PAD_ILP 2
+#define MOE_PAD_ILP 1
 #endif
 #ifndef MOE_RESTORE_ILP
-#define MOE_RESTORE_ILP 4
+#define MOE_RESTORE_ILP 3
 #endif
 #ifndef MOE_PAD_STREAM
 #define MOE_PAD_STREAM 2
@@ -38,7 +38,10 @@ namespace {
 #ifndef MOE_RESTORE_STREAM
 #define MOE_RESTORE_STREAM 1
 #endif
-constexpr int kCopyThreads = 256;
+#ifndef MOE_COPY_THREADS
+#define MOE_COPY_THREADS 256
+#endif
+constexpr int kCopyThreads = MOE_COPY_THREADS;
 constexpr int kPadIlp = MOE_PAD_ILP;
 constexpr int kRestoreIlp = MOE_RESTORE_ILP;
 constexpr int kMapRows = 256;         // row_map entries per map workgroup (one per lane)
