@@ -278,7 +278,9 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
     uint8_t *__restrict__ out_probs, int32_t *__restrict__ dev_status) {
   const int64_t W = dv.W;
   const int64_t total = (int64_t)out_cap * W;
-  const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kPadIlp + threadIdx.x;
+  const int64_t base0 = spill_block() * kCopyThreads * kPadIlp;
+  if (base0 >= total) return;  // a workgroup past the end
+  const int64_t base = base0 + threadIdx.x;
   U v[kPadIlp];
   int bad = 0;
 #pragma unroll
@@ -330,7 +332,9 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
   const int64_t W = dv.W;
   const int64_t rows = max(out_cap, n_cap);
   const int64_t total = rows * W;
-  const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kRestoreIlp + threadIdx.x;
+  const int64_t base0 = spill_block() * kCopyThreads * kRestoreIlp;
+  if (base0 >= total) return;  // a workgroup past the end
+  const int64_t base = base0 + threadIdx.x;
   U v[kRestoreIlp];
   int32_t dst[kRestoreIlp];
   int64_t dd[kRestoreIlp], cc[kRestoreIlp];
@@ -375,9 +379,9 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
   report(dev_status, bad);
 }
 
-inline unsigned copy_blocks(int64_t units, int ilp) {
+inline int64_t copy_blocks(int64_t units, int ilp) {
   const int64_t per = (int64_t)kCopyThreads * ilp;
-  return (unsigned)((units + per - 1) / per);
+  return (units + per - 1) / per;
 }
 
 }  // namespace
@@ -398,13 +402,14 @@ hipError_t launch_pad_copy(const void *in, const void *probs, int prob_bytes, in
                            void *out, void *out_probs, int32_t *dev_status, hipStream_t s) {
   const int64_t units = (int64_t)out_cap * row_units;
   if (units == 0) return hipSuccess;
-  const dim3 grid(copy_blocks(units, kPadIlp)), block(kCopyThreads);
+  const int64_t blocks = copy_blocks(units, kPadIlp);
+  const dim3 grid = spill_grid(blocks), block(kCopyThreads);
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
   const bool stream = units * unit_bytes * 2 > kStreamBytes;
   const RowDiv dv = row_div(row_units);
   // flat indices of the last workgroup stay below 2^32 on the fast path
-  const bool idx64 = (int64_t)grid.x * kCopyThreads * kPadIlp >= ((int64_t)1 << 32);
+  const bool idx64 = blocks * kCopyThreads * kPadIlp >= ((int64_t)1 << 32);
 #define MOE_PAD(UT, NTL, NTS)                                                                  \
   do {                                                                                         \
     if (idx64)                                                                                 \
@@ -436,12 +441,13 @@ hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes
                                void *out, void *out_probs, int32_t *dev_status, hipStream_t s) {
   const int64_t units = (int64_t)(out_cap > n_cap ? out_cap : n_cap) * row_units;
   if (units == 0) return hipSuccess;
-  const dim3 grid(copy_blocks(units, kRestoreIlp)), block(kCopyThreads);
+  const int64_t blocks = copy_blocks(units, kRestoreIlp);
+  const dim3 grid = spill_grid(blocks), block(kCopyThreads);
   const auto *pp = static_cast<const uint8_t *>(probs);
   auto *op = static_cast<uint8_t *>(out_probs);
   const bool stream = ((int64_t)out_cap + n_cap) * row_units * unit_bytes > kStreamBytes;
   const RowDiv dv = row_div(row_units);
-  const bool idx64 = (int64_t)grid.x * kCopyThreads * kRestoreIlp >= ((int64_t)1 << 32);
+  const bool idx64 = blocks * kCopyThreads * kRestoreIlp >= ((int64_t)1 << 32);
 #define MOE_RESTORE(UT, NTL, NTS)                                                              \
   do {                                                                                         \
     if (idx64)                                                                                 \

@@ -11,6 +11,23 @@ namespace moe {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
+// A dispatch packet counts its grid in work-items, 32 bits per dimension, so
+// gridDim.x * blockDim.x must stay below 2^32 (beyond it the grid is silently
+// cut short).  Launches of many workgroups therefore spill into gridDim.z:
+// the workgroup index is x + gridDim.x * z, and the last z-slab may hold
+// workgroups past the end, which return at once.
+constexpr unsigned kMaxGridX = 1u << 20;
+
+inline dim3 spill_grid(int64_t blocks, unsigned y = 1) {
+  if (blocks < 1) blocks = 1;
+  const unsigned x = (unsigned)(blocks < (int64_t)kMaxGridX ? blocks : (int64_t)kMaxGridX);
+  return dim3(x, y, (unsigned)((blocks + x - 1) / x));
+}
+
+__device__ __forceinline__ int64_t spill_block() {
+  return (int64_t)blockIdx.x + (int64_t)gridDim.x * blockIdx.z;
+}
+
 // 16 bytes as a native clang vector (the non-temporal builtins need one).
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 

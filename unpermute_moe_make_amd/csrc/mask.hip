@@ -64,7 +64,9 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
     SideRows side, int32_t *__restrict__ dev_status) {
   __shared__ int64_t srow[kSlotChunk];
   __shared__ int szero[kSlotChunk];
-  const int t = blockIdx.x;
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
   const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
   const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
 
@@ -126,7 +128,9 @@ __global__ __launch_bounds__(kRowThreads) void mask_unpermute_kernel(
   __shared__ int64_t srow[kSlotChunk];
   __shared__ float sp[kSlotChunk];
   __shared__ float sup[MOE_MAX_EXPERTS];
-  const int t = blockIdx.x;
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
   const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
   const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
   const bool scatter = unpermuted_probs != nullptr && blockIdx.y == 0;
@@ -212,7 +216,9 @@ __global__ __launch_bounds__(MAXT) void mask_unpermute_bwd_kernel(
   __shared__ int se[kSlotChunk];
   __shared__ float sred[MAXT / kWave][kBatch];
   __shared__ float sdp[MOE_MAX_EXPERTS];
-  const int t = blockIdx.x;
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
   const int64_t pass = (int64_t)blockDim.x * VPT;
   const int64_t stride = pass * gridDim.y;
   const int64_t cfirst = (int64_t)blockIdx.y * pass + threadIdx.x;
@@ -315,7 +321,7 @@ void mask_permute_dispatch(const void *x, const float *probs, const int32_t *map
                            const SideRows &side, int32_t *st, hipStream_t s) {
   RowShape sh = row_shape_vpt(V, 2, kRowThreads);   // as the top-k permute
   if (sh.threads == 0) sh = row_shape(V, true);
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
   const U *xp = static_cast<const U *>(x);
   U *op = static_cast<U *>(out);
 #define MOE_MASK_PERMUTE(VPTV)                                                                 \
@@ -335,7 +341,7 @@ void mask_unpermute_dispatch(const void *in, const float *mp, const float *pp,
                              float *up, int32_t *st, hipStream_t s) {
   using U = typename Bf16Unit<EPV>::T;
   const RowShape sh = row_shape(V, true);
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
   const U *ip = static_cast<const U *>(in);
   U *op = static_cast<U *>(out);
 #define MOE_MASK_UNPERMUTE(VPTV, MERGE)                                                        \
@@ -369,12 +375,12 @@ void mask_unpermute_bwd_dispatch(const void *d_out, const void *fwd_in, const fl
   // unpermute backward.
   const RowShape wide = row_shape_vpt(V, 1, 1024);
   if (wide.threads > kRowThreads) {
-    hipLaunchKernelGGL((mask_unpermute_bwd_kernel<EPV, 1, NT, 1024>), dim3(T, 1),
+    hipLaunchKernelGGL((mask_unpermute_bwd_kernel<EPV, 1, NT, 1024>), spill_grid(T, 1),
                        dim3(wide.threads), 0, s, gp, fp, mp, map, T, V, E, n_rows, dp, dmp, st);
     return;
   }
   const RowShape sh = row_shape(V, dmp == nullptr);
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
 #define MOE_MASK_BWD(VPTV)                                                                      \
   hipLaunchKernelGGL((mask_unpermute_bwd_kernel<EPV, VPTV, NT, kRowThreads>), grid, block, 0, s, \
                      gp, fp, mp, map, T, V, E, n_rows, dp, dmp, st)

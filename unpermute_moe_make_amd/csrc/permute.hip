@@ -79,7 +79,9 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
     int64_t V, int k, int E, int n_rows, U *__restrict__ out, float *__restrict__ out_probs,
     SideRows side, int32_t *__restrict__ dev_status) {
   __shared__ int64_t srow[kMaxTopk];
-  const int t = blockIdx.x;
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
   const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
 
   // The token's own row: issue the loads before resolving the slots.
@@ -127,7 +129,9 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
   using U = typename Unit::T;
   __shared__ int64_t srow[kMaxTopk];
   __shared__ float sp[kMaxTopk];
-  const int t = blockIdx.x;
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
   const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
 
   const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
@@ -211,7 +215,9 @@ __global__ __launch_bounds__(kRowThreads) void combine_ep_kernel(
   __shared__ float sp[kMaxTopk];
   __shared__ int srank[kMaxTopk];
   __shared__ int sorder[kMaxTopk];
-  const int t = blockIdx.x;
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
   const int64_t c0 = (int64_t)blockIdx.y * blockDim.x * VPT + threadIdx.x;
 
   const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
@@ -324,7 +330,9 @@ __global__ __launch_bounds__(MAXT) void combine_bwd_kernel(
   __shared__ int64_t srow[kMaxTopk];
   __shared__ float sp[kMaxTopk];
   __shared__ float sred[MAXT / kWave][KB];
-  const int t = blockIdx.x;
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
   const int64_t pass = (int64_t)blockDim.x * VPT;
   const int64_t stride = pass * gridDim.y;
   const int64_t cfirst = (int64_t)blockIdx.y * pass + threadIdx.x;
@@ -427,7 +435,7 @@ hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *to
   // faster with 128 lanes than with 256)
   RowShape sh = row_shape_vpt(V, MOE_PERMUTE_VPT, kRowThreads);
   if (sh.threads == 0) sh = row_shape(V, true);
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
   const U *xp = static_cast<const U *>(x);
   U *op = static_cast<U *>(out);
 #define MOE_PERMUTE(VPTV)                                                                     \
@@ -448,7 +456,7 @@ void combine_k(const RowShape &sh, int T, const void *in, const float *probs,
                int n_rows, void *out, const float *gsrc, float *gdst, int32_t *st,
                hipStream_t s) {
   using U = typename Bf16Unit<EPV>::T;
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
   const U *ip = static_cast<const U *>(in);
   U *op = static_cast<U *>(out);
 #define MOE_COMBINE(KBV)                                                                     \
@@ -473,7 +481,7 @@ void combine_bwd_k(const RowShape &sh, int T, const void *d_out, const void *fwd
                    int64_t V, int k, int E, int n_rows, void *d_in, float *d_probs, int32_t *st,
                    hipStream_t s) {
   using U = typename Bf16Unit<EPV>::T;
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
   const U *gp = static_cast<const U *>(d_out);
   const U *fp = static_cast<const U *>(fwd_in);
   U *dp = static_cast<U *>(d_in);
@@ -538,7 +546,7 @@ void combine_ep_dispatch(const void *in, const float *probs, const int32_t *topk
   U *op = static_cast<U *>(out);
   // (one unit per lane on up to 1024 lanes was measured slower here)
   const RowShape sh = row_shape(V, true);
-  const dim3 grid(T, sh.ysplit), block(sh.threads);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
 #define MOE_EP(VPTV)                                                                          \
   hipLaunchKernelGGL((combine_ep_kernel<EPV, VPTV, NT, FP64>), grid, block, 0, s,             \
                      ip, probs, topk_idx, row_id_map, T, V, k, E, n_rows, per_rank,           \

@@ -197,7 +197,9 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void topk_softmax_kernel(
   __shared__ uint32_t skey[kGroups][MOE_MAX_TOPK];
   const int grp = threadIdx.x / G;
   const int gl = threadIdx.x % G;
-  const int t = blockIdx.x * kGroups + grp;
+  const int64_t b = spill_block();
+  if (b * kGroups >= T) return;  // a workgroup past the last token
+  const int64_t t = b * kGroups + grp;
   const bool live = t < T;
   const int64_t row = (int64_t)(live ? t : T - 1) * E;
 
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void topk_softmax_bwd_kernel(
   __shared__ float srow[kRouterWaves][MOE_MAX_EXPERTS];
   const int wv = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * kRouterWaves + wv;
+  const int64_t t = spill_block() * kRouterWaves + wv;
   if (t >= T) return;   // whole wave leaves; only wave-level syncs below
   for (int e = lane; e < E; e += kWave) srow[wv][e] = 0.0f;
   // k <= 64: lane j owns slot j
@@ -306,7 +308,7 @@ template <int EB, int G>
 void launch_router_g(const void *logits, int T, int E, int k, int32_t *topk_idx, void *probs,
                      int prob_bytes, hipStream_t s) {
   constexpr int kGroups = kRouterWaves * (kWave / G);
-  const dim3 grid((T + kGroups - 1) / kGroups), block(kRouterWaves * kWave);
+  const dim3 grid = spill_grid((T + kGroups - 1) / kGroups), block(kRouterWaves * kWave);
   const int per = (E + G - 1) / G;
 #define MOE_ROUTER_CASE(P)                                                                 \
   if (per <= P) {                                                                          \
@@ -348,7 +350,8 @@ hipError_t launch_topk_softmax_bwd(const void *d_probs, const void *probs, int p
                                    const int32_t *topk_idx, int T, int E, int k, void *d_logits,
                                    int logit_bytes, int32_t *dev_status, hipStream_t s) {
   if (E > MOE_MAX_EXPERTS || k > kWave) return hipErrorInvalidValue;
-  const dim3 grid((T + kRouterWaves - 1) / kRouterWaves), block(kRouterWaves * kWave);
+  const dim3 grid = spill_grid((T + kRouterWaves - 1) / kRouterWaves),
+             block(kRouterWaves * kWave);
 #define MOE_ROUTER_BWD(PB, OB)                                                              \
   hipLaunchKernelGGL((topk_softmax_bwd_kernel<PB, OB>), grid, block, 0, s, d_probs, probs, \
                      topk_idx, T, E, k, d_logits, dev_status)
