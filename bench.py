@@ -46,6 +46,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip timing the step replayed from a captured hipGraph")
+    ap.add_argument("--no-cold", dest="cold", action="store_false",
+                    help="skip the cold-cache per-op pass (keeps a kernel trace to the "
+                         "warm calls)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB three times "
                          "(a known-size reference for hardware byte counters)")
@@ -132,14 +135,26 @@ def pmc_traffic(workload: str, op: str):
 
 # --------------------------------------------------------------- setup ----
 
+# hipEventDisableSystemFence: recording such an event takes no system-scope
+# fence, i.e. no L2 write-back and invalidate at every marker.  The events
+# here only time work (their results are read after a device synchronize), and
+# without the flag every marker flushes the caches: on the 4096-token step the
+# markers around one op per step cost 6.7 us per step, and an op's event time
+# exceeded its kernel time by 1.6 us.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class HipEvents:
     """Raw HIP events recorded through ctypes: far less host overhead per
     record than torch.cuda.Event, so timing every op does not starve the GPU."""
 
-    def __init__(self):
+    def __init__(self, flags: int = HIP_EVENT_DISABLE_SYSTEM_FENCE):
         import torch  # noqa: F401  (the HIP runtime is already loaded by torch)
         self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.flags = flags
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
@@ -147,8 +162,8 @@ class HipEvents:
 
     def create(self):
         ev = ctypes.c_void_p()
-        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         return ev
 
     def record(self, ev, stream):
@@ -312,13 +327,15 @@ def build_chunks(m, cw):
 # --------------------------------------------------------- CPU baseline ----
 
 def op_stats(times, nbytes):
-    """Mean, median, p10 / p90 of sorted event times (µs) and the rate."""
+    """Mean, median, p10 / p90 of sorted event times (µs) and the rate at the
+    median."""
     n = len(times)
     mean = sum(times) / n
-    return {"us_mean": round(mean, 2), "us_median": round(times[n // 2], 2),
+    med = times[n // 2]
+    return {"us_mean": round(mean, 2), "us_median": round(med, 2),
             "us_p10": round(times[n // 10], 2), "us_p90": round(times[(9 * n) // 10], 2),
-            "bytes": nbytes, "GBps": round(nbytes / (mean * 1e-6) / 1e9, 1),
-            "pct_hbm_peak": round(100 * nbytes / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+            "bytes": nbytes, "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
 
 
 def cpu_baseline(name, w, target_s, step_bytes):
@@ -427,9 +444,10 @@ def main():
     # writes back whatever was dirty, so the op starts from clean, unrelated
     # cache contents.  (A write pass would leave 256 MB of dirty lines whose
     # write-back the op would then pay.)
-    flush = torch.ones(512 << 18, dtype=torch.float32, device="cuda:0")
-    evc = [{n: (hev.create(), hev.create()) for n in names} for _ in range(K2)]
-    for i in range(K2):
+    K3 = K2 if args.cold else 0
+    flush = torch.ones(512 << 18 if K3 else 1, dtype=torch.float32, device="cuda:0")
+    evc = [{n: (hev.create(), hev.create()) for n in names} for _ in range(K3)]
+    for i in range(K3):
         for n, fn, a in step.ops:
             flush.sum()
             hev.record(evc[i][n][0], sv)
@@ -440,7 +458,8 @@ def main():
     torch.cuda.synchronize()
     del flush
     per_op_cold = {n: op_stats(sorted(hev.elapsed_us(evc[i][n][0], evc[i][n][1])
-                                      for i in range(K2)), op_bytes[n]) for n in names}
+                                      for i in range(K3)), op_bytes[n]) for n in names} \
+        if K3 else None
 
     # Timed region: exactly K steps; events only around the dominant op.
     K = args.steps
