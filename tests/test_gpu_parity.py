@@ -141,7 +141,8 @@ def test_row_map_configs(m, name):
                                    (257, 8, 3), (1000, 3, 3), (700, 2048, 8), (300, 64, 9),
                                    (130, 100, 64), (5000, 1, 1), (4097, 257, 7),
                                    (16384, 3, 2), (16385, 8, 2), (70000, 64, 4),
-                                   (300000, 2, 1)])
+                                   (300000, 2, 1), (512, 64, 8), (4096, 2, 1), (683, 9, 6),
+                                   (8, 512, 8), (8, 513, 8), (1024, 4, 4)])
 def test_row_map_edges(m, T, E, k):
     say(f"row_map edge T={T} E={E} k={k}")
     w = workloads.random_routed(T, 8, E, k, seed=T * 31 + E, with_dy=False, zipf_s=0.7)
@@ -149,6 +150,24 @@ def test_row_map_edges(m, T, E, k):
     rm = sentinel_i32((E, T))
     off = sentinel_i32((E + 1,))
     m.moe_make_row_id_map(w.topk_idx.to(DEV), E, row_id_map=rm, expert_offsets=off)
+    assert_bits_equal(rm.cpu().numpy(), ref_map, "row_id_map")
+    assert_bits_equal(off.cpu().numpy(), ref_off, "expert_offsets")
+
+
+@pytest.mark.parametrize("T,E,k", [(16, 32, 4), (300, 64, 6)])
+def test_row_map_unaligned_indices(m, T, E, k):
+    """topk_idx 4 bytes past a 16-byte boundary: the map takes its two-launch
+    form even for short token ranges; same result."""
+    say(f"row_map unaligned topk_idx T={T} E={E} k={k}")
+    w = workloads.random_routed(T, 8, E, k, seed=T + 7, with_dy=False)
+    ref_map, ref_off = oracle.row_id_map(w.topk_idx.numpy(), E)
+    buf = torch.empty(T * k + 4, dtype=torch.int32, device=DEV)
+    idx = buf[1:1 + T * k].view(T, k)
+    idx.copy_(w.topk_idx)
+    assert idx.data_ptr() % 16 == 4
+    rm = sentinel_i32((E, T))
+    off = sentinel_i32((E + 1,))
+    m.moe_make_row_id_map(idx, E, row_id_map=rm, expert_offsets=off)
     assert_bits_equal(rm.cpu().numpy(), ref_map, "row_id_map")
     assert_bits_equal(off.cpu().numpy(), ref_off, "expert_offsets")
 

@@ -37,6 +37,18 @@ constexpr int kWavesPerBlock = kTokPerBlock / kWave;
 constexpr int kFusedMaxBlocks = 64;  // up to 16384 tokens: write derives bases itself
 constexpr int kScanThreads = 256;
 constexpr int kCountBatch = 8;     // topk indices loaded per lane before use
+// One-launch map up to this many (token, slot) entries and experts, and the
+// experts per workgroup there; build-time tuning (every workgroup counts all
+// entries with LDS atomics, which costs more than the second launch it saves
+// beyond about 4096 entries).
+#ifndef MOE_SINGLE_MAX_ENTRIES
+#define MOE_SINGLE_MAX_ENTRIES 4096
+#endif
+constexpr int kSingleMaxEntries = MOE_SINGLE_MAX_ENTRIES;
+constexpr int kSingleMaxExperts = 512;
+#ifndef MOE_SINGLE_EPW
+#define MOE_SINGLE_EPW 4
+#endif
 // Experts per write workgroup: 8 while there are few token blocks (more
 // workgroups to spread the map stores), 16 beyond (less repeated base
 // derivation); chosen by measurement.
@@ -153,6 +165,26 @@ __global__ __launch_bounds__(kScanThreads) void rowmap_colscan_kernel(
   if (threadIdx.x == 0) totals[e] = carry;
 }
 
+// The row_id_map entries of block b's tokens for experts [e0, e0+ne): lane =
+// token; rank in its wave tile = routed tokens below it (mbcnt of the mask).
+template <int EPW>
+__device__ __forceinline__ void write_block_rows(
+    const unsigned long long (*s_mask)[EPW], const int (*s_base)[EPW], int b, int e0, int ne,
+    int T, int32_t *__restrict__ row_id_map) {
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int t = b * kTokPerBlock + tid;
+  if (t >= T) return;
+  for (int i = 0; i < ne; i++) {
+    const unsigned long long m = s_mask[w][i];
+    const unsigned below = __builtin_amdgcn_mbcnt_hi(
+        (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    const int v = ((m >> lane) & 1ull) ? s_base[w][i] + (int)below : -1;
+    row_id_map[(int64_t)(e0 + i) * T + t] = v;
+  }
+}
+
 // FUSED: derive totals and the earlier-block prefix from counts[nb][E];
 // otherwise counts already holds the prefix and totals the expert totals.
 // Grid (nb, ceil(E / EPW)): block (b, y) writes the entries of experts
@@ -213,19 +245,107 @@ __global__ __launch_bounds__(kTokPerBlock) void rowmap_write_kernel(
     }
   }
   __syncthreads();
+  write_block_rows<EPW>(s_mask, s_base, b, e0, ne, T, row_id_map);
+}
 
-  const int w = tid / kWave;
-  const int lane = tid & (kWave - 1);
-  const int t = b * kTokPerBlock + tid;
-  if (t >= T) return;
-  for (int i = 0; i < ne; i++) {
-    const unsigned long long m = s_mask[w][i];
-    // number of routed tokens below this lane in the wave tile
-    const unsigned below = __builtin_amdgcn_mbcnt_hi(
-        (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-    const int v = ((m >> lane) & 1ull) ? s_base[w][i] + (int)below : -1;
-    row_id_map[(int64_t)(e0 + i) * T + t] = v;
+// Short token ranges in one launch: every workgroup stages all T*k indices in
+// LDS (as 16-bit experts) and counts them itself with LDS atomic adds -- the
+// rows of every expert, and the rows of its own experts among the tokens
+// before its block -- while the 64-bit lane masks of its own block give the
+// in-tile ranks as above.  Counts and masks are order-free, so no arrival
+// order decides a row.  Every workgroup reading all the indices is what
+// bounds this path to kSingleMaxEntries.  (kdiv, kshift): floor(f / k) =
+// (umulhi(kdiv, f) + f) >> kshift for every flat index f < 2^32.
+template <int EPW>
+__global__ __launch_bounds__(kTokPerBlock) void rowmap_single_kernel(
+    const int32_t *__restrict__ topk_idx, int T, int k, int E, uint32_t kdiv, int kshift,
+    int32_t *__restrict__ row_id_map, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ dev_status) {
+  extern __shared__ int s_cnt[];                         // [E] counts, then offsets
+  __shared__ uint16_t s_idx[kSingleMaxEntries];          // experts, 0xFFFF = invalid
+  __shared__ int s_pre[EPW];
+  __shared__ int s_base[kWavesPerBlock][EPW];
+  __shared__ unsigned long long s_mask[kWavesPerBlock][EPW];
+  __shared__ int wave_tot[kTokPerBlock / kWave];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int e0 = blockIdx.y * EPW;
+  const int ne = min(EPW, E - e0);
+  const int n = T * k;
+  const int t_blk = b * kTokPerBlock;
+
+  // All 16-byte loads of a lane in flight at once (topk_idx is 16-byte
+  // aligned on this path); the tail of n % 4 entries is read singly.
+  constexpr int kLoads = (kSingleMaxEntries + 4 * kTokPerBlock - 1) / (4 * kTokPerBlock);
+  const v4u *src4 = reinterpret_cast<const v4u *>(topk_idx);
+  const int n4 = n / 4;
+  v4u r[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; i++) {
+    const int q = tid + i * kTokPerBlock;
+    if (q < n4) r[i] = src4[q];
   }
+  for (int e = tid; e < E; e += kTokPerBlock) s_cnt[e] = 0;
+  if (tid < EPW) {
+    s_pre[tid] = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; w++) s_mask[w][tid] = 0ull;
+  }
+  auto expert16 = [E](uint32_t e) -> uint16_t { return e < (uint32_t)E ? (uint16_t)e : 0xFFFF; };
+#pragma unroll
+  for (int i = 0; i < kLoads; i++) {
+    const int q = tid + i * kTokPerBlock;
+    if (q < n4) {
+      s_idx[4 * q] = expert16(r[i].x);
+      s_idx[4 * q + 1] = expert16(r[i].y);
+      s_idx[4 * q + 2] = expert16(r[i].z);
+      s_idx[4 * q + 3] = expert16(r[i].w);
+    }
+  }
+  if (tid < n - 4 * n4) s_idx[4 * n4 + tid] = expert16((uint32_t)topk_idx[4 * n4 + tid]);
+  __syncthreads();
+
+  int bad = 0;
+  for (int f = tid; f < n; f += kTokPerBlock) {
+    const uint32_t e = s_idx[f];
+    if (e == 0xFFFF) {
+      bad |= MOE_DEV_BAD_EXPERT;
+      continue;
+    }
+    atomicAdd(&s_cnt[e], 1);
+    const int ge = (int)e - e0;
+    if ((unsigned)ge < (unsigned)ne) {
+      const int t = (int)(((uint64_t)__umulhi(kdiv, (uint32_t)f) + (uint32_t)f) >> kshift);
+      if (t < t_blk) {
+        atomicAdd(&s_pre[ge], 1);
+      } else if (t < t_blk + kTokPerBlock) {
+        const int tl = t - t_blk;
+        const unsigned long long bit = 1ull << (tl & (kWave - 1));
+        const unsigned long long old = atomicOr(&s_mask[tl / kWave][ge], bit);
+        if (old & bit) bad |= MOE_DEV_DUP_EXPERT;
+      }
+    }
+  }
+  // every workgroup sees every index: the first one reports bad experts,
+  // each reports the repeats it finds in its own block and experts
+  if (b != 0 || blockIdx.y != 0) bad &= ~MOE_DEV_BAD_EXPERT;
+  report(dev_status, bad);
+  __syncthreads();
+  const int total = block_scan_lds(s_cnt, E, wave_tot);
+  if (b == 0 && blockIdx.y == 0) {
+    for (int e = tid; e < E; e += kTokPerBlock) expert_offsets[e] = s_cnt[e];
+    if (tid == 0) expert_offsets[E] = total;
+  }
+  if (tid < ne) {
+    int run = s_cnt[e0 + tid] + s_pre[tid];
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; w++) {
+      s_base[w][tid] = run;
+      run += __popcll(s_mask[w][tid]);
+    }
+  }
+  __syncthreads();
+  write_block_rows<EPW>(s_mask, s_base, b, e0, ne, T, row_id_map);
 }
 
 // ----------------------------------------------------- mask-map (TE) form --
@@ -438,6 +558,21 @@ __global__ void fill_kernel(int32_t *__restrict__ p, int n, int32_t v) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// floor(f / k) = (umulhi(m, f) + f) >> l for every f < 2^32, with
+// l = ceil(log2 k) and m = floor(2^32 (2^l - k) / k) + 1 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication").
+struct KDiv {
+  uint32_t m;
+  int l;
+};
+
+inline KDiv k_div(int k) {
+  int l = 0;
+  while ((1 << l) < k) l++;
+  const uint64_t num = ((uint64_t)1 << 32) * (((uint64_t)1 << l) - (uint64_t)k);
+  return KDiv{(uint32_t)(num / (uint64_t)k + 1), l};
+}
+
 struct Workspace {
   unsigned long long *masks;
   int32_t *counts;
@@ -473,9 +608,18 @@ hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *
     return hipGetLastError();
   }
   const int nb = (T + kTokPerBlock - 1) / kTokPerBlock;
+  const size_t lds_write = (size_t)E * sizeof(int);
+  if ((int64_t)T * k <= kSingleMaxEntries && E <= kSingleMaxExperts &&
+      reinterpret_cast<uintptr_t>(topk_idx) % 16 == 0) {
+    constexpr int epw = MOE_SINGLE_EPW;
+    const KDiv kd = k_div(k);
+    hipLaunchKernelGGL((rowmap_single_kernel<epw>), dim3(nb, (E + epw - 1) / epw),
+                       dim3(kTokPerBlock), lds_write, s, topk_idx, T, k, E, kd.m, kd.l,
+                       row_id_map, expert_offsets, dev_status);
+    return hipGetLastError();
+  }
   const Workspace w = carve(ws, nb, E);
   const size_t lds_count = (size_t)kWavesPerBlock * E * sizeof(unsigned long long);
-  const size_t lds_write = (size_t)E * sizeof(int);
   const bool small = nb <= kSmallBlocks;
   const dim3 wgrid(nb, (E + (small ? 8 : 16) - 1) / (small ? 8 : 16));
   hipLaunchKernelGGL(rowmap_count_kernel, dim3(nb), dim3(kTokPerBlock), lds_count, s, topk_idx,
