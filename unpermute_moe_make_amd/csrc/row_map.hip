@@ -444,6 +444,7 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
     const int32_t *__restrict__ counts, const int32_t *__restrict__ totals, int T, int E,
     int nb, int num_out, int32_t *__restrict__ map, int32_t *__restrict__ expert_offsets) {
   __shared__ int s_off[MOE_MAX_EXPERTS];
+  __shared__ int s_pre[MOE_MAX_EXPERTS];   // rows of the earlier blocks (FUSED)
   __shared__ unsigned long long s_mask[kWavesPerBlock][kMaskChunk];
   __shared__ int s_base[kWavesPerBlock][kMaskChunk];
   __shared__ int wave_tot[kTokPerBlock / kWave];
@@ -452,8 +453,14 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
   for (int e = tid; e < E; e += kTokPerBlock) {
     int tot = 0;
     if (FUSED) {
+      int pre = 0;
 #pragma unroll 16
-      for (int b2 = 0; b2 < nb; b2++) tot += counts[(int64_t)b2 * E + e];
+      for (int b2 = 0; b2 < nb; b2++) {
+        const int c = counts[(int64_t)b2 * E + e];
+        tot += c;
+        pre += (b2 < b) ? c : 0;
+      }
+      s_pre[e] = pre;
     } else {
       tot = totals[e];
     }
@@ -512,13 +519,7 @@ __global__ __launch_bounds__(kTokPerBlock) void maskmap_write_kernel(
     __syncthreads();   // the previous chunk's readers are done
     if (tid < nc) {
       const int e = c0 + tid;
-      int pre = 0;
-      if (FUSED) {
-#pragma unroll 16
-        for (int b2 = 0; b2 < b; b2++) pre += counts[(int64_t)b2 * E + e];
-      } else {
-        pre = counts[(int64_t)b * E + e];
-      }
+      const int pre = FUSED ? s_pre[e] : counts[(int64_t)b * E + e];
       int run = s_off[e] + pre;
 #pragma unroll
       for (int ww = 0; ww < kWavesPerBlock; ww++) {
