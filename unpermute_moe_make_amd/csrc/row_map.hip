@@ -432,6 +432,54 @@ __device__ __forceinline__ uint32_t nonzero_bits(v4u v) {
   return out;
 }
 
+// Masks from a [T][E] routing mask by wave ballots, when every mask row is a
+// whole number of 16-byte vectors on a 16-byte aligned base: lane = token of
+// the wave tile; the lane reads its own row 64 experts at a time as a 64-bit
+// set, and one ballot per expert is that expert's token mask for the tile.
+// All of a lane's loads for a group of 64 experts are in flight together.
+// (Used for up to 64 experts; the loop handles any count.)
+template <int MB>
+__global__ __launch_bounds__(kTokPerBlock) void maskmap_count_ballot_kernel(
+    const void *__restrict__ routing_map, int T, int E, unsigned long long *__restrict__ masks,
+    int32_t *__restrict__ counts) {
+  extern __shared__ int s_cnt[];  // [4][E]
+  constexpr int kPerVec = 16 / MB;         // mask entries per 16-byte vector
+  constexpr int kVecs = kWave / kPerVec;   // vectors per 64 experts
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int t = b * kTokPerBlock + tid;
+  const bool live = t < T;
+  const v4u *row = reinterpret_cast<const v4u *>(static_cast<const uint8_t *>(routing_map) +
+                                                 (int64_t)(live ? t : 0) * E * MB);
+  for (int g0 = 0; g0 < E; g0 += kWave) {
+    const int nv = min(kVecs, (E - g0) / kPerVec);   // E * MB is a multiple of 16
+    v4u v[kVecs];
+#pragma unroll
+    for (int q = 0; q < kVecs; q++)
+      v[q] = (live && q < nv) ? row[g0 / kPerVec + q] : v4u{0u, 0u, 0u, 0u};
+    unsigned long long bits = 0ull;
+#pragma unroll
+    for (int q = 0; q < kVecs; q++)
+      bits |= (unsigned long long)nonzero_bits<MB>(v[q]) << (q * kPerVec);
+    unsigned long long mine = 0ull;
+    const int ng = min(kWave, E - g0);
+    for (int i = 0; i < ng; i++) {
+      const unsigned long long m = __ballot((bits >> i) & 1ull);
+      mine = lane == i ? m : mine;
+    }
+    if (lane < ng) {
+      masks[((int64_t)b * kWavesPerBlock + w) * E + g0 + lane] = mine;
+      s_cnt[w * E + g0 + lane] = __popcll(mine);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kTokPerBlock)
+    counts[(int64_t)b * E + e] =
+        s_cnt[e] + s_cnt[E + e] + s_cnt[2 * E + e] + s_cnt[3 * E + e];
+}
+
 // Per-token map rows.  FUSED as for rowmap_write_kernel.  Each lane owns one
 // token.  Chunk by chunk from the top expert down, the block stages each
 // expert's wave-tile masks and row bases in LDS; the lane reads its own
@@ -657,22 +705,29 @@ hipError_t launch_maskmap(const void *routing_map, int mask_bytes, int T, int E,
   // Vector loads of 4 entries when rows allow them.
   const uintptr_t a = reinterpret_cast<uintptr_t>(routing_map);
   const bool vec = E % 4 == 0 && a % (4 * (uintptr_t)mask_bytes) == 0;
+  // Each lane's mask row is read in 16-byte vectors when every row starts
+  // 16-byte aligned.
+  const bool rvec = ((int64_t)E * mask_bytes) % 16 == 0 && a % 16 == 0;
 #define MOE_MASK_COUNT(MB, V)                                                                 \
   hipLaunchKernelGGL((maskmap_count_kernel<MB, V>), dim3(nb), dim3(kTokPerBlock), lds_count, s, \
                      routing_map, T, E, w.masks, w.counts)
+#define MOE_MASK_BALLOT(MB)                                                                   \
+  hipLaunchKernelGGL((maskmap_count_ballot_kernel<MB>), dim3(nb), dim3(kTokPerBlock),         \
+                     lds_count, s, routing_map, T, E, w.masks, w.counts)
+  // Ballots for up to 64 experts (one ballot per expert; beyond that the
+  // expert-per-lane walk over the tile's tokens was measured faster).
+  const bool ballot = rvec && E <= kWave;
   if (mask_bytes == 4) {
-    if (vec) MOE_MASK_COUNT(4, 4); else MOE_MASK_COUNT(4, 1);
+    if (ballot) MOE_MASK_BALLOT(4); else if (vec) MOE_MASK_COUNT(4, 4); else MOE_MASK_COUNT(4, 1);
   } else {
-    if (vec) MOE_MASK_COUNT(1, 4); else MOE_MASK_COUNT(1, 1);
+    if (ballot) MOE_MASK_BALLOT(1); else if (vec) MOE_MASK_COUNT(1, 4); else MOE_MASK_COUNT(1, 1);
   }
+#undef MOE_MASK_BALLOT
 #undef MOE_MASK_COUNT
   const bool fused = nb <= kFusedMaxBlocks;
   if (!fused)
     hipLaunchKernelGGL(rowmap_colscan_kernel, dim3(E), dim3(kScanThreads), 0, s, w.counts, nb,
                        E, w.totals);
-  // Each lane's mask row is read in 16-byte vectors when every row starts
-  // 16-byte aligned.
-  const bool rvec = ((int64_t)E * mask_bytes) % 16 == 0 && a % 16 == 0;
 #define MOE_MASK_WRITE(F, MB, VC)                                                              \
   hipLaunchKernelGGL((maskmap_write_kernel<F, MB, VC>), dim3(nb), dim3(kTokPerBlock), 0, s,     \
                      routing_map, w.masks, w.counts, w.totals, T, E, nb, num_out, map,         \
