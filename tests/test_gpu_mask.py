@@ -100,11 +100,12 @@ def test_mask_map_configs(m, name, dtype):
 @pytest.mark.parametrize("T,E,density,num_out", [
     (1, 1, 1.0, -1), (63, 5, 0.5, -1), (257, 7, 0.3, -1), (300, 160, 0.6, -1),
     (100, 2048, 0.05, -1), (20000, 16, 0.25, -1), (1000, 64, 0.2, 5000), (1000, 64, 0.2, 0),
-    (500, 33, 0.9, 100000), (17000, 8, 0.5, 30000)])
+    (500, 33, 0.9, 100000), (17000, 8, 0.5, 30000), (1024, 64, 0.3, -1),
+    (1025, 64, 0.3, 20000), (700, 48, 0.5, 1000), (16, 64, 1.0, -1), (1024, 16, 0.0, -1)])
 @pytest.mark.parametrize("dtype", [torch.uint8, torch.int32])
 def test_mask_map_shapes_and_dropping(m, T, E, density, num_out, dtype):
     """Tokens routed to more than 64 experts, E not a multiple of 4, over 64
-    token blocks (the column-scan path), and dropping."""
+    token blocks (the column-scan path), empty masks, and dropping."""
     say(f"mask map T={T} E={E} d={density} num_out={num_out} {dtype}")
     mask = random_mask(T, E, density, seed=T + E)
     got, off = build_map(m, mask.to(dtype).to(DEV), num_out)
