@@ -106,20 +106,44 @@ __device__ inline ChunkTables carve_tables(void *lds, int C, int G) {
   return t;
 }
 
-// Exclusive scan across the 64 lanes of one wave; *total gets the sum.
+// Lane l - S of the same 16-lane row (DPP row_shr:S), or 0 when that lane is
+// in an earlier row.  Needs every lane of the wave active.
+template <int S>
+__device__ __forceinline__ int64_t row_shr64(int64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x110 + S, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x110 + S, 0xF, 0xF,
+                                             false);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Exclusive scan across the 64 lanes of one wave (all active); *total gets
+// the sum.  A scan inside each 16-lane row by DPP row shifts (1, 2, 4, 8),
+// then the totals of the earlier rows (lanes 15, 31, 47) added: DPP moves
+// and four lane reads instead of a chain of cross-lane permutes through LDS.
 __device__ __forceinline__ int64_t wave_exclusive_scan(int64_t v, int64_t *total) {
-  const int lane = threadIdx.x & (kWave - 1);
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
   int64_t incl = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int64_t u = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += u;
-  }
-  *total = __shfl(incl, kWave - 1, kWave);
+  incl += row_shr64<1>(incl);
+  incl += row_shr64<2>(incl);
+  incl += row_shr64<4>(incl);
+  incl += row_shr64<8>(incl);
+  const int64_t r0 = readlane64(incl, 15), r1 = readlane64(incl, 31);
+  const int64_t r2 = readlane64(incl, 47), r3 = readlane64(incl, 63);
+  incl += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+  *total = r0 + r1 + r2 + r3;
   return incl - v;
 }
 
+// OR of v over the wave (all lanes active).  Status bits are almost always
+// zero, which one ballot shows; otherwise a butterfly of cross-lane permutes.
 __device__ __forceinline__ int wave_or(int v) {
+  if (__ballot(v != 0) == 0ull) return 0;
 #pragma unroll
   for (int d = kWave / 2; d >= 1; d >>= 1) v |= __shfl_xor(v, d, kWave);
   return v;
@@ -309,14 +333,15 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
 
 // --------------------------------------------------------------- restore --
 
-// Token total of the chunk metadata, summed by one wave (every lane gets it).
+// Token total of the chunk metadata, summed by one wave (every lane gets it;
+// all lanes of the wave active).
 __device__ __forceinline__ int64_t wave_total(const int32_t *__restrict__ sizes, int C) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t s = 0;
   for (int i = lane; i < C; i += kWave) s += sizes[i];
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d, kWave);
-  return s;
+  int64_t total;
+  wave_exclusive_scan(s, &total);
+  return total;
 }
 
 // Flat index over [0, max(out_cap, n_cap)) x W: unit (i, c) scatters padded

@@ -143,12 +143,25 @@ __device__ __forceinline__ void copy_side_row(const SideRows &s, int64_t from, i
   }
 }
 
-// Wave-wide fp32 sum by butterfly exchanges; every lane gets the total.
-// The exchange pattern is fixed, so the result is reproducible.
+// Wave-wide fp32 sum (every lane of the wave active); every lane gets the
+// total.  DPP row permutes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror) leave each lane of a 16-lane row holding the
+// row's sum, then the four row sums are added in a fixed order: register
+// moves and four lane reads instead of a chain of cross-lane permutes
+// through LDS.  The pattern is fixed, so the result is reproducible.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
 }  // namespace moe
