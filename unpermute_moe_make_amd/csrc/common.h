@@ -156,6 +156,24 @@ __device__ __forceinline__ float dpp_f32(float v) {
 __device__ __forceinline__ float readlane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
+// Inclusive scan of an int across the wave (every lane active): DPP row
+// shifts by 1, 2, 4, 8 inside each 16-lane row (a lane whose source is in an
+// earlier row adds 0), then the totals of the earlier rows (lanes 15, 31, 47).
+template <int S>
+__device__ __forceinline__ int row_shr_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x110 + S, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  v += row_shr_i32<1>(v);
+  v += row_shr_i32<2>(v);
+  v += row_shr_i32<4>(v);
+  v += row_shr_i32<8>(v);
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);

@@ -121,12 +121,7 @@ __device__ int block_scan_lds(int *a, int n, int *wave_tot) {
   for (int i = beg; i < end; i++) sum += a[i];
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
-  int incl = sum;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int v = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += v;
-  }
+  const int incl = wave_inclusive_scan(sum);
   __syncthreads();
   if (lane == kWave - 1) wave_tot[w] = incl;
   __syncthreads();
