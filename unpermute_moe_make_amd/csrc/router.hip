@@ -50,6 +50,11 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
+// Lane `l`'s value (a 64-lane group combines its four row results this way).
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
 template <int G>
 __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   v = max(v, dpp<kDppQuadXor1>(v));
@@ -57,8 +62,7 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   v = max(v, dpp<kDppHalfMirror>(v));
   v = max(v, dpp<kDppMirror>(v));
   if constexpr (G == 64) {
-    v = max(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
-    v = max(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
+    v = max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
   }
   return v;
 }
@@ -70,8 +74,7 @@ __device__ __forceinline__ uint32_t group_min(uint32_t v) {
   v = min(v, dpp<kDppHalfMirror>(v));
   v = min(v, dpp<kDppMirror>(v));
   if constexpr (G == 64) {
-    v = min(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
-    v = min(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
+    v = min(min(lane_u32(v, 0), lane_u32(v, 16)), min(lane_u32(v, 32), lane_u32(v, 48)));
   }
   return v;
 }
@@ -83,8 +86,7 @@ __device__ __forceinline__ float group_sum(float v) {
   v += __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v)));
   v += __uint_as_float(dpp<kDppMirror>(__float_as_uint(v)));
   if constexpr (G == 64) {
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
+    v = (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
   }
   return v;
 }
@@ -96,8 +98,7 @@ __device__ __forceinline__ uint32_t group_sum_u32(uint32_t v) {
   v += dpp<kDppHalfMirror>(v);
   v += dpp<kDppMirror>(v);
   if constexpr (G == 64) {
-    v += (uint32_t)__shfl_xor((int)v, 16, kWave);
-    v += (uint32_t)__shfl_xor((int)v, 32, kWave);
+    v = (lane_u32(v, 0) + lane_u32(v, 16)) + (lane_u32(v, 32) + lane_u32(v, 48));
   }
   return v;
 }
