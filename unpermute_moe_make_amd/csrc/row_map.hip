@@ -34,7 +34,17 @@ namespace {
 
 constexpr int kTokPerBlock = 256;  // 4 waves x 64 tokens
 constexpr int kWavesPerBlock = kTokPerBlock / kWave;
-constexpr int kFusedMaxBlocks = 64;  // up to 16384 tokens: write derives bases itself
+// Build-time tuning: token blocks up to which the write kernel derives its
+// bases itself (16384 tokens), and experts per write workgroup beyond 32
+// blocks (measured: 16 and 32 alike at 16384 tokens, 64 slower).
+#ifndef MOE_FUSED_MAX_BLOCKS
+#define MOE_FUSED_MAX_BLOCKS 64
+#endif
+#ifndef MOE_WRITE_EPW_LARGE
+#define MOE_WRITE_EPW_LARGE 16
+#endif
+constexpr int kFusedMaxBlocks = MOE_FUSED_MAX_BLOCKS;
+constexpr int kWriteEpwLarge = MOE_WRITE_EPW_LARGE;
 constexpr int kScanThreads = 256;
 constexpr int kCountBatch = 8;     // topk indices loaded per lane before use
 // One-launch map up to this many (token, slot) entries and experts, and the
@@ -665,7 +675,8 @@ hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *
   const Workspace w = carve(ws, nb, E);
   const size_t lds_count = (size_t)kWavesPerBlock * E * sizeof(unsigned long long);
   const bool small = nb <= kSmallBlocks;
-  const dim3 wgrid(nb, (E + (small ? 8 : 16) - 1) / (small ? 8 : 16));
+  const int epw = small ? 8 : kWriteEpwLarge;
+  const dim3 wgrid(nb, (E + epw - 1) / epw);
   hipLaunchKernelGGL(rowmap_count_kernel, dim3(nb), dim3(kTokPerBlock), lds_count, s, topk_idx,
                      T, k, E, w.masks, w.counts, dev_status);
   if (nb <= kFusedMaxBlocks) {
@@ -673,12 +684,14 @@ hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *
       hipLaunchKernelGGL((rowmap_write_kernel<true, 8>), wgrid, dim3(kTokPerBlock), lds_write, s,
                          w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
     else
-      hipLaunchKernelGGL((rowmap_write_kernel<true, 16>), wgrid, dim3(kTokPerBlock), lds_write,
+      hipLaunchKernelGGL((rowmap_write_kernel<true, kWriteEpwLarge>), wgrid, dim3(kTokPerBlock),
+                         lds_write,
                          s, w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
   } else {
     hipLaunchKernelGGL(rowmap_colscan_kernel, dim3(E), dim3(kScanThreads), 0, s, w.counts, nb,
                        E, w.totals);
-    hipLaunchKernelGGL((rowmap_write_kernel<false, 16>), wgrid, dim3(kTokPerBlock), lds_write, s,
+    hipLaunchKernelGGL((rowmap_write_kernel<false, kWriteEpwLarge>), wgrid, dim3(kTokPerBlock),
+                       lds_write, s,
                        w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
   }
   return hipGetLastError();
