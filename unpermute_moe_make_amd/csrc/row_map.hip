@@ -685,14 +685,14 @@ hipError_t launch_rowmap(const int32_t *topk_idx, int T, int k, int E, int32_t *
                          w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
     else
       hipLaunchKernelGGL((rowmap_write_kernel<true, kWriteEpwLarge>), wgrid, dim3(kTokPerBlock),
-                         lds_write,
-                         s, w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
+                         lds_write, s, w.masks, w.counts, w.totals, T, E, nb, row_id_map,
+                         expert_offsets);
   } else {
     hipLaunchKernelGGL(rowmap_colscan_kernel, dim3(E), dim3(kScanThreads), 0, s, w.counts, nb,
                        E, w.totals);
     hipLaunchKernelGGL((rowmap_write_kernel<false, kWriteEpwLarge>), wgrid, dim3(kTokPerBlock),
-                       lds_write, s,
-                       w.masks, w.counts, w.totals, T, E, nb, row_id_map, expert_offsets);
+                       lds_write, s, w.masks, w.counts, w.totals, T, E, nb, row_id_map,
+                       expert_offsets);
   }
   return hipGetLastError();
 }
