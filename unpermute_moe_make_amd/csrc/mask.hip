@@ -340,6 +340,7 @@ void mask_unpermute_dispatch(const void *in, const float *mp, const float *pp,
                              const int32_t *map, int T, int64_t V, int E, int n_rows, void *out,
                              float *up, int32_t *st, hipStream_t s) {
   using U = typename Bf16Unit<EPV>::T;
+  // (two units per lane on 128 lanes was measured 6% slower for 4 KiB rows)
   const RowShape sh = row_shape(V, true);
   const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
   const U *ip = static_cast<const U *>(in);

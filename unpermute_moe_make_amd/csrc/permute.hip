@@ -507,8 +507,7 @@ void combine_dispatch(const void *in, const float *probs, const int32_t *topk_id
                       void *out, const float *gsrc, float *gdst, int32_t *st, hipStream_t s) {
   // two units per lane when a row fits one pass, as in the permute (measured:
   // the 4 KiB-row unpermute and permute backward 2% faster than 256 x 1)
-  RowShape sh = row_shape_vpt(V, 2, kRowThreads);
-  if (sh.threads == 0) sh = row_shape(V, true);
+  const RowShape sh = gather_shape(V);
   switch (sh.vpt) {
     case 1: combine_k<EPV, 1, NTM>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
     case 2: combine_k<EPV, 2, NTM>(sh, T, in, probs, topk_idx, row_id_map, V, k, E, n_rows, out, gsrc, gdst, st, s); break;
@@ -547,7 +546,8 @@ void combine_ep_dispatch(const void *in, const float *probs, const int32_t *topk
   using U = typename Bf16Unit<EPV>::T;
   const U *ip = static_cast<const U *>(in);
   U *op = static_cast<U *>(out);
-  // (one unit per lane on up to 1024 lanes was measured slower here)
+  // (one unit per lane on up to 1024 lanes, and two units per lane on 128
+  // lanes for 4 KiB rows, were measured slower here)
   const RowShape sh = row_shape(V, true);
   const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
 #define MOE_EP(VPTV)                                                                          \

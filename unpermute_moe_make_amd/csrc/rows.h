@@ -35,6 +35,12 @@ inline RowShape row_shape_vpt(int64_t V, int vpt, int max_threads) {
   return RowShape{(int)th, vpt, 1};
 }
 
+// Shape of the combine (unpermute, permute backward): two units per lane
+// when the row fits one pass of up to kRowThreads lanes, else row_shape.
+#ifndef MOE_GATHER_VPT
+#define MOE_GATHER_VPT 2
+#endif
+
 // One workgroup per token row (slice): cover V units with `threads` lanes of
 // `vpt` units each, preferring the least idle lanes, then mid-size groups.
 inline RowShape row_shape(int64_t V, bool allow_split) {
@@ -63,6 +69,12 @@ inline RowShape row_shape(int64_t V, bool allow_split) {
     }
   }
   return best;
+}
+
+inline RowShape gather_shape(int64_t V) {
+  RowShape sh = row_shape_vpt(V, MOE_GATHER_VPT, kRowThreads);
+  if (sh.threads == 0) sh = row_shape(V, true);
+  return sh;
 }
 
 }  // namespace moe
