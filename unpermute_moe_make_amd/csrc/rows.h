@@ -11,6 +11,9 @@
 #ifndef MOE_ROW_VPT
 #define MOE_ROW_VPT 0
 #endif
+#ifndef MOE_GATHER_VPT
+#define MOE_GATHER_VPT 2
+#endif
 
 namespace moe {
 
@@ -34,12 +37,6 @@ inline RowShape row_shape_vpt(int64_t V, int vpt, int max_threads) {
   if (th > max_threads) return RowShape{0, 0, 0};
   return RowShape{(int)th, vpt, 1};
 }
-
-// Shape of the combine (unpermute, permute backward): two units per lane
-// when the row fits one pass of up to kRowThreads lanes, else row_shape.
-#ifndef MOE_GATHER_VPT
-#define MOE_GATHER_VPT 2
-#endif
 
 // One workgroup per token row (slice): cover V units with `threads` lanes of
 // `vpt` units each, preferring the least idle lanes, then mid-size groups.
@@ -71,6 +68,9 @@ inline RowShape row_shape(int64_t V, bool allow_split) {
   return best;
 }
 
+// Shape of the combine (unpermute, permute backward): MOE_GATHER_VPT (two)
+// units per lane when the row fits one pass of up to kRowThreads lanes, else
+// row_shape.
 inline RowShape gather_shape(int64_t V) {
   RowShape sh = row_shape_vpt(V, MOE_GATHER_VPT, kRowThreads);
   if (sh.threads == 0) sh = row_shape(V, true);
