@@ -4,16 +4,16 @@
 //
 // Map.  Wave 0 of every map workgroup rebuilds the small chunk tables in LDS
 // from the device-resident split sizes and chunk order -- input-order source
-// offsets, sorted-order prefixes, padded group starts -- with cross-lane
-// shuffle scans and no workgroup barrier, so the build costs a few hundred
-// cycles after the metadata loads.  The workgroup then writes its slice of
+// offsets, sorted-order prefixes, padded group starts -- with wave scans (DPP
+// row shifts and lane reads) and no workgroup barrier, so the build costs a
+// few hundred cycles after the metadata loads.  The workgroup then writes its slice of
 // the padded destination -> source row map by two binary searches per row.
 // Every workgroup validates the metadata the same way; on bad metadata the
 // whole map is -1 (so the copies write zeros) and workgroup 0 reports it.
 //
 // Copies.  Both walk a flat index over (row, unit) with 16-byte units where
-// the row allows, consecutive lanes on consecutive units, several units per
-// lane loaded before any is stored.  The pad copy writes every destination
+// the row allows, consecutive lanes on consecutive units, each lane's units
+// (one in the pad copy, three in the restore) loaded before any is stored.  The pad copy writes every destination
 // row (zeros where the map is -1).  The restore scatters every mapped row
 // back to its source and writes zeros to the rows past the token total,
 // which it sums from the split sizes on the device.
@@ -150,8 +150,8 @@ __device__ __forceinline__ int wave_or(int v) {
 }
 
 // Built by ONE wave (call from all 64 lanes of wave 0): each lane owns a
-// contiguous segment of chunks and of groups, scans run across lanes with
-// shuffles, and lanes exchange table entries through LDS ordered by
+// contiguous segment of chunks and of groups, scans run across lanes, and
+// lanes exchange table entries through LDS ordered by
 // wave-level fences -- no workgroup barrier inside.  Returns the device
 // status bits (the same value in every lane); non-zero means the tables
 // must not be used.
