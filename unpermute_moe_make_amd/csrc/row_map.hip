@@ -24,6 +24,8 @@
 //   earlier blocks would grow quadratically, so a column-scan kernel (one
 //   workgroup per expert, a parallel scan over the blocks) computes the
 //   bases once and the write kernel reads them: three launches.
+//   With few entries (up to 4096 token slots) one launch does it all: each
+//   workgroup counts every index itself (rowmap_single_kernel).
 #include <type_traits>
 
 #include "common.h"
