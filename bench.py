@@ -102,6 +102,17 @@ OP_KERNELS = {
     "sort_chunks_and_pad": ["chunk_map_kernel", "pad_copy_kernel"],
     "unpad_and_restore": ["restore_copy_kernel"],
 }
+# Padded buffers up to this size are written by one launch that also builds
+# the map (the library's threshold for fusing the two).
+FUSED_PAD_MAX_BYTES = 128 << 20
+
+
+def op_kernels(op, cfg):
+    """Kernels that op launches for the workload configuration cfg."""
+    if op == "sort_chunks_and_pad" and cfg.get("out_cap", 0) * cfg.get("H", 0) * 2 <= \
+            FUSED_PAD_MAX_BYTES:
+        return ["pad_fused_kernel"]
+    return OP_KERNELS[op]
 
 
 def kernel_source_hash() -> str:
@@ -503,7 +514,7 @@ def main():
         "step_bytes": step_bytes,
         "per_op": per_op,
         "per_op_cold": per_op_cold,
-        "roofline": {"bound": "hbm", "kernel": dom, "kernels": OP_KERNELS[dom],
+        "roofline": {"bound": "hbm", "kernel": dom, "kernels": op_kernels(dom, cfg),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "us_per_launch": round(dom_us, 2),
                      "bytes_per_launch": op_bytes[dom],

@@ -593,10 +593,15 @@ def test_chunks_configs(m, name):
 
 @pytest.mark.parametrize("case", ["fp32_tokens", "fp16_probs", "odd_hidden", "align1_identity",
                                   "empty_group", "short_total", "big_cap", "all_empty",
-                                  "h1536", "h7168", "h7000_fp32"])
+                                  "h1536", "h7168", "h7000_fp32", "wide_two_launch",
+                                  "tall_one_launch"])
 def test_chunk_edges(m, case):
     say(f"chunk edge {case}")
     kw = dict(N=3000, seed=50, H=256, num_ranks=4, num_experts=6, align=16, num_empty=5)
+    if case == "wide_two_launch":      # a 143 MB padded buffer: map and copy launched apart
+        kw.update(N=2100, H=32768)
+    if case == "tall_one_launch":      # 140000 short rows: 64 rows per fused workgroup
+        kw.update(N=140000, H=64)
     if case == "fp32_tokens":
         kw["dtype"] = torch.float32
     if case == "odd_hidden":

@@ -430,14 +430,12 @@ MOE_PERM_API int moe_sort_chunks_and_pad(const void *in, const void *probs, int 
   if (!aligned(split_sizes, 4) || !aligned(sorted_idx, 4) || !aligned(row_map, 4) ||
       !aligned(padded_offsets, 4) || !aligned(dev_status, 4))
     return MOE_ERR_ALIGN;
-  hipError_t e = moe::launch_chunk_map(split_sizes, sorted_idx, C, R, align, n_cap, out_cap,
-                                       row_map, padded_offsets, dev_status, stream);
-  if (e != hipSuccess) return MOE_ERR_HIP;
   const int unit = chunk_unit(elem_bytes, H, in, out);
   const int64_t row_units = (int64_t)H * elem_bytes / unit;
-  return hip_status(moe::launch_pad_copy(in, out_probs ? probs : nullptr, prob_bytes, unit,
-                                         row_units, n_cap, row_map, out_cap, out, out_probs,
-                                         dev_status, stream));
+  return hip_status(moe::launch_sort_and_pad(in, out_probs ? probs : nullptr, prob_bytes, unit,
+                                             row_units, split_sizes, sorted_idx, C, R, align,
+                                             n_cap, out_cap, out, out_probs, row_map,
+                                             padded_offsets, dev_status, stream));
 }
 
 namespace {

@@ -38,13 +38,24 @@ namespace {
 #ifndef MOE_RESTORE_STREAM
 #define MOE_RESTORE_STREAM 1
 #endif
+#ifndef MOE_FUSED_MAX_BYTES
+#define MOE_FUSED_MAX_BYTES (128ll << 20)
+#endif
+#ifndef MOE_FUSED_ILP
+#define MOE_FUSED_ILP 2
+#endif
+#ifndef MOE_FUSED_WGS
+#define MOE_FUSED_WGS 2048
+#endif
 #ifndef MOE_COPY_THREADS
 #define MOE_COPY_THREADS 256
 #endif
 constexpr int kCopyThreads = MOE_COPY_THREADS;
 constexpr int kPadIlp = MOE_PAD_ILP;
 constexpr int kRestoreIlp = MOE_RESTORE_ILP;
+constexpr int kFusedIlp = MOE_FUSED_ILP;
 constexpr int kMapRows = 256;         // row_map entries per map workgroup (one per lane)
+constexpr int kMetaBatch = 4;         // chunk metadata loads in flight per lane
 
 // Row / unit split of a flat unit index u over rows of W units without a
 // hardware divide: q = floor(u / W) = (umulhi(m, u) + u) >> l, with
@@ -164,17 +175,33 @@ __device__ int build_chunk_tables_wave(const int32_t *__restrict__ split_sizes,
   const int c0 = min(C, lane * per), c1 = min(C, c0 + per);
   int bad = 0;
   int64_t seg = 0;
-  for (int c = c0; c < c1; c++) {
-    int s = split_sizes[c];
-    const int o = sorted_idx[c];
-    if (s < 0) bad |= MOE_DEV_BAD_CHUNKS;
-    if (s > n_cap) bad |= MOE_DEV_OVERFLOW;
-    if ((unsigned)o >= (unsigned)C) bad |= MOE_DEV_BAD_CHUNKS;
-    s = max(s, 0);
-    t.size[c] = s;
-    t.order[c] = o;
-    t.seen[c] = 0;
-    seg += s;
+  // the metadata loads of kMetaBatch chunks are all issued before the first
+  // is used: one memory round trip per batch
+  for (int cb = c0; cb < c1; cb += kMetaBatch) {
+    int sz[kMetaBatch], od[kMetaBatch];
+#pragma unroll
+    for (int b = 0; b < kMetaBatch; b++) {
+      const int c = min(cb + b, c1 - 1);
+      sz[b] = split_sizes[c];
+      od[b] = sorted_idx[c];
+    }
+#pragma unroll
+    for (int b = 0; b < kMetaBatch; b++) {
+      // the checks use the loads outside the branch, which keeps the
+      // compiler from sinking a load into it (and so behind the first use)
+      const int c = cb + b;
+      const bool in = c < c1;
+      const int s = in ? sz[b] : 0, o = in ? od[b] : 0;
+      if (s < 0) bad |= MOE_DEV_BAD_CHUNKS;
+      if (s > n_cap) bad |= MOE_DEV_OVERFLOW;
+      if ((unsigned)o >= (unsigned)C) bad |= MOE_DEV_BAD_CHUNKS;
+      seg += max(s, 0);
+      if (in) {
+        t.size[c] = max(s, 0);
+        t.order[c] = o;
+        t.seen[c] = 0;
+      }
+    }
   }
   __syncwarp();
   for (int q = c0; q < c1; q++) {
@@ -211,8 +238,10 @@ __device__ int build_chunk_tables_wave(const int32_t *__restrict__ split_sizes,
   const int g0 = min(G, lane * perg), g1 = min(G, g0 + perg);
   int64_t gseg = 0;
   for (int g = g0; g < g1; g++) {
-    const int64_t n = (int64_t)t.qoff[(g + 1) * R] - t.qoff[g * R];
-    const int64_t padded = ((n + A - 1) / A) * A;
+    // n and A are non-negative int32 (qoff never decreases), so n + A - 1
+    // fits 32 unsigned bits and the division needs no 64-bit routine
+    const uint32_t n = (uint32_t)(t.qoff[(g + 1) * R] - t.qoff[g * R]);
+    const int64_t padded = (int64_t)((n + (uint32_t)A - 1u) / (uint32_t)A) * A;
     t.g_pad[g] = padded;
     gseg += padded;
   }
@@ -329,6 +358,139 @@ __global__ __launch_bounds__(kCopyThreads) void pad_copy_kernel(
     if (u < total) st_row<NTS>(v[i], out + u);
   }
   report(dev_status, bad);
+}
+
+// Buffer accesses: the descriptor holds a base and a length in bytes, and
+// the hardware drops a store, and returns zero for a load, whose offset is
+// past the length -- a tail lane or a padding row needs no branch and no
+// select on loaded data.  Descriptor word 3 is the gfx9 data format field
+// (32-bit data) that raw buffer accesses expect.
+constexpr int kBufWord3 = 0x00020000;
+constexpr uint32_t kNoRow = 0xFFFFFFF0u;  // an offset past every descriptor's length
+constexpr int64_t kMaxBufBytes = kNoRow;  // lengths stay at or below it
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, kBufWord3);
+}
+
+template <bool NT, typename U> __device__ __forceinline__ U buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ v4u buf_load<false, v4u>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ v4u buf_load<true, v4u>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+template <> __device__ __forceinline__ uint32_t buf_load<false, uint32_t>(__amdgpu_buffer_rsrc_t r,
+                                                                        uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ uint16_t buf_load<false, uint16_t>(__amdgpu_buffer_rsrc_t r,
+                                                                        uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+template <bool NT>
+__device__ __forceinline__ void buf_store(v4u v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, NT ? 2 : 0);
+}
+template <bool NT>
+__device__ __forceinline__ void buf_store(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, NT ? 2 : 0);
+}
+template <bool NT>
+__device__ __forceinline__ void buf_store(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, NT ? 2 : 0);
+}
+
+// Map and pad copy in one launch, for calls small enough that the saved
+// launch outweighs rebuilding the tables in every workgroup.  Workgroup b
+// owns destination rows [b * rows_per, (b + 1) * rows_per), rows_per <=
+// kWave: wave 0 builds the tables, resolves the slice's source rows into LDS
+// (writing them to row_map and copying their probs), and after one barrier
+// the whole workgroup copies the slice's units in stages of kFusedIlp units
+// per lane.  The loads of stage j + 1 are issued before the stores of stage
+// j, and every access is unconditional (a tail lane re-reads the slice's last
+// unit and stores past the slice, a padding row loads zeros through an
+// offset past the source), so the wait for a stage's loads never waits for
+// the stores issued just before them.  Workgroup 0 also writes
+// padded_offsets and reports bad metadata.  Needs a slice shorter than 2^31
+// bytes and a source of at most kMaxBufBytes.
+template <typename U, bool NTL, bool NTS>
+__global__ __launch_bounds__(kCopyThreads) void pad_fused_kernel(
+    const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, RowDiv dv,
+    const int32_t *__restrict__ split_sizes, const int32_t *__restrict__ sorted_idx, int C, int R,
+    int A, int n_cap, int out_cap, int rows_per, U *__restrict__ out,
+    uint8_t *__restrict__ out_probs, int32_t *__restrict__ row_map,
+    int32_t *__restrict__ padded_offsets, int32_t *__restrict__ dev_status) {
+  extern __shared__ int64_t lds[];
+  __shared__ int32_t s_src[kWave];
+  const int G = C / R;
+  const ChunkTables t = carve_tables(lds, C, G);
+  const int64_t blk = spill_block();
+  const int64_t d0 = blk * rows_per;
+  const int n_rows = (int)max((int64_t)0, min((int64_t)rows_per, (int64_t)out_cap - d0));
+  if (threadIdx.x < kWave) {
+    const int bad = build_chunk_tables_wave(split_sizes, sorted_idx, C, R, A, n_cap, out_cap, t);
+    if (blk == 0) {
+      if (threadIdx.x == 0) report(dev_status, bad);
+      for (int g = threadIdx.x; g <= G; g += kWave) padded_offsets[g] = bad ? 0 : (int32_t)t.g_pad[g];
+    }
+    if ((int)threadIdx.x < n_rows) {
+      const int64_t d = d0 + threadIdx.x;
+      const int32_t s = bad ? -1 : chunk_src_row(t, G, R, d);
+      s_src[threadIdx.x] = s;
+      row_map[d] = s;
+      if (out_probs != nullptr) copy_prob(probs, s, out_probs, d, prob_bytes);
+    }
+  }
+  __syncthreads();
+  const int64_t W = dv.W;
+  const int n_units = (int)(n_rows * W);
+  if (n_units == 0) return;
+  constexpr int kStep = kCopyThreads * kFusedIlp;
+  const int n_stages = (n_units + kStep - 1) / kStep;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t src = slice_rsrc(const_cast<U *>(in),
+                                                (uint32_t)((int64_t)n_cap * W * sizeof(U)));
+  const __amdgpu_buffer_rsrc_t dst = slice_rsrc(out + d0 * W, (uint32_t)n_units * sizeof(U));
+  auto load_stage = [&](int j, U (&w)[kFusedIlp]) {
+#pragma unroll
+    for (int i = 0; i < kFusedIlp; i++) {
+      const int u = min(j * kStep + i * kCopyThreads + tid, n_units - 1);
+      int64_t r, c;
+      split_unit<false>(u, dv, r, c);
+      const int32_t s = s_src[r];
+      const uint32_t off = s >= 0 ? (uint32_t)(((int64_t)s * W + c) * sizeof(U)) : kNoRow;
+      w[i] = buf_load<NTL, U>(src, off);
+    }
+  };
+  auto store_stage = [&](int j, const U (&w)[kFusedIlp]) {
+#pragma unroll
+    for (int i = 0; i < kFusedIlp; i++)
+      buf_store<NTS>(w[i], dst, (uint32_t)(j * kStep + i * kCopyThreads + tid) * sizeof(U));
+  };
+  // Two register sets, two stages per trip: no copy between them, so no
+  // wait on loads just issued.  A stage index past the last one stores
+  // nothing (every offset is past the slice).
+  U va[kFusedIlp], vb[kFusedIlp];
+  load_stage(0, va);
+  // Dropped stores, held after the first loads by the compiler fence, so
+  // that entering the loop, as on every later trip, kFusedIlp stores sit
+  // between one stage's loads and the next stage's: the wait at the loop
+  // head then does not cover the stores issued just before the back edge.
+  asm volatile("" ::: "memory");
+  U zero[kFusedIlp];
+#pragma unroll
+  for (int i = 0; i < kFusedIlp; i++) zero[i] = zero_unit<U>();
+  store_stage(n_stages + 1, zero);
+  int j = 0;
+  do {  // n_stages >= 1: no zero-trip branch for the first loads to sink past
+    load_stage(min(j + 1, n_stages - 1), vb);
+    store_stage(j, va);
+    load_stage(min(j + 2, n_stages - 1), va);
+    store_stage(j + 1, vb);
+    j += 2;
+  } while (j < n_stages);
 }
 
 // --------------------------------------------------------------- restore --
@@ -495,6 +657,57 @@ hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes
     default: MOE_RESTORE(uint16_t, false, false); break;
   }
 #undef MOE_RESTORE
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_and_pad(const void *in, const void *probs, int prob_bytes, int unit_bytes,
+                               int64_t row_units, const int32_t *split_sizes,
+                               const int32_t *sorted_idx, int C, int R, int A, int n_cap,
+                               int out_cap, void *out, void *out_probs, int32_t *row_map,
+                               int32_t *padded_offsets, int32_t *dev_status, hipStream_t s) {
+  const int G = C / R;
+  // rows per workgroup: enough workgroups to fill the chip once, at most one
+  // row per lane of wave 0
+  const int64_t want = ((int64_t)out_cap + MOE_FUSED_WGS - 1) / MOE_FUSED_WGS;
+  const int rows_per = (int)std::min<int64_t>(kWave, std::max<int64_t>(1, want));
+  // fused only for a small destination, whose copy is short next to a
+  // launch; the fused copy addresses the source and a workgroup's slice with
+  // 32-bit byte offsets
+  const int64_t out_bytes = (int64_t)out_cap * row_units * unit_bytes;
+  const bool fits = (int64_t)n_cap * row_units * unit_bytes <= kMaxBufBytes &&
+                    ((int64_t)rows_per + 2) * row_units * unit_bytes +
+                            (int64_t)kCopyThreads * kFusedIlp * unit_bytes * 2 <
+                        ((int64_t)1 << 31);
+  if (out_bytes > (int64_t)MOE_FUSED_MAX_BYTES || !fits) {
+    const hipError_t e = launch_chunk_map(split_sizes, sorted_idx, C, R, A, n_cap, out_cap,
+                                          row_map, padded_offsets, dev_status, s);
+    if (e != hipSuccess) return e;
+    return launch_pad_copy(in, probs, prob_bytes, unit_bytes, row_units, n_cap, row_map, out_cap,
+                           out, out_probs, dev_status, s);
+  }
+  const size_t lds = chunk_tables_bytes(C, G);
+  const int64_t blocks = out_cap > 0 ? ((int64_t)out_cap + rows_per - 1) / rows_per : 1;
+  const dim3 grid = spill_grid(blocks), block(kCopyThreads);
+  const auto *pp = static_cast<const uint8_t *>(probs);
+  auto *op = static_cast<uint8_t *>(out_probs);
+  const bool stream = (int64_t)out_cap * row_units * unit_bytes * 2 > kStreamBytes;
+  const RowDiv dv = row_div(row_units);
+#define MOE_FUSED(UT, NTL, NTS)                                                                \
+  hipLaunchKernelGGL((pad_fused_kernel<UT, NTL, NTS>), grid, block, lds, s,                    \
+                     static_cast<const UT *>(in), pp, prob_bytes, dv, split_sizes, sorted_idx, C, \
+                     R, A, n_cap, out_cap, rows_per, static_cast<UT *>(out), op, row_map,      \
+                     padded_offsets, dev_status)
+  switch (unit_bytes) {
+    case 16:
+      if (stream)
+        MOE_FUSED(v4u, (MOE_PAD_STREAM & 1) != 0, (MOE_PAD_STREAM & 2) != 0);
+      else
+        MOE_FUSED(v4u, false, false);
+      break;
+    case 4: MOE_FUSED(uint32_t, false, false); break;
+    default: MOE_FUSED(uint16_t, false, false); break;
+  }
+#undef MOE_FUSED
   return hipGetLastError();
 }
 

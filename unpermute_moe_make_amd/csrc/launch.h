@@ -85,6 +85,13 @@ hipError_t launch_chunk_map(const int32_t *split_sizes, const int32_t *sorted_id
 hipError_t launch_pad_copy(const void *in, const void *probs, int prob_bytes, int unit_bytes,
                            int64_t row_units, int n_cap, const int32_t *row_map, int out_cap,
                            void *out, void *out_probs, int32_t *dev_status, hipStream_t s);
+// The map and the pad copy of one sort-and-pad call: one fused launch for a
+// small destination, else the map and the pad copy.
+hipError_t launch_sort_and_pad(const void *in, const void *probs, int prob_bytes, int unit_bytes,
+                               int64_t row_units, const int32_t *split_sizes,
+                               const int32_t *sorted_idx, int C, int R, int A, int n_cap,
+                               int out_cap, void *out, void *out_probs, int32_t *row_map,
+                               int32_t *padded_offsets, int32_t *dev_status, hipStream_t s);
 hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes, int unit_bytes,
                                int64_t row_units, const int32_t *row_map,
                                const int32_t *split_sizes, int C, int out_cap, int n_cap,
