@@ -74,13 +74,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
-// fp64 -> bf16 RNE without double rounding: truncate to fp32 and OR the
-// sticky bit into its last place (round to odd keeps 16 guard bits), then
-// round that fp32 value to bf16 as above.
+// fp64 -> bf16 RNE without double rounding: round to odd at fp32 precision
+// (fp32 keeps 16 more bits than bf16 at every exponent, so the second
+// rounding is then exact), then round that fp32 value to bf16 as above.
+// Round to odd from the hardware's nearest conversion: when it was inexact,
+// step one place toward zero if it rounded away (the truncated value; at
+// overflow, infinity becomes the largest finite fp32) and set the last bit.
 __device__ __forceinline__ uint32_t f64_to_bf16(double d) {
-  const float f = __double2float_rz(d);
+  const float f = (float)d;
   uint32_t u = __float_as_uint(f);
-  if (d == d && (double)f != d) u |= 1u;
+  const double back = (double)f;
+  if (d == d && back != d) {
+    if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1u;
+    u |= 1u;
+  }
   return f32_to_bf16(__uint_as_float(u));
 }
 // Round an fp32 value to bf16 precision, keeping it as fp32.
