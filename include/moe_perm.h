@@ -396,7 +396,9 @@ MOE_PERM_API int moe_permute_mask_scaled(const void *x, int elem_bytes, const vo
  *   in           [n_cap][hidden] elements of elem_bytes (2: bf16/fp16,
  *                4: fp32), copied bitwise.  Chunk c occupies split_sizes[c]
  *                rows, chunks back to back in input order from row 0.
- *   probs        [n_cap] elements of prob_bytes (2 or 4), or NULL.
+ *   probs        [n_cap] elements of prob_bytes (2 or 4), or NULL.  With
+ *                n_cap == 0 it may be NULL even when out_probs is not (then
+ *                out_probs is all zero).
  *   split_sizes  [num_chunks] int32, device.
  *   sorted_idx   [num_chunks] int32, device: input chunk at sorted position
  *                q.  Positions [g*R, (g+1)*R) form group g, R =
@@ -431,7 +433,8 @@ MOE_PERM_API int moe_sort_chunks_and_pad(const void *in, const void *probs, int 
  *   out[row_map[d]] = in[d]   for every d with row_map[d] >= 0
  *   out[s] = 0                for s in [sum(split_sizes), n_cap)
  *
- *   in        [out_cap][hidden] (elem_bytes), probs [out_cap] or NULL.
+ *   in        [out_cap][hidden] (elem_bytes), probs [out_cap] or NULL
+ *             (with out_cap == 0, NULL also when out_probs is not).
  *   row_map   [out_cap] from moe_sort_chunks_and_pad.
  *   split_sizes [num_chunks] device (gives the token total).
  *   out       [n_cap][hidden], out_probs [n_cap] or NULL.
@@ -454,7 +457,8 @@ MOE_PERM_API int moe_unpad_and_restore_chunks(const void *in, const void *probs,
  *   moe_unpad_and_restore_chunks_bwd: gradient of the restore w.r.t. the
  *     padded buffer = the pad copy applied to the restored gradient
  *     (padding rows get zero gradient).
- * Arguments as in the forward calls they mirror.
+ * Arguments as in the forward calls they mirror (the gradient of the
+ * probs may likewise be NULL when its tensor has no rows).
  * ------------------------------------------------------------------------ */
 MOE_PERM_API int moe_sort_chunks_and_pad_bwd(const void *d_out, const void *d_out_probs,
                                              int elem_bytes, int prob_bytes,

@@ -143,16 +143,20 @@ def test_chunk_host_errors(lib):
     assert call(C=4096, R=8) == MOE_ERR_UNSUPPORTED
     assert call(eb=8) == MOE_ERR_UNSUPPORTED
     assert call(sizes=None) == MOE_ERR_NULL
-    assert call(out_probs=P(FAKE)) == MOE_ERR_NULL
+    assert call(out_probs=P(FAKE)) == MOE_ERR_NULL      # prob output with no probs (n_cap > 0)
     assert call(out=P(FAKE + 2), eb=4) == MOE_ERR_ALIGN
     g = lib.moe_unpad_and_restore_chunks
     assert g(P(FAKE), None, 2, 4, P(FAKE), None, 128, 2048, 64, 100, P(FAKE), None, None,
              None) == MOE_ERR_NULL
     assert g(P(FAKE), None, 3, 4, P(FAKE), P(FAKE), 128, 2048, 64, 100, P(FAKE), None, None,
              None) == MOE_ERR_UNSUPPORTED
+    assert g(P(FAKE), None, 2, 4, P(FAKE), P(FAKE), 128, 2048, 64, 100, P(FAKE), P(FAKE), None,
+             None) == MOE_ERR_NULL                   # out_probs without probs, out_cap > 0
     h = lib.moe_unpad_and_restore_chunks_bwd
     assert h(P(FAKE), None, 2, 4, None, 2048, 64, 100, P(FAKE), None, None,
              None) == MOE_ERR_NULL
+    assert h(P(FAKE), None, 2, 4, P(FAKE), 2048, 64, 100, P(FAKE), P(FAKE), None,
+             None) == MOE_ERR_NULL                   # d_in_probs without d_out_probs, n_cap > 0
 
 
 def test_binding_rejects_host_tensors():

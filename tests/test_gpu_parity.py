@@ -678,6 +678,53 @@ def test_chunk_bad_metadata_sets_status(m):
     assert int(st.item()) & m.DEV_OVERFLOW
 
 
+@pytest.mark.parametrize("out_cap", [0, 1, 100, 5000])
+def test_chunk_no_source_rows(m, out_cap):
+    """N_cap = 0 (an empty, null input): every chunk is empty, so every padded
+    row is zero and unmapped, every padded offset 0; the restore of nothing
+    writes nothing."""
+    say(f"chunk sort-and-pad with no source rows, out_cap={out_cap}")
+    C, R, H = 8, 4, 256
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    probs = torch.empty(0, dtype=torch.float32, device=DEV)
+    sizes = torch.zeros(C, dtype=torch.int32)
+    order = torch.arange(C, dtype=torch.int32)
+    cw = workloads.Chunked("empty", x.cpu(), probs.cpu(), sizes, order, R, 16, out_cap)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, out_p, rm, off = _run_chunks(m, cw, x, probs, sizes.to(DEV), order.to(DEV), st)
+    r_out, r_p, r_rm, r_off = oracle.sort_chunks_and_pad(
+        np.zeros((0, H), np.uint16), np.zeros(0, np.float32), sizes.numpy(), order.numpy(), R,
+        16, out_cap)
+    assert int(st.item()) == 0
+    assert_bits_equal(rm.cpu().numpy(), r_rm, "row_map")
+    assert_bits_equal(off.cpu().numpy(), r_off, "padded_offsets")
+    assert_bits_equal(_raw(out), r_out, "padded tokens")
+    assert_bits_equal(_raw(out_p), r_p, "padded probs")
+    back, back_p = m.moe_unpad_and_restore_chunks(out, rm, sizes.to(DEV), 0, out_p, dev_status=st)
+    torch.cuda.synchronize()
+    assert back.shape == (0, H) and back_p.shape == (0,) and int(st.item()) == 0
+
+
+def test_chunk_negative_size_sets_status(m):
+    """A negative chunk size is bad metadata: the status says so and the whole
+    padded buffer is zero and unmapped, through the one-launch path (small
+    buffer) and the two-launch path (a buffer past its size limit)."""
+    say("chunk negative size")
+    for H in (64, 32768):
+        cw = workloads.chunked(2100, seed=52, H=H, num_ranks=4, num_experts=6, align=16,
+                               num_empty=5)
+        sizes = cw.split_sizes.clone()
+        sizes[3] = -1
+        x, probs = cw.x.to(DEV), cw.probs.to(DEV)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        out, out_p, rm, off = _run_chunks(m, cw, x, probs, sizes.to(DEV),
+                                          cw.sorted_idx.to(DEV), st)
+        torch.cuda.synchronize()
+        assert int(st.item()) & m.DEV_BAD_CHUNKS, H
+        assert bool((rm == -1).all()) and bool((out.view(torch.int16) == 0).all()), H
+        assert bool((off == 0).all()) and bool((out_p == 0).all()), H
+
+
 def test_chunk_graph_replay(m):
     """Sort-and-pad + restore captured once at the 32768-token size, replayed
     with eight different split-size draws at fixed buffer sizes."""

@@ -424,7 +424,8 @@ MOE_PERM_API int moe_sort_chunks_and_pad(const void *in, const void *probs, int 
   if (!split_sizes || !sorted_idx || !padded_offsets) return MOE_ERR_NULL;
   if (out_cap > 0 && (!out || !row_map)) return MOE_ERR_NULL;
   if (n_cap > 0 && !in) return MOE_ERR_NULL;
-  if (out_probs != nullptr && probs == nullptr) return MOE_ERR_NULL;
+  // with no source rows an empty probs tensor may be NULL; no kernel reads it
+  if (out_probs != nullptr && probs == nullptr && n_cap > 0) return MOE_ERR_NULL;
   int st = check_chunk_elems(elem_bytes, prob_bytes, in, out, probs, out_probs);
   if (st) return st;
   if (!aligned(split_sizes, 4) || !aligned(sorted_idx, 4) || !aligned(row_map, 4) ||
@@ -448,7 +449,7 @@ int restore_common(const void *in, const void *probs, int elem_bytes, int prob_b
   if (!split_sizes) return MOE_ERR_NULL;
   if (out_cap > 0 && (!in || !row_map)) return MOE_ERR_NULL;
   if (n_cap > 0 && !out) return MOE_ERR_NULL;
-  if (out_probs != nullptr && probs == nullptr) return MOE_ERR_NULL;
+  if (out_probs != nullptr && probs == nullptr && out_cap > 0) return MOE_ERR_NULL;
   int st = check_chunk_elems(elem_bytes, prob_bytes, in, out, probs, out_probs);
   if (st) return st;
   if (!aligned(split_sizes, 4) || !aligned(row_map, 4) || !aligned(dev_status, 4))
@@ -492,7 +493,7 @@ MOE_PERM_API int moe_unpad_and_restore_chunks_bwd(const void *d_out, const void 
   if (n_cap < 0 || out_cap < 0 || H < 1) return MOE_ERR_SHAPE;
   if (out_cap > 0 && (!d_in || !row_map)) return MOE_ERR_NULL;
   if (n_cap > 0 && out_cap > 0 && !d_out) return MOE_ERR_NULL;
-  if (d_in_probs != nullptr && d_out_probs == nullptr) return MOE_ERR_NULL;
+  if (d_in_probs != nullptr && d_out_probs == nullptr && n_cap > 0) return MOE_ERR_NULL;
   int st = check_chunk_elems(elem_bytes, prob_bytes, d_out, d_in, d_out_probs, d_in_probs);
   if (st) return st;
   if (!aligned(row_map, 4) || !aligned(dev_status, 4)) return MOE_ERR_ALIGN;
