@@ -180,6 +180,53 @@ def test_row_map_empty(m):
     assert_bits_equal(off.cpu().numpy(), np.zeros(9, np.int32), "expert_offsets")
 
 
+def test_routed_ops_no_tokens(m):
+    """T = 0: every routed call, forward and backward, in every form, accepts
+    the empty (NULL-pointer) tensors, returns OK with empty outputs and
+    leaves the status clear; the maps' expert offsets are all zero."""
+    say("routed ops with T=0")
+    T, k, E, H = 0, 4, 8, 64
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    idx = torch.zeros((T, k), dtype=torch.int32, device=DEV)
+    rm, off = m.moe_make_row_id_map(idx, E, dev_status=st)
+    assert rm.shape == (E, T) and bool((off == 0).all())
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    probs = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    out, out_p = m.moe_permute(x, idx, rm, probs, dev_status=st)
+    assert out.shape == (0, H) and out_p.shape == (0,)
+    assert m.moe_unpermute(out, idx, rm, probs, dev_status=st).shape == (0, H)
+    for fp64 in (False, True):
+        assert m.moe_unpermute_ep(out, idx, rm, 2, probs, fp64_cross=fp64,
+                                  dev_status=st).shape == (0, H)
+    d_in, d_p = m.moe_unpermute_bwd(x, idx, rm, probs, out, dev_status=st)
+    assert d_in.shape == (0, H) and d_p.shape == (0, k)
+    d_x, d_pp = m.moe_permute_bwd(out, idx, rm, out_p, dev_status=st)
+    assert d_x.shape == (0, H) and d_pp.shape == (0, k)
+    x8 = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=DEV)
+    sc = torch.empty((T, 2), dtype=torch.float32, device=DEV)
+    o8, osc, _ = m.moe_permute_scaled(x8, idx, rm, sc, dev_status=st)
+    assert o8.shape == (0, H) and osc.shape == (0, 2)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    ti, tp = m.moe_topk_softmax(logits, k)
+    assert ti.shape == (0, k) and tp.shape == (0, k)
+    assert m.moe_topk_softmax_bwd(tp, tp, ti, E, dev_status=st).shape == (0, E)
+    mask = torch.zeros((T, E), dtype=torch.bool, device=DEV)
+    mm, moff = m.moe_make_mask_row_id_map(mask)
+    assert mm.shape == (0, 2 * E + 1) and bool((moff == 0).all())
+    pe = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    mo, mop = m.moe_permute_mask(x, mm, 0, pe, dev_status=st)
+    assert mo.shape == (0, H) and mop.shape == (0,)
+    mu = m.moe_unpermute_mask(mo, mm, pe, dev_status=st)
+    mu = mu[0] if isinstance(mu, tuple) else mu
+    assert mu.shape == (0, H)
+    mb = m.moe_unpermute_mask_bwd(x, mo, pe, mm, dev_status=st)
+    assert mb[0].shape == (0, H)
+    ms = m.moe_permute_mask_scaled(x8, mm, 0, sc, dev_status=st)
+    assert ms[0].shape == (0, H)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+
+
 def test_row_map_bad_routing_sets_status(m):
     say("row_map bad expert / duplicate expert")
     idx = torch.tensor([[0, 1], [2, 9], [3, 3], [1, 0]], dtype=torch.int32, device=DEV)
