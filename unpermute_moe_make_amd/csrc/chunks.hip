@@ -1,20 +1,28 @@
 // Fused chunk sort-and-pad and unpad-and-restore (TransformerEngine PR "Fuse
-// MoE chunk sorting and padding", Description, Changes and Diagram): one map
-// kernel and two copy kernels.
+// MoE chunk sorting and padding", Description, Changes and Diagram): the
+// sort-and-pad is one launch that builds the map and copies (padded buffers
+// up to MOE_FUSED_MAX_BYTES), or a map kernel and a pad copy; the restore is
+// one copy kernel.
 //
 // Map.  Wave 0 of every map workgroup rebuilds the small chunk tables in LDS
 // from the device-resident split sizes and chunk order -- input-order source
 // offsets, sorted-order prefixes, padded group starts -- with wave scans (DPP
-// row shifts and lane reads) and no workgroup barrier, so the build costs a
-// few hundred cycles after the metadata loads.  The workgroup then writes its slice of
-// the padded destination -> source row map by two binary searches per row.
+// row shifts and lane reads) and no workgroup barrier: after the metadata
+// loads it is a chain of LDS round trips and scans, about 2 us with the row
+// searches.  The workgroup then writes its slice of the padded destination ->
+// source row map by two binary searches per row.
 // Every workgroup validates the metadata the same way; on bad metadata the
 // whole map is -1 (so the copies write zeros) and workgroup 0 reports it.
 //
+// Fused.  Every workgroup builds the tables the same way, resolves the source
+// rows of its slice of destination rows, and copies the slice (see
+// pad_fused_kernel).
+//
 // Copies.  Both walk a flat index over (row, unit) with 16-byte units where
 // the row allows, consecutive lanes on consecutive units, each lane's units
-// (one in the pad copy, three in the restore) loaded before any is stored.  The pad copy writes every destination
-// row (zeros where the map is -1).  The restore scatters every mapped row
+// (one in the pad copy, three in the restore) loaded before any is stored.
+// The pad copy writes every destination row (zeros where the map is -1).
+// The restore scatters every mapped row
 // back to its source and writes zeros to the rows past the token total,
 // which it sums from the split sizes on the device.
 #include "common.h"
