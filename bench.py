@@ -250,7 +250,8 @@ def build_routed(m, w):
              k, E, n, p(dP), p(dprob), None,)
     step.add("permute_bwd", lib.moe_permute_bwd, p(dP), p(d_pp), p(idx), p(rm), T, H, k, E, n,
              p(dx), p(dprob2), None,)
-    # Rows beyond the step (SURVEY "next" rows), timed on their own.
+    # The library's further operations (EP combine, router, mask-map form, FP8
+    # rows), timed on their own after the step.
     y_ep = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     logits = w.logits.to(dev).contiguous()
     r_idx = torch.empty((T, k), dtype=torch.int32, device=dev)

@@ -92,7 +92,7 @@ def _brute_rows(topk_idx: np.ndarray, E: int):
 # ---------------------------------------------------- (1) the row map ------
 
 def test_worked_example_second_pass():
-    g = _read_golden("p2_worked_example.txt")
+    g = _read_golden("make_row_id_map_worked_example.txt")
     mask = np.array(g["routing_map"], dtype=np.int32)          # [T][E]
     pass2 = np.array(g["pass2"], dtype=np.int32)               # [T][E]
     T, E = mask.shape
@@ -103,7 +103,7 @@ def test_worked_example_second_pass():
 
 
 def test_worked_example_third_pass():
-    g = _read_golden("p2_worked_example.txt")
+    g = _read_golden("make_row_id_map_worked_example.txt")
     mask = np.array(g["routing_map"], dtype=np.int32)
     T, E = mask.shape
     pt, pe = np.nonzero(mask)
@@ -750,7 +750,7 @@ def _check_mask_map(m, pairs, E):
 @pytest.mark.parametrize("dtype", [np.int32, np.uint8])
 def test_mask_map_worked_example(dtype):
     """The worked example's third pass, entry for entry (unused entries -1)."""
-    g = _read_golden("p2_worked_example.txt")
+    g = _read_golden("make_row_id_map_worked_example.txt")
     mask = np.array(g["routing_map"], dtype=dtype)
     T, E = mask.shape
     m, off = oracle.mask_row_id_map(mask)
