@@ -63,7 +63,6 @@ constexpr int kPadIlp = MOE_PAD_ILP;
 constexpr int kRestoreIlp = MOE_RESTORE_ILP;
 constexpr int kFusedIlp = MOE_FUSED_ILP;
 constexpr int kMapRows = 256;         // row_map entries per map workgroup (one per lane)
-constexpr int kMetaBatch = 4;         // chunk metadata loads in flight per lane
 
 // Row / unit split of a flat unit index u over rows of W units without a
 // hardware divide: q = floor(u / W) = (umulhi(m, u) + u) >> l, with
@@ -103,11 +102,11 @@ __device__ __forceinline__ void split_unit(int64_t u, const RowDiv &dv, int64_t 
 // capacity check rejects them.
 struct ChunkTables {
   int64_t *g_pad;    // [G+1] padded start of each group; g_pad[G] = padded total
-  int32_t *src_off;  // [C]   first source row of each input chunk
   int32_t *qoff;     // [C+1] sorted-order prefix of chunk sizes
-  int32_t *order;    // [C]   input chunk at each sorted position
+  int32_t *qsrc;     // [C]   first source row of the chunk at each sorted position
+  int32_t *src_off;  // [C]   first source row of each input chunk
   int32_t *size;     // [C]   chunk sizes (input order)
-  int32_t *seen;     // [C]   permutation check
+  int32_t *inv;      // [C]   sorted position of each input chunk (permutation check)
 };
 
 inline size_t chunk_tables_bytes(int C, int G) {
@@ -117,13 +116,21 @@ inline size_t chunk_tables_bytes(int C, int G) {
 __device__ inline ChunkTables carve_tables(void *lds, int C, int G) {
   ChunkTables t;
   t.g_pad = reinterpret_cast<int64_t *>(lds);
-  t.src_off = reinterpret_cast<int32_t *>(t.g_pad + G + 1);
-  t.qoff = t.src_off + C;
-  t.order = t.qoff + C + 1;
-  t.size = t.order + C;
-  t.seen = t.size + C;
+  t.qoff = reinterpret_cast<int32_t *>(t.g_pad + G + 1);
+  t.qsrc = t.qoff + C + 1;
+  t.src_off = t.qsrc + C;
+  t.size = t.src_off + C;
+  t.inv = t.size + C;
   return t;
 }
+
+// Chunks (and groups) per lane of the table build, a compile-time bound so
+// that a lane's entries live in registers: 4 up to 256 chunks, 32 up to
+// MOE_MAX_CHUNKS.
+constexpr int kPerSmall = 4;
+constexpr int kPerLarge = 32;
+static_assert(kWave * kPerLarge >= MOE_MAX_CHUNKS, "table build covers every chunk count");
+inline int table_per(int C) { return C <= kWave * kPerSmall ? kPerSmall : kPerLarge; }
 
 // Lane l - S of the same 16-lane row (DPP row_shr:S), or 0 when that lane is
 // in an earlier row.  Needs every lane of the wave active.
@@ -168,12 +175,17 @@ __device__ __forceinline__ int wave_or(int v) {
   return v;
 }
 
-// Built by ONE wave (call from all 64 lanes of wave 0): each lane owns a
-// contiguous segment of chunks and of groups, scans run across lanes, and
-// lanes exchange table entries through LDS ordered by
-// wave-level fences -- no workgroup barrier inside.  Returns the device
-// status bits (the same value in every lane); non-zero means the tables
-// must not be used.
+// Built by ONE wave (call from all 64 lanes of wave 0): lane l owns the
+// contiguous chunks [l * per, (l + 1) * per) (per <= PER), held in registers;
+// scans run across lanes (DPP), and lanes exchange entries through LDS
+// ordered by wave-level fences -- no workgroup barrier inside.  The order is
+// checked to be a permutation by scattering each sorted position to its
+// input chunk and reading it back: a repeated chunk leaves one of its
+// positions overwritten.  Each step issues all its memory operations before
+// using any, so the build is one global round trip and three LDS round
+// trips.  Returns the device status bits (the same value in every lane);
+// non-zero means the tables must not be used.
+template <int PER>
 __device__ int build_chunk_tables_wave(const int32_t *__restrict__ split_sizes,
                                        const int32_t *__restrict__ sorted_idx, int C, int R,
                                        int A, int n_cap, int out_cap, const ChunkTables &t) {
@@ -181,84 +193,93 @@ __device__ int build_chunk_tables_wave(const int32_t *__restrict__ split_sizes,
   const int lane = threadIdx.x & (kWave - 1);
   const int per = (C + kWave - 1) / kWave;
   const int c0 = min(C, lane * per), c1 = min(C, c0 + per);
+  int sz[PER], od[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int c = min(c0 + i, C - 1);
+    sz[i] = split_sizes[c];
+    od[i] = sorted_idx[c];
+  }
   int bad = 0;
   int64_t seg = 0;
-  // the metadata loads of kMetaBatch chunks are all issued before the first
-  // is used: one memory round trip per batch
-  for (int cb = c0; cb < c1; cb += kMetaBatch) {
-    int sz[kMetaBatch], od[kMetaBatch];
 #pragma unroll
-    for (int b = 0; b < kMetaBatch; b++) {
-      const int c = min(cb + b, c1 - 1);
-      sz[b] = split_sizes[c];
-      od[b] = sorted_idx[c];
-    }
-#pragma unroll
-    for (int b = 0; b < kMetaBatch; b++) {
-      // the checks use the loads outside the branch, which keeps the
-      // compiler from sinking a load into it (and so behind the first use)
-      const int c = cb + b;
-      const bool in = c < c1;
-      const int s = in ? sz[b] : 0, o = in ? od[b] : 0;
-      if (s < 0) bad |= MOE_DEV_BAD_CHUNKS;
-      if (s > n_cap) bad |= MOE_DEV_OVERFLOW;
-      if ((unsigned)o >= (unsigned)C) bad |= MOE_DEV_BAD_CHUNKS;
-      seg += max(s, 0);
-      if (in) {
-        t.size[c] = max(s, 0);
-        t.order[c] = o;
-        t.seen[c] = 0;
-      }
-    }
+  for (int i = 0; i < PER; i++) {
+    const bool in = c0 + i < c1;
+    const int s = in ? sz[i] : 0, o = in ? od[i] : 0;
+    if (s < 0) bad |= MOE_DEV_BAD_CHUNKS;
+    if (s > n_cap) bad |= MOE_DEV_OVERFLOW;
+    if ((unsigned)o >= (unsigned)C) bad |= MOE_DEV_BAD_CHUNKS;
+    sz[i] = max(s, 0);
+    od[i] = (unsigned)o < (unsigned)C ? o : 0;
+    seg += sz[i];
   }
-  __syncwarp();
-  for (int q = c0; q < c1; q++) {
-    const int o = t.order[q];
-    if ((unsigned)o < (unsigned)C) atomicAdd(&t.seen[o], 1);
-  }
-  __syncwarp();
-  for (int c = c0; c < c1; c++)
-    if (t.seen[c] != 1) bad |= MOE_DEV_BAD_CHUNKS;
-  bad = wave_or(bad);
-
   // Source offsets: exclusive scan of the sizes in input order.
   int64_t n_act;
   int64_t run = wave_exclusive_scan(seg, &n_act);
-  for (int c = c0; c < c1; c++) {
-    t.src_off[c] = (int32_t)min(run, (int64_t)INT32_MAX);
-    run += t.size[c];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int c = c0 + i;  // as an input chunk, and as a sorted position
+    if (c < c1) {
+      t.size[c] = sz[i];
+      t.src_off[c] = (int32_t)min(run, (int64_t)INT32_MAX);
+      t.inv[od[i]] = c;
+    }
+    run += sz[i];
   }
+  __syncwarp();
+  // Per sorted position: its chunk's size and source start, and the check.
+  int ssz[PER], qs[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int q = c0 + i;
+    const int back = t.inv[od[i]];
+    ssz[i] = t.size[od[i]];
+    qs[i] = t.src_off[od[i]];
+    if (q < c1 && back != q) bad |= MOE_DEV_BAD_CHUNKS;
+  }
+  bad = wave_or(bad);
   if (n_act > n_cap) bad |= MOE_DEV_OVERFLOW;
-  // Sorted-order prefix of the sizes (only meaningful with a valid order).
+  // Sorted-order prefix of the sizes (all zero when the metadata is bad).
   int64_t sseg = 0;
-  if (!bad)
-    for (int q = c0; q < c1; q++) sseg += t.size[t.order[q]];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    ssz[i] = (c0 + i < c1 && !bad) ? ssz[i] : 0;
+    sseg += ssz[i];
+  }
   int64_t stot;
   run = wave_exclusive_scan(sseg, &stot);
-  for (int q = c0; q < c1; q++) {
-    t.qoff[q] = (int32_t)min(run, (int64_t)INT32_MAX);
-    if (!bad) run += t.size[t.order[q]];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int q = c0 + i;
+    if (q < c1) {
+      t.qoff[q] = (int32_t)min(run, (int64_t)INT32_MAX);
+      t.qsrc[q] = qs[i];
+    }
+    run += ssz[i];
   }
   if (lane == kWave - 1) t.qoff[C] = (int32_t)min(stot, (int64_t)INT32_MAX);
   __syncwarp();
-  // Groups: padded lengths, then their exclusive scan.
+  // Groups: padded lengths, then their exclusive scan (G <= C, so a lane
+  // owns at most PER groups).
   const int perg = (G + kWave - 1) / kWave;
   const int g0 = min(G, lane * perg), g1 = min(G, g0 + perg);
+  int64_t gp[PER];
   int64_t gseg = 0;
-  for (int g = g0; g < g1; g++) {
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int g = min(g0 + i, G - 1);
     // n and A are non-negative int32 (qoff never decreases), so n + A - 1
     // fits 32 unsigned bits and the division needs no 64-bit routine
     const uint32_t n = (uint32_t)(t.qoff[(g + 1) * R] - t.qoff[g * R]);
-    const int64_t padded = (int64_t)((n + (uint32_t)A - 1u) / (uint32_t)A) * A;
-    t.g_pad[g] = padded;
-    gseg += padded;
+    gp[i] = g0 + i < g1 ? (int64_t)((n + (uint32_t)A - 1u) / (uint32_t)A) * A : 0;
+    gseg += gp[i];
   }
   int64_t pad_total;
   run = wave_exclusive_scan(gseg, &pad_total);
-  for (int g = g0; g < g1; g++) {
-    const int64_t p = t.g_pad[g];
-    t.g_pad[g] = run;
-    run += p;
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    if (g0 + i < g1) t.g_pad[g0 + i] = run;
+    run += gp[i];
   }
   if (lane == kWave - 1) t.g_pad[G] = pad_total;
   if (pad_total > out_cap) bad |= MOE_DEV_OVERFLOW;
@@ -288,7 +309,7 @@ __device__ __forceinline__ int32_t chunk_src_row(const ChunkTables &t, int G, in
   if (local >= (int64_t)t.qoff[(g + 1) * R] - gs) return -1;
   const int64_t u = gs + local;  // position in the sorted token order
   const int q = last_le(t.qoff, g * R, (g + 1) * R, u);
-  return (int32_t)(t.src_off[t.order[q]] + (u - t.qoff[q]));
+  return (int32_t)(t.qsrc[q] + (u - t.qoff[q]));
 }
 
 __device__ __forceinline__ void copy_prob(const uint8_t *src, int64_t si, uint8_t *dst,
@@ -305,6 +326,7 @@ __device__ __forceinline__ void copy_prob(const uint8_t *src, int64_t si, uint8_
 
 // Grid ceil(out_cap / kMapRows): wave 0 of every workgroup builds the tables,
 // then all lanes write the workgroup's slice of row_map.
+template <int PER>
 __global__ __launch_bounds__(kCopyThreads) void chunk_map_kernel(
     const int32_t *__restrict__ split_sizes, const int32_t *__restrict__ sorted_idx, int C, int R,
     int A, int n_cap, int out_cap, int32_t *__restrict__ row_map,
@@ -314,7 +336,8 @@ __global__ __launch_bounds__(kCopyThreads) void chunk_map_kernel(
   const int G = C / R;
   const ChunkTables t = carve_tables(lds, C, G);
   if (threadIdx.x < kWave) {
-    const int bad = build_chunk_tables_wave(split_sizes, sorted_idx, C, R, A, n_cap, out_cap, t);
+    const int bad =
+        build_chunk_tables_wave<PER>(split_sizes, sorted_idx, C, R, A, n_cap, out_cap, t);
     if (threadIdx.x == 0) bad_s = bad;
   }
   __syncthreads();
@@ -381,20 +404,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(void *base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, kBufWord3);
 }
 
-template <bool NT, typename U> __device__ __forceinline__ U buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off);
-template <> __device__ __forceinline__ v4u buf_load<false, v4u>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-template <> __device__ __forceinline__ v4u buf_load<true, v4u>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
-}
-template <> __device__ __forceinline__ uint32_t buf_load<false, uint32_t>(__amdgpu_buffer_rsrc_t r,
-                                                                        uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-template <> __device__ __forceinline__ uint16_t buf_load<false, uint16_t>(__amdgpu_buffer_rsrc_t r,
-                                                                        uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+template <bool NT, typename U>
+__device__ __forceinline__ U buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  constexpr int aux = NT ? 2 : 0;
+  if constexpr (sizeof(U) == 16)
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, aux);
+  else if constexpr (sizeof(U) == 4)
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, aux);
+  else
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, aux);
 }
 
 template <bool NT>
@@ -423,7 +441,7 @@ __device__ __forceinline__ void buf_store(uint16_t v, __amdgpu_buffer_rsrc_t r, 
 // the stores issued just before them.  Workgroup 0 also writes
 // padded_offsets and reports bad metadata.  Needs a slice shorter than 2^31
 // bytes and a source of at most kMaxBufBytes.
-template <typename U, bool NTL, bool NTS>
+template <typename U, bool NTL, bool NTS, int PER>
 __global__ __launch_bounds__(kCopyThreads) void pad_fused_kernel(
     const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, RowDiv dv,
     const int32_t *__restrict__ split_sizes, const int32_t *__restrict__ sorted_idx, int C, int R,
@@ -438,7 +456,8 @@ __global__ __launch_bounds__(kCopyThreads) void pad_fused_kernel(
   const int64_t d0 = blk * rows_per;
   const int n_rows = (int)max((int64_t)0, min((int64_t)rows_per, (int64_t)out_cap - d0));
   if (threadIdx.x < kWave) {
-    const int bad = build_chunk_tables_wave(split_sizes, sorted_idx, C, R, A, n_cap, out_cap, t);
+    const int bad =
+        build_chunk_tables_wave<PER>(split_sizes, sorted_idx, C, R, A, n_cap, out_cap, t);
     if (blk == 0) {
       if (threadIdx.x == 0) report(dev_status, bad);
       for (int g = threadIdx.x; g <= G; g += kWave) padded_offsets[g] = bad ? 0 : (int32_t)t.g_pad[g];
@@ -587,8 +606,14 @@ hipError_t launch_chunk_map(const int32_t *split_sizes, const int32_t *sorted_id
   const int G = C / R;
   const size_t lds = chunk_tables_bytes(C, G);
   const int blocks = out_cap > 0 ? (int)(((int64_t)out_cap + kMapRows - 1) / kMapRows) : 1;
-  hipLaunchKernelGGL(chunk_map_kernel, dim3(blocks), dim3(kCopyThreads), lds, s, split_sizes,
-                     sorted_idx, C, R, A, n_cap, out_cap, row_map, padded_offsets, dev_status);
+  if (table_per(C) == kPerSmall)
+    hipLaunchKernelGGL(chunk_map_kernel<kPerSmall>, dim3(blocks), dim3(kCopyThreads), lds, s,
+                       split_sizes, sorted_idx, C, R, A, n_cap, out_cap, row_map, padded_offsets,
+                       dev_status);
+  else
+    hipLaunchKernelGGL(chunk_map_kernel<kPerLarge>, dim3(blocks), dim3(kCopyThreads), lds, s,
+                       split_sizes, sorted_idx, C, R, A, n_cap, out_cap, row_map, padded_offsets,
+                       dev_status);
   return hipGetLastError();
 }
 
@@ -700,11 +725,18 @@ hipError_t launch_sort_and_pad(const void *in, const void *probs, int prob_bytes
   auto *op = static_cast<uint8_t *>(out_probs);
   const bool stream = (int64_t)out_cap * row_units * unit_bytes * 2 > kStreamBytes;
   const RowDiv dv = row_div(row_units);
-#define MOE_FUSED(UT, NTL, NTS)                                                                \
-  hipLaunchKernelGGL((pad_fused_kernel<UT, NTL, NTS>), grid, block, lds, s,                    \
+#define MOE_FUSED_P(UT, NTL, NTS, PER)                                                         \
+  hipLaunchKernelGGL((pad_fused_kernel<UT, NTL, NTS, PER>), grid, block, lds, s,               \
                      static_cast<const UT *>(in), pp, prob_bytes, dv, split_sizes, sorted_idx, C, \
                      R, A, n_cap, out_cap, rows_per, static_cast<UT *>(out), op, row_map,      \
                      padded_offsets, dev_status)
+#define MOE_FUSED(UT, NTL, NTS)                                                                \
+  do {                                                                                         \
+    if (table_per(C) == kPerSmall)                                                             \
+      MOE_FUSED_P(UT, NTL, NTS, kPerSmall);                                                    \
+    else                                                                                       \
+      MOE_FUSED_P(UT, NTL, NTS, kPerLarge);                                                    \
+  } while (0)
   switch (unit_bytes) {
     case 16:
       if (stream)
@@ -716,6 +748,7 @@ hipError_t launch_sort_and_pad(const void *in, const void *probs, int prob_bytes
     default: MOE_FUSED(uint16_t, false, false); break;
   }
 #undef MOE_FUSED
+#undef MOE_FUSED_P
   return hipGetLastError();
 }
 
