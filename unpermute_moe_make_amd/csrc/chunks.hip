@@ -8,7 +8,7 @@
 // from the device-resident split sizes and chunk order -- input-order source
 // offsets, sorted-order prefixes, padded group starts -- with wave scans (DPP
 // row shifts and lane reads) and no workgroup barrier: after the metadata
-// loads it is a chain of LDS round trips and scans, about 2 us with the row
+// loads, three LDS round trips and three scans, about 1.5 us with the row
 // searches.  The workgroup then writes its slice of the padded destination ->
 // source row map by two binary searches per row.
 // Every workgroup validates the metadata the same way; on bad metadata the
