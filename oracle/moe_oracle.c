@@ -45,6 +45,14 @@
  * -ffp-contract=off keeps every a*b+c that is not an explicit fmaf() as
  * two roundings.
  *
+ * Parity unpinned at the bit level: the prob-grad dot products of
+ * oracle_unpermute_bwd and oracle_mask_unpermute_bwd (the pages leave the
+ * summation order open) and the router's softmax weights and gradients
+ * (fp32 exponentials the pages do not fix).  Each is computed here in fp64
+ * and rounded once; the GPU results are held to it within a stated bound.
+ * The tests pin the dots to a numpy fp64 dot of the widened rows and the
+ * router to a stable sort with a library softmax and its autograd.
+ *
  * Return codes (all functions): 0 ok, otherwise one of the ORC_* values.
  * Outputs are unspecified after an error.
  */
