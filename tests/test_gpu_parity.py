@@ -431,7 +431,8 @@ def test_permute_bwd_configs(m, name):
 @pytest.mark.parametrize("T,H,E,k", [(1, 8, 2, 1), (37, 7, 9, 3), (100, 24, 16, 2),
                                      (64, 64, 12, 9), (40, 136, 80, 64), (33, 2056, 12, 5),
                                      (20, 7168, 16, 4), (9, 20480, 8, 8), (17, 20481, 4, 2),
-                                     (300, 512, 32, 1)])
+                                     (300, 512, 32, 1), (50, 96, 6, 6), (3, 8, 64, 64),
+                                     (17, 1, 4, 2)])
 def test_row_kernels_edges(m, T, H, E, k):
     say(f"row kernels edge T={T} H={H} E={E} k={k}")
     w = workloads.random_routed(T, H, E, k, seed=H + k)
