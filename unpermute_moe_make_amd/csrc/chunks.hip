@@ -33,7 +33,9 @@ namespace {
 
 // Build-time tuning: units in flight per lane, and the streaming policy of
 // calls larger than kStreamBytes (bit 0: non-temporal loads, bit 1:
-// non-temporal stores).
+// non-temporal stores); for the one-launch sort-and-pad, the largest padded
+// buffer it takes (bytes; larger ones get the map + copy pair), its units
+// per lane per stage, and the workgroup count its rows per workgroup aim at.
 #ifndef MOE_PAD_ILP
 #define MOE_PAD_ILP 1
 #endif

@@ -4,10 +4,11 @@
 // gfx950 design.  One workgroup owns one token (and, for very long rows, a
 // slice of it: grid.y).  The first `k` lanes resolve the token's k
 // destination rows r_j = row_id_map[topk_idx[t][j]][t] (and its k weights)
-// into LDS with two parallel loads; meanwhile every lane has already issued
-// its loads of the token's own row where the kernel needs it.  Each lane then
-// moves VPT 16-byte vectors per row, all loads of a lane in flight before
-// its first store, so a wave keeps VPT*k*1 KiB outstanding.  Row offsets are
+// into LDS, lane j with two dependent loads; meanwhile every lane has
+// already issued its loads of the token's own row where the kernel needs it.
+// Each lane then moves VPT 16-byte vectors per row, all loads of a lane in
+// flight before its first store (a combine wave keeps VPT * k KiB of
+// gathers outstanding).  Row offsets are
 // 64-bit.  There is no LDS tiling of the rows themselves: each byte is read
 // once and written once, and HBM bandwidth is the bound.
 //
