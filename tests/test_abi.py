@@ -247,3 +247,19 @@ def test_next_rows_host_errors(lib):
                None) == MOE_ERR_NULL
     assert pms(None, 1, None, 0, None, None, 0, 64, 8, 0, None, None, None, None,
                None) == MOE_OK             # T == 0
+
+
+def test_bench_names_the_kernels_the_library_launches():
+    """bench.py names the kernels behind each op for its roofline entry; the
+    sort-and-pad is one fused launch up to the library's padded-buffer limit,
+    so the bench's copy of that limit must equal the library's default."""
+    import bench
+    src = open(os.path.join(ROOT, "unpermute_moe_make_amd", "csrc", "chunks.hip")).read()
+    mt = re.search(r"#define MOE_FUSED_MAX_BYTES \((\d+)ll << (\d+)\)", src)
+    assert mt, "fused sort-and-pad limit not found"
+    assert bench.FUSED_PAD_MAX_BYTES == int(mt.group(1)) << int(mt.group(2))
+    small = {"out_cap": 10240, "H": 2048}
+    large = {"out_cap": 34816, "H": 2048}
+    assert bench.op_kernels("sort_chunks_and_pad", small) == ["pad_fused_kernel"]
+    assert bench.op_kernels("sort_chunks_and_pad", large) == ["chunk_map_kernel",
+                                                              "pad_copy_kernel"]
