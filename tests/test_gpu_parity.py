@@ -642,10 +642,17 @@ def test_chunks_configs(m, name):
 @pytest.mark.parametrize("case", ["fp32_tokens", "fp16_probs", "odd_hidden", "align1_identity",
                                   "empty_group", "short_total", "big_cap", "all_empty",
                                   "h1536", "h7168", "h7000_fp32", "wide_two_launch",
-                                  "tall_one_launch"])
+                                  "tall_one_launch", "chunks512", "chunks2048",
+                                  "chunks512_two_launch"])
 def test_chunk_edges(m, case):
     say(f"chunk edge {case}")
     kw = dict(N=3000, seed=50, H=256, num_ranks=4, num_experts=6, align=16, num_empty=5)
+    if case == "chunks512":            # past 256 chunks: 8 per lane in the table build
+        kw.update(num_ranks=8, num_experts=64, num_empty=100)
+    if case == "chunks2048":           # the most chunks a call takes
+        kw.update(N=20000, num_ranks=16, num_experts=128, num_empty=300, align=8)
+    if case == "chunks512_two_launch":
+        kw.update(N=2100, H=32768, num_ranks=8, num_experts=64, num_empty=100)
     if case == "wide_two_launch":      # a 143 MB padded buffer: map and copy launched apart
         kw.update(N=2100, H=32768)
     if case == "tall_one_launch":      # 140000 short rows: 64 rows per fused workgroup
