@@ -14,10 +14,13 @@ k=6).  Every call goes straight through the C ABI (ctypes, precomputed
 device pointers) on torch's current stream.
 
 Printed: one JSON line with the throughput in algorithmic GB/s (bytes the
-method must move, divided by the measured step time), the per-op times
-measured with HIP events inside the timed region, the roofline of the
-dominant kernel, and the CPU oracle's rate on a bounded sample as a
-reported baseline.
+method must move, divided by the measured step time); the per-op times from
+a breakdown pass with HIP events around every op (before the timed region)
+and from a cold pass (the Infinity Cache flushed by a 512 MiB read before
+each op); the rate of the step replayed from a captured hipGraph; the
+roofline of the dominant kernel (its events inside the timed region, its
+HBM bytes from stored rocprofv3 counters while the kernel sources match);
+and the CPU oracle's rate on a bounded sample as a reported baseline.
 """
 from __future__ import annotations
 
