@@ -780,11 +780,16 @@ def test_chunk_negative_size_sets_status(m):
         assert bool((off == 0).all()) and bool((out_p == 0).all()), H
 
 
-def test_chunk_graph_replay(m):
-    """Sort-and-pad + restore captured once at the 32768-token size, replayed
-    with eight different split-size draws at fixed buffer sizes."""
-    cw = workloads.chunks32k(with_replays=True)
-    say("chunk graph replay 32768 tokens, 8 routings")
+@pytest.mark.parametrize("N", [8192, 32768])
+def test_chunk_graph_replay(m, N):
+    """Sort-and-pad + restore captured once, replayed with eight different
+    split-size draws at fixed buffer sizes: at 8192 tokens the one-launch
+    sort-and-pad, at 32768 the map + copy pair."""
+    if N == 32768:
+        cw = workloads.chunks32k(with_replays=True)
+    else:
+        cw = workloads.chunked(N, seed=3, replay_seeds=tuple(range(3000, 3008)), name="c8k")
+    say(f"chunk graph replay {N} tokens, 8 routings")
     x, probs = cw.x.to(DEV), cw.probs.to(DEV)
     sizes_s = cw.split_sizes.to(DEV)
     order = cw.sorted_idx.to(DEV)
