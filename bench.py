@@ -105,9 +105,16 @@ OP_KERNELS = {
     "sort_chunks_and_pad": ["chunk_map_kernel", "pad_copy_kernel"],
     "unpad_and_restore": ["restore_copy_kernel"],
 }
-# Padded buffers up to this size are written by one launch that also builds
-# the map (the library's threshold for fusing the two).
+# The library's launch rules that change which kernels an op runs: padded
+# buffers up to FUSED_PAD_MAX_BYTES are written by one launch that also
+# builds the map; a row map of at most ROWMAP_SINGLE_MAX_ENTRIES (token,
+# slot) entries and ROWMAP_SINGLE_MAX_EXPERTS experts (16-byte aligned
+# indices, as here) is one launch; past ROWMAP_FUSED_MAX_BLOCKS blocks of
+# 256 tokens a column scan runs between its two kernels.
 FUSED_PAD_MAX_BYTES = 128 << 20
+ROWMAP_SINGLE_MAX_ENTRIES = 4096
+ROWMAP_SINGLE_MAX_EXPERTS = 512
+ROWMAP_FUSED_MAX_BLOCKS = 64
 
 
 def op_kernels(op, cfg):
@@ -115,6 +122,12 @@ def op_kernels(op, cfg):
     if op == "sort_chunks_and_pad" and cfg.get("out_cap", 0) * cfg.get("H", 0) * 2 <= \
             FUSED_PAD_MAX_BYTES:
         return ["pad_fused_kernel"]
+    if op == "row_map":
+        T, k, E = cfg.get("T", 0), cfg.get("k", 0), cfg.get("E", 0)
+        if T * k <= ROWMAP_SINGLE_MAX_ENTRIES and E <= ROWMAP_SINGLE_MAX_EXPERTS:
+            return ["rowmap_single_kernel"]
+        if (T + 255) // 256 > ROWMAP_FUSED_MAX_BLOCKS:
+            return ["rowmap_count_kernel", "rowmap_colscan_kernel", "rowmap_write_kernel"]
     return OP_KERNELS[op]
 
 

@@ -263,3 +263,13 @@ def test_bench_names_the_kernels_the_library_launches():
     assert bench.op_kernels("sort_chunks_and_pad", small) == ["pad_fused_kernel"]
     assert bench.op_kernels("sort_chunks_and_pad", large) == ["chunk_map_kernel",
                                                               "pad_copy_kernel"]
+    rsrc = open(os.path.join(ROOT, "unpermute_moe_make_amd", "csrc", "row_map.hip")).read()
+    for name, val in (("MOE_SINGLE_MAX_ENTRIES", bench.ROWMAP_SINGLE_MAX_ENTRIES),
+                      ("MOE_FUSED_MAX_BLOCKS", bench.ROWMAP_FUSED_MAX_BLOCKS)):
+        mt = re.search(r"#define " + name + r" (\d+)", rsrc)
+        assert mt and int(mt.group(1)) == val, name
+    mt = re.search(r"constexpr int kSingleMaxExperts = (\d+);", rsrc)
+    assert mt and int(mt.group(1)) == bench.ROWMAP_SINGLE_MAX_EXPERTS
+    assert bench.op_kernels("row_map", {"T": 16, "k": 4, "E": 32}) == ["rowmap_single_kernel"]
+    assert bench.op_kernels("row_map", {"T": 4096, "k": 6, "E": 64}) == [
+        "rowmap_count_kernel", "rowmap_write_kernel"]
