@@ -1,0 +1,91 @@
+"""The oracle's pins catch plausible mistakes: each case plants one mistake in
+a copy of the oracle's C source (on the CPU, in a temporary directory),
+builds it, and runs the whole pin suite against it in a child process; some
+pin must fail.  The checked-in oracle is never touched.
+
+The mistakes are the ones an implementation of the pages' steps could
+plausibly make: a fused multiply-add split into two roundings, the slot
+order reversed, the accumulator started at -0, ties rounded away from even,
+a wrong prob index, the counting sort walked backwards, one group of
+padding too many, a transposed chunk index, a dropped prob in the act-grad
+scatter, the EP ranks added in reverse, the EP partials not rounded, and a
+gradient sum that overwrites instead of accumulating.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ORACLE_C = os.path.join(ROOT, "oracle", "moe_oracle.c")
+PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+
+_UNPERMUTE_SLOT = (
+    "for (int j = 0; j < k; j++) {\n"
+    "                int64_t r;\n"
+    "                int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);\n"
+    "                if (s) return s;\n"
+    "                float p = probs ? probs[(int64_t)t * k + j] : 1.0f;\n"
+    "                acc = fmaf(")
+
+MUTATIONS = [
+    ("fma_split",
+     "acc = fmaf(p, bf16_to_f32(in[r * H + h]), acc);",
+     "acc = p * bf16_to_f32(in[r * H + h]) + acc;"),
+    ("slot_order_reversed",
+     _UNPERMUTE_SLOT,
+     _UNPERMUTE_SLOT.replace("for (int j = 0; j < k; j++) {\n",
+                             "for (int jj = 0; jj < k; jj++) {\n"
+                             "                int j = k - 1 - jj;\n")),
+    ("negative_zero_start",
+     "float acc = +0.0f;\n            " + _UNPERMUTE_SLOT,
+     "float acc = -0.0f;\n            " + _UNPERMUTE_SLOT),
+    ("ties_away_from_even",
+     "if (kept & 1u) kept += 1u;    /* exactly halfway: to even        */",
+     "kept += 1u;"),
+    ("prob_index",
+     "float p = probs ? probs[(int64_t)t * k + j] : 1.0f;\n                acc = fmaf(",
+     "float p = probs ? probs[(int64_t)t * k] : 1.0f;\n                acc = fmaf("),
+    ("row_map_walked_backwards",
+     "    for (int64_t i = 0; i < npairs; i++) {\n        int t = pair_token[i];",
+     "    for (int64_t ii = 0; ii < npairs; ii++) {\n"
+     "        int64_t i = npairs - 1 - ii;\n        int t = pair_token[i];"),
+    ("padding_one_group_too_many",
+     "int64_t padded = ((n_g + A - 1) / A) * A;",
+     "int64_t padded = (n_g / A + 1) * A;"),
+    ("chunk_index_transposed",
+     "row_map[d] = (int32_t)(src_off[c] + i);",
+     "row_map[d] = (int32_t)(src_off[q] + i);"),
+    ("act_grad_drops_prob",
+     "float prod = g * p;          /* one fp32 rounding */",
+     "float prod = g;"),
+    ("ep_ranks_reversed",
+     "for (int rank = 0; rank < ep_size; rank++) {",
+     "for (int rank = ep_size - 1; rank >= 0; rank--) {"),
+    ("ep_partials_unrounded",
+     "if (bf16_partials) partial = bf16_to_f32(f32_to_bf16_rne(partial));",
+     "(void)bf16_partials;"),
+    ("grad_sum_overwrites",
+     "acc = acc + bf16_to_f32(d_out[r * H + h]);",
+     "acc = bf16_to_f32(d_out[r * H + h]);"),
+]
+
+_RUNNER = (
+    "import sys; sys.path.insert(0, sys.argv[1]); import oracle; oracle._LIB = sys.argv[2]; "
+    "import pytest; sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', sys.argv[3]]))")
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    src = open(ORACLE_C).read()
+    assert src.count(old) == 1, f"{name}: the line to change is not unique in the oracle"
+    mutant_c = tmp_path / "moe_oracle.c"
+    mutant_c.write_text(src.replace(old, new, 1))
+    mutant_so = tmp_path / "liboracle_mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+                           "-shared", "-fPIC", str(mutant_c), "-o", str(mutant_so), "-lm"])
+    r = subprocess.run([sys.executable, "-c", _RUNNER, ROOT, str(mutant_so), PINS],
+                       capture_output=True, text=True, timeout=600, cwd=str(tmp_path))
+    assert r.returncode == 1, (
+        f"{name}: no pin failed (exit {r.returncode})\n{r.stdout[-2000:]}\n{r.stderr[-2000:]}")

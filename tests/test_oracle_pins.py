@@ -600,6 +600,18 @@ def test_unpermute_ep_crafted_rank_order():
     assert _one_token_unpermute(x, None) == 0x0000
 
 
+def test_unpermute_ep_crafted_ranks_added_in_ascending_order():
+    """Partials 2^24, 1, -2^24 on ranks 0, 1, 2 (one slot each): added from +0
+    in ascending rank order ([MCORE-BI] unpermute_with_bf16_rank_partials, the
+    rank-ordered cross-rank sum), fp32 rounds 2^24 + 1 back to 2^24 (a tie, to
+    even) and the result is 0; in descending order it would be 1.  In fp64 the
+    sum is exact in any order: 1."""
+    x = [2.0 ** 24, 1.0, -(2.0 ** 24)]
+    for partials in (True, False):
+        assert _one_token_ep(x, None, [0, 1, 2], 3, 3, partials, False) == 0x0000
+        assert _one_token_ep(x, None, [0, 1, 2], 3, 3, partials, True) == 0x3F80
+
+
 def test_unpermute_ep_crafted_fp64_cross_sum():
     """Partials 1+2^-8, 2^-30, 2^-30 (fp32 partials): the fp32 rank sum drops
     the small terms and lands on the bf16 tie 1+2^-8 (-> even, 0x3F80); the
