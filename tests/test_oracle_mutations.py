@@ -4,12 +4,14 @@ builds it, and runs the whole pin suite against it in a child process; some
 pin must fail.  The checked-in oracle is never touched.
 
 The mistakes are the ones an implementation of the pages' steps could
-plausibly make: a fused multiply-add split into two roundings, the slot
-order reversed, the accumulator started at -0, ties rounded away from even,
-a wrong prob index, the counting sort walked backwards, one group of
-padding too many, a transposed chunk index, a dropped prob in the act-grad
-scatter, the EP ranks added in reverse, the EP partials not rounded, and a
-gradient sum that overwrites instead of accumulating.
+plausibly make, in every oracle function: the combine's arithmetic (a fused
+multiply-add split, slot order reversed, a -0 start, ties away from even, a
+wrong prob index), the counting sort walked backwards, the chunk map's
+padding and indexing, the backward scatters and sums, the EP rank order,
+partial rounding and fp64 sum, the router's tie-break, normalisation and
+gradient, the mask map's row order and dropping, the zero-prob rule, the
+mask combine's unfused arithmetic and gradient dot, the scale rows, the
+restore's zero tail, and the fp64 -> bf16 rounding.
 """
 import os
 import subprocess
@@ -69,6 +71,45 @@ MUTATIONS = [
     ("grad_sum_overwrites",
      "acc = acc + bf16_to_f32(d_out[r * H + h]);",
      "acc = bf16_to_f32(d_out[r * H + h]);"),
+    ("router_ties_to_higher_expert",
+     "if (best < 0 || v > bv) { best = e; bv = v; }",
+     "if (best < 0 || v >= bv) { best = e; bv = v; }"),
+    ("router_weights_unnormalised",
+     "double w = exp(lv[j] - lv[0]) / sum;",
+     "double w = exp(lv[j] - lv[0]);"),
+    ("router_grad_without_dot",
+     "w * (dp - dot));",
+     "w * dp);"),
+    ("mask_map_rows_ascending",
+     "return (x->row < y->row) - (x->row > y->row);",
+     "return (x->row > y->row) - (x->row < y->row);"),
+    ("mask_drop_off_by_one",
+     "if (dense[i] >= num_out) dense[i] = -1;",
+     "if (dense[i] > num_out) dense[i] = -1;"),
+    ("mask_zero_prob_rule_lost",
+     "zero_row = p == 0.0f;\n            }\n            for (int h = 0; h < H; h++)",
+     "zero_row = 0;\n            }\n            for (int h = 0; h < H; h++)"),
+    ("scaled_mask_zero_prob_rule_lost",
+     "zero_row = p == 0.0f;\n            }\n            if (zero_row)",
+     "zero_row = 0;\n            }\n            if (zero_row)"),
+    ("mask_combine_fused",
+     "if (merging_probs) v = v * merging_probs[(int64_t)t * E + e];\n                acc = acc + v;",
+     "acc = merging_probs ? fmaf(v, merging_probs[(int64_t)t * E + e], acc) : acc + v;"),
+    ("mask_grad_dot_uses_product",
+     "dot += (double)bf16_to_f32(fwd_in[(int64_t)row * H + h]) * (double)g;",
+     "dot += (double)bf16_to_f32(fwd_in[(int64_t)row * H + h]) * (double)prod;"),
+    ("scale_row_of_token_zero",
+     "copy_bytes(out_scale + r * scale_row_bytes, scale + (int64_t)t * scale_row_bytes,",
+     "copy_bytes(out_scale + r * scale_row_bytes, scale,"),
+    ("restore_tail_not_zeroed",
+     "for (int64_t s = n_act; s < N_cap; s++) {",
+     "for (int64_t s = N_cap; s < N_cap; s++) {"),
+    ("f64_to_bf16_one_bit_too_many",
+     "int qexp = e - 8;",
+     "int qexp = e - 9;"),
+    ("unpermute_ep_fp64_sum_in_fp32",
+     "total64 = total64 + (double)partial;",
+     "total64 = (float)(total64 + (double)partial);"),
 ]
 
 _RUNNER = (
