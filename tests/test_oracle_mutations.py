@@ -110,6 +110,24 @@ MUTATIONS = [
     ("unpermute_ep_fp64_sum_in_fp32",
      "total64 = total64 + (double)partial;",
      "total64 = (float)(total64 + (double)partial);"),
+    ("permute_bwd_prob_gather_index",
+     "d_probs[(int64_t)t * k + j] = d_out_probs[r];",
+     "d_probs[(int64_t)t * k + j] = d_out_probs[(int64_t)t * k + j];"),
+    ("chunk_order_repeat_accepted",
+     "if (c < 0 || c >= C || seen[c]) { status = ORC_BAD_CHUNKS; goto done; }",
+     "if (c < 0 || c >= C) { status = ORC_BAD_CHUNKS; goto done; }"),
+    ("row_map_repeat_accepted",
+     "if (row_id_map[slot] != -1) { status = ORC_DUP_EXPERT; break; }",
+     ""),
+    ("mask_offsets_ignore_dropping",
+     "if (expert_offsets) expert_offsets[e] = (int32_t)(num_out >= 0 && row > num_out ? num_out : row);",
+     "if (expert_offsets) expert_offsets[e] = (int32_t)row;"),
+    ("chunk_map_overflow_accepted",
+     "    if (total > N_cap) { status = ORC_OVERFLOW; goto done; }",
+     ""),
+    ("restore_overflow_accepted",
+     "    if (n_act > N_cap) return ORC_OVERFLOW;\n    return restore_copy(",
+     "    return restore_copy("),
 ]
 
 _RUNNER = (

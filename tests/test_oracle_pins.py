@@ -446,6 +446,11 @@ def test_chunk_restore_zero_tail_and_errors():
         oracle.chunk_map(s, q, 2, 4, 9, 7)
     with pytest.raises(oracle.OracleError):      # tokens exceed the input buffer
         oracle.chunk_map(s, q, 2, 4, 5, 12)
+    # the restore's token total past its buffer is the same capacity overflow
+    # (reading Q14: capacity overflow is an error, outputs unspecified)
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.unpad_and_restore_chunks(out, None, rm, np.array([2, 1, 0, 7], np.int32), 9)
+    assert ei.value.code == 6
     # an all-empty group takes no rows
     s0 = np.array([0, 0, 2, 1], np.int32)
     _, offs0 = oracle.chunk_map(s0, np.arange(4, dtype=np.int32), 2, 4, 3, 8)
