@@ -125,6 +125,20 @@ MUTATIONS = [
     ("chunk_map_overflow_accepted",
      "    if (total > N_cap) { status = ORC_OVERFLOW; goto done; }",
      ""),
+    ("row_map_bad_expert_accepted",
+     "        if (pair_expert[i] < 0 || pair_expert[i] >= E) return ORC_BAD_EXPERT;",
+     ""),
+    ("mask_unpermuted_probs_zero",
+     "unpermuted_probs[(int64_t)t * E + e] = permuted_probs[row];",
+     "unpermuted_probs[(int64_t)t * E + e] = 0.0f;"),
+    ("pad_probs_from_destination_index",
+     "memcpy(out_probs + (int64_t)d * prob_bytes, probs + (int64_t)s * prob_bytes,",
+     "memcpy(out_probs + (int64_t)d * prob_bytes, probs + (int64_t)d * prob_bytes,"),
+    ("scaled_mask_scale_skipped_on_zero_prob",
+     "            if (scale && out_scale && scale_row_bytes > 0)\n"
+     "                copy_bytes(out_scale + (int64_t)row * scale_row_bytes,",
+     "            if (scale && out_scale && scale_row_bytes > 0 && !zero_row)\n"
+     "                copy_bytes(out_scale + (int64_t)row * scale_row_bytes,"),
     ("restore_overflow_accepted",
      "    if (n_act > N_cap) return ORC_OVERFLOW;\n    return restore_copy(",
      "    return restore_copy("),
