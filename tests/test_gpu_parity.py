@@ -516,6 +516,43 @@ def test_bitwise_repeatable(m):
                 assert torch.equal(a, b)
 
 
+def test_two_streams_at_once(m):
+    """The library keeps no state between calls: two routed chains with
+    different shapes and routings, each with its own workspace, enqueued
+    alternately on two streams so that they overlap, give the oracle's
+    results on both."""
+    say("two routed chains on two streams at once")
+    cases = [(700, 2048, 64, 6, 31), (900, 1536, 32, 4, 32)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    work, outs = [], []
+    for (T, H, E, k, seed) in cases:
+        w = workloads.random_routed(T, H, E, k, seed=seed)
+        x, idx, probs, dy = to_dev(w)
+        ws = torch.empty(m.moe_make_row_id_map_workspace_bytes(T, k, E), dtype=torch.uint8,
+                         device=DEV)
+        work.append((w, x, idx, probs, ws))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, (w, x, idx, probs, ws) in enumerate(work):
+            with torch.cuda.stream(streams[i]):
+                rm, off = m.moe_make_row_id_map(idx, w.num_experts, workspace=ws)
+                out, out_p = m.moe_permute(x, idx, rm, probs)
+                y = m.moe_unpermute(out, idx, rm, probs)
+                if rep == 2:
+                    outs.append((rm, out, out_p, y))
+    torch.cuda.synchronize()
+    for (w, _, _, _, _), (rm, out, out_p, y) in zip(work, outs):
+        ib, pb = w.topk_idx.numpy(), w.probs.numpy()
+        ref_map, _ = oracle.row_id_map(ib, w.num_experts)
+        assert_bits_equal(rm.cpu().numpy(), ref_map, "row_id_map")
+        o, op = oracle.permute(workloads.bf16_bits(w.x), pb, ib, ref_map)
+        assert_bits_equal(bits(out), o, "permute")
+        assert_bits_equal(out_p.cpu().numpy(), op, "permuted probs")
+        assert_bits_equal(bits(y), oracle.unpermute(o, pb, ib, ref_map), "unpermute")
+
+
 def test_graph_replay_routing(m):
     """Map + permute + unpermute captured once, replayed with new routings."""
     T, H, E, k = 1024, 1024, 32, 4
