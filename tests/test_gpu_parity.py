@@ -456,6 +456,11 @@ def test_row_kernels_edges(m, T, H, E, k):
     assert_bits_equal(bits(d_in), ref_in, "unpermute_bwd")
     rows = oracle_rows(ib, ref_map)
     dprob_ok(d_p.cpu().numpy(), bits(P)[rows], workloads.bf16_bits(w.dy), ref_p)
+    # without prob grads a long row may be split over several workgroups
+    d_in2, none = m.moe_unpermute_bwd(dy, idx, rm, probs, P, probs_grad=False,
+                                      d_in=sentinel_bf16((T * k, H)))
+    assert none is None
+    assert_bits_equal(bits(d_in2), ref_in, "unpermute_bwd without prob grads")
     dpp = torch.randn(T * k, generator=torch.Generator().manual_seed(3)).to(DEV)
     d_x, d_pp = m.moe_permute_bwd(P, idx, rm, dpp, d_x=sentinel_bf16((T, H)),
                                   d_probs=sentinel_f32((T, k)))
