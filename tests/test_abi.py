@@ -273,3 +273,34 @@ def test_bench_names_the_kernels_the_library_launches():
     assert bench.op_kernels("row_map", {"T": 16, "k": 4, "E": 32}) == ["rowmap_single_kernel"]
     assert bench.op_kernels("row_map", {"T": 4096, "k": 6, "E": 64}) == [
         "rowmap_count_kernel", "rowmap_write_kernel"]
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include "moe_perm.h"
+int main(void) {
+    /* host checks only: each call is rejected before any HIP call */
+    int a = moe_permute(0, 0, 0, 0, 4, 64, 2, 8, 8, 0, 0, 0, 0);
+    int b = moe_sort_chunks_and_pad(0, 0, 2, 4, 100, 64, 0, 0, 128, 8, 128, 2048, 0, 0, 0, 0,
+                                    0, 0);
+    size_t ws = moe_make_row_id_map_workspace_bytes(4096, 6, 64);
+    printf("%d %d %zu %s\n", a, b, ws, moe_status_string(a));
+    return !(a == MOE_ERR_NULL && b == MOE_ERR_NULL && ws > 0);
+}
+"""
+
+
+def test_plain_c_caller(tmp_path):
+    """The boundary is a C ABI: a C99 program built by gcc against the header
+    links the library and gets its host-side answers (no GPU involved)."""
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.join(ROOT, "unpermute_moe_make_amd")
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror",
+                           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                           "-I", "/opt/rocm/include", str(src), "-L", libdir, "-lmoeperm",
+                           "-Wl,-rpath," + libdir, "-o", str(exe)])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.split()[:2] == [str(MOE_ERR_NULL), str(MOE_ERR_NULL)]
