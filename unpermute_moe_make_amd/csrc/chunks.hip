@@ -20,7 +20,7 @@
 //
 // Copies.  Both walk a flat index over (row, unit) with 16-byte units where
 // the row allows, consecutive lanes on consecutive units, each lane's units
-// (one in the pad copy, three in the restore) loaded before any is stored.
+// (one in the pad copy, four in the restore) loaded before any is stored.
 // The pad copy writes every destination row (zeros where the map is -1).
 // The restore scatters every mapped row
 // back to its source and writes zeros to the rows past the token total,
@@ -40,7 +40,7 @@ namespace {
 #define MOE_PAD_ILP 1
 #endif
 #ifndef MOE_RESTORE_ILP
-#define MOE_RESTORE_ILP 3
+#define MOE_RESTORE_ILP 4
 #endif
 #ifndef MOE_PAD_STREAM
 #define MOE_PAD_STREAM 2
@@ -535,61 +535,92 @@ __device__ __forceinline__ int64_t wave_total(const int32_t *__restrict__ sizes,
   return total;
 }
 
-// Flat index over [0, max(out_cap, n_cap)) x W: unit (i, c) scatters padded
-// row i (if mapped) and zero-fills restored row i (if past the token total).
+// Flat index over [0, max(out_cap, n_cap)) x W: unit (d, c) scatters padded
+// row d (if mapped) and zero-fills restored row d (if past the token total).
 // NTL / NTS: stream the (dense, sequential) padded source rows / the
 // restored rows.
-template <typename U, bool NTL, bool NTS, bool IDX64>
+// A workgroup's units are one contiguous range, so the map entries, padded
+// rows and probs it reads are slices, read through range-checked buffer
+// descriptors: a lane loads all its map entries, then all its rows and
+// probs (an unmapped unit's offset lies past the slice, and its load returns
+// zero without touching memory), and stores only after that.  With the row
+// loads under a branch on the map entry, each lane waited for one unit's
+// row before the next unit's map entry arrived (the vector memory counter
+// retires in issue order), one row in flight per lane.  PB: bytes per prob
+// (2 or 4; a compile-time width keeps the prob loads branch-free too).
+template <typename U, int PB, bool NTL, bool NTS, bool IDX64>
 __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
-    const U *__restrict__ in, const uint8_t *__restrict__ probs, int prob_bytes, RowDiv dv,
+    const U *__restrict__ in, const uint8_t *__restrict__ probs, RowDiv dv,
     const int32_t *__restrict__ row_map, const int32_t *__restrict__ split_sizes, int C,
     int out_cap, int n_cap, U *__restrict__ out, uint8_t *__restrict__ out_probs,
     int32_t *__restrict__ dev_status) {
+  constexpr int kSpan = kCopyThreads * kRestoreIlp;
   const int64_t W = dv.W;
   const int64_t rows = max(out_cap, n_cap);
   const int64_t total = rows * W;
-  const int64_t base0 = spill_block() * kCopyThreads * kRestoreIlp;
+  const int64_t base0 = spill_block() * kSpan;
   if (base0 >= total) return;  // a workgroup past the end
-  const int64_t base = base0 + threadIdx.x;
+  // Slices: padded rows [d_first, d_end) of row_map and probs, units
+  // [base0, base0 + n_in) of in; each at most kSpan entries.
+  int64_t d_first, d_last, c_unused;
+  split_unit<IDX64>(base0, dv, d_first, c_unused);
+  split_unit<IDX64>(min(total, base0 + kSpan) - 1, dv, d_last, c_unused);
+  const int64_t d_end = min((int64_t)out_cap, d_last + 1);
+  const int64_t n_map = max((int64_t)0, d_end - d_first);
+  const int64_t n_in = max((int64_t)0, min((int64_t)out_cap * W, base0 + kSpan) - base0);
+  const bool with_probs = out_probs != nullptr;
+  // an empty slice (nothing of it is read) still gets a valid base address
+  void *const any = const_cast<int32_t *>(split_sizes);
+  const __amdgpu_buffer_rsrc_t map_r = slice_rsrc(
+      n_map > 0 ? (void *)(const_cast<int32_t *>(row_map) + d_first) : any, (uint32_t)(n_map * 4));
+  const __amdgpu_buffer_rsrc_t in_r = slice_rsrc(
+      n_in > 0 ? (void *)(const_cast<U *>(in) + base0) : any, (uint32_t)(n_in * sizeof(U)));
+  const bool prob_slice = with_probs && n_map > 0;
+  const __amdgpu_buffer_rsrc_t prob_r =
+      slice_rsrc(prob_slice ? (void *)(const_cast<uint8_t *>(probs) + d_first * PB) : any,
+                 prob_slice ? (uint32_t)(n_map * PB) : 0u);
+  const int tid = threadIdx.x;
+  int64_t d[kRestoreIlp], c[kRestoreIlp];
+  int32_t s[kRestoreIlp];
+#pragma unroll
+  for (int i = 0; i < kRestoreIlp; i++) {
+    split_unit<IDX64>(base0 + tid + i * kCopyThreads, dv, d[i], c[i]);
+    const uint32_t off = d[i] < d_end ? (uint32_t)((d[i] - d_first) * 4) : kNoRow;
+    s[i] = (int32_t)buf_load<false, uint32_t>(map_r, off);
+  }
   U v[kRestoreIlp];
-  int32_t dst[kRestoreIlp];
-  int64_t dd[kRestoreIlp], cc[kRestoreIlp];
+  uint32_t pv[kRestoreIlp];
   int bad = 0;
 #pragma unroll
   for (int i = 0; i < kRestoreIlp; i++) {
-    const int64_t u = base + (int64_t)i * kCopyThreads;
-    dst[i] = -1;
-    dd[i] = -1;
-    cc[i] = 0;
-    if (u < total) {
-      int64_t d, c;
-      split_unit<IDX64>(u, dv, d, c);
-      dd[i] = d;
-      cc[i] = c;
-      if (d < out_cap) {
-        const int32_t s = row_map[d];
-        if (s >= n_cap) bad |= MOE_DEV_BAD_ROW;
-        if (s >= 0 && s < n_cap) {
-          dst[i] = s;
-          v[i] = ld_row<NTL>(in + u);
-          if (c == 0 && out_probs != nullptr) copy_prob(probs, d, out_probs, s, prob_bytes);
-        }
-      }
-    }
+    const int32_t si = d[i] < d_end ? s[i] : -1;
+    if (si >= n_cap) bad |= MOE_DEV_BAD_ROW;
+    const bool mapped = si >= 0 && si < n_cap;
+    s[i] = mapped ? si : -1;
+    const uint32_t off = mapped ? (uint32_t)((tid + i * kCopyThreads) * sizeof(U)) : kNoRow;
+    v[i] = buf_load<NTL, U>(in_r, off);
+    const uint32_t poff = mapped && c[i] == 0 ? (uint32_t)((d[i] - d_first) * PB) : kNoRow;
+    if constexpr (PB == 4)
+      pv[i] = buf_load<false, uint32_t>(prob_r, poff);
+    else
+      pv[i] = buf_load<false, uint16_t>(prob_r, poff);
   }
   const int64_t n_act = wave_total(split_sizes, C);
   if (n_act > n_cap) bad |= MOE_DEV_OVERFLOW;
 #pragma unroll
   for (int i = 0; i < kRestoreIlp; i++) {
-    const int64_t u = base + (int64_t)i * kCopyThreads;
-    if (u < total) {
-      const int64_t d = dd[i];
-      const int64_t c = cc[i];
-      if (dst[i] >= 0) st_row<NTS>(v[i], out + (int64_t)dst[i] * W + c);
-      if (d >= n_act && d < n_cap) {
-        st_row<NTS>(zero_unit<U>(), out + u);
-        if (c == 0 && out_probs != nullptr) copy_prob(probs, -1, out_probs, d, prob_bytes);
+    if (s[i] >= 0) {
+      st_row<NTS>(v[i], out + (int64_t)s[i] * W + c[i]);
+      if (c[i] == 0 && with_probs) {
+        if constexpr (PB == 4)
+          reinterpret_cast<uint32_t *>(out_probs)[s[i]] = pv[i];
+        else
+          reinterpret_cast<uint16_t *>(out_probs)[s[i]] = (uint16_t)pv[i];
       }
+    }
+    if (d[i] >= n_act && d[i] < n_cap) {  // then the unit is below total
+      st_row<NTS>(zero_unit<U>(), out + d[i] * W + c[i]);
+      if (c[i] == 0 && with_probs) copy_prob(probs, -1, out_probs, d[i], PB);
     }
   }
   report(dev_status, bad);
@@ -670,16 +701,25 @@ hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes
   const bool stream = ((int64_t)out_cap + n_cap) * row_units * unit_bytes > kStreamBytes;
   const RowDiv dv = row_div(row_units);
   const bool idx64 = blocks * kCopyThreads * kRestoreIlp >= ((int64_t)1 << 32);
-#define MOE_RESTORE(UT, NTL, NTS)                                                              \
+  // without probs nothing reads or writes them, whatever the width
+  const bool half_probs = out_probs != nullptr && prob_bytes == 2;
+#define MOE_RESTORE_PB(UT, PB, NTL, NTS)                                                       \
   do {                                                                                         \
     if (idx64)                                                                                 \
-      hipLaunchKernelGGL((restore_copy_kernel<UT, NTL, NTS, true>), grid, block, 0, s,         \
-                         static_cast<const UT *>(in), pp, prob_bytes, dv, row_map, split_sizes, \
-                         C, out_cap, n_cap, static_cast<UT *>(out), op, dev_status);           \
+      hipLaunchKernelGGL((restore_copy_kernel<UT, PB, NTL, NTS, true>), grid, block, 0, s,     \
+                         static_cast<const UT *>(in), pp, dv, row_map, split_sizes, C,         \
+                         out_cap, n_cap, static_cast<UT *>(out), op, dev_status);              \
     else                                                                                       \
-      hipLaunchKernelGGL((restore_copy_kernel<UT, NTL, NTS, false>), grid, block, 0, s,        \
-                         static_cast<const UT *>(in), pp, prob_bytes, dv, row_map, split_sizes, \
-                         C, out_cap, n_cap, static_cast<UT *>(out), op, dev_status);           \
+      hipLaunchKernelGGL((restore_copy_kernel<UT, PB, NTL, NTS, false>), grid, block, 0, s,    \
+                         static_cast<const UT *>(in), pp, dv, row_map, split_sizes, C,         \
+                         out_cap, n_cap, static_cast<UT *>(out), op, dev_status);              \
+  } while (0)
+#define MOE_RESTORE(UT, NTL, NTS)                                                              \
+  do {                                                                                         \
+    if (half_probs)                                                                            \
+      MOE_RESTORE_PB(UT, 2, NTL, NTS);                                                         \
+    else                                                                                       \
+      MOE_RESTORE_PB(UT, 4, NTL, NTS);                                                         \
   } while (0)
   switch (unit_bytes) {
     case 16:
@@ -691,6 +731,7 @@ hipError_t launch_restore_copy(const void *in, const void *probs, int prob_bytes
     case 4: MOE_RESTORE(uint32_t, false, false); break;
     default: MOE_RESTORE(uint16_t, false, false); break;
   }
+#undef MOE_RESTORE_PB
 #undef MOE_RESTORE
   return hipGetLastError();
 }
