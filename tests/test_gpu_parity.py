@@ -802,6 +802,57 @@ def test_chunk_no_source_rows(m, out_cap):
     assert back.shape == (0, H) and back_p.shape == (0,) and int(st.item()) == 0
 
 
+@pytest.mark.parametrize("H,dtype,pkind,n_cap,n_act,extra", [
+    (1, torch.bfloat16, "f16", 3000, 500, 7),     # 2-byte units, one per row
+    (3, torch.bfloat16, "f32", 2500, 700, 0),     # odd row width
+    (8, torch.bfloat16, None, 4096, 4000, 300),   # one 16-byte unit per row
+    (5, torch.float32, "f32", 1500, 1499, 1),     # 4-byte units
+    (2048, torch.bfloat16, "f16", 300, 120, 64),  # 256 units per row
+    (8, torch.bfloat16, "f32", 5000, 0, 0),       # no tokens: all zero tail
+])
+def test_restore_slice_edges(m, H, dtype, pkind, n_cap, n_act, extra):
+    """The restore reads each workgroup's map entries, padded rows and probs
+    as slices of one contiguous range of units: slices that straddle the end
+    of the padded buffer, restored buffers longer than the padded one (the
+    zero tail past the token total), rows of one unit (a workgroup spans
+    hundreds of rows), and every prob width, each against the oracle."""
+    say(f"restore slice edges H={H} dtype={dtype} probs={pkind} n_cap={n_cap} n_act={n_act}")
+    g = torch.Generator().manual_seed(n_cap + H)
+    R, E, A = 4, 8, 8
+    x = torch.randn(n_cap, H, generator=g).to(dtype)
+    probs = None
+    if pkind is not None:
+        probs = torch.rand(n_cap, generator=g)
+        if pkind == "f16":
+            probs = probs.to(torch.float16)
+    sizes = workloads.chunk_sizes(n_act, R, E, 3, g)
+    order = workloads.expert_major_order(R, E)
+    out_cap = workloads.padded_capacity(n_act, E, A) + extra
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sd = sizes.to(DEV)
+    out, out_p, rm, _ = m.moe_sort_chunks_and_pad(
+        x.to(DEV), sd, order.to(DEV), R, A, out_cap, None if probs is None else probs.to(DEV),
+        dev_status=st)
+    pr = None if probs is None else _raw(probs)
+    r_out, r_p, r_rm, _ = oracle.sort_chunks_and_pad(_raw(x), pr, sizes.numpy(), order.numpy(),
+                                                     R, A, out_cap)
+    assert_bits_equal(rm.cpu().numpy(), r_rm, "row_map")
+    assert_bits_equal(_raw(out), r_out, "padded rows")
+    nan_fill = torch.full((n_cap, H), float("nan"), dtype=dtype, device=DEV)
+    nan_probs = None if probs is None else torch.full((n_cap,), float("nan"), dtype=probs.dtype,
+                                                      device=DEV)
+    back, back_p = m.moe_unpad_and_restore_chunks(out, rm, sd, n_cap, out_p, out=nan_fill,
+                                                  out_probs=nan_probs, dev_status=st)
+    ref_b, ref_bp = oracle.unpad_and_restore_chunks(r_out, r_p, r_rm, sizes.numpy(), n_cap)
+    assert_bits_equal(_raw(back), ref_b, "restored rows")
+    if probs is not None:
+        assert_bits_equal(_raw(back_p), ref_bp, "restored probs")
+    else:
+        assert back_p is None
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+
+
 def test_chunk_negative_size_sets_status(m):
     """A negative chunk size is bad metadata: the status says so and the whole
     padded buffer is zero and unmapped, through the one-launch path (small
