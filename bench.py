@@ -2,25 +2,38 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one pass of the whole routed path over one batch of synthetic
-input already resident in HBM:
-  routed workloads (finegrain, skewed, tiny):
-      row map -> permute (+probs) -> weighted unpermute
-      -> unpermute backward (act grad + prob grads) -> permute backward
-  chunk workloads (chunks8k, chunks32k):
-      sort-and-pad (+probs) -> unpad-and-restore (+probs)
-The default workload is the fine-grained MoE layer (T=4096, H=2048, E=64,
-k=6).  Every call goes straight through the C ABI (ctypes, precomputed
-device pointers) on torch's current stream.
+The metric is the permute + unpermute roundtrip (GB/s of algorithmic bytes,
+% of the 8 TB/s HBM peak, us per call).  For a routed workload (default: the
+skewed MoE layer, T=16384, H=7168, E=256, k=8) a timed step is one roundtrip
+over one batch of synthetic input already resident in HBM:
 
-Printed: one JSON line with the throughput in algorithmic GB/s (bytes the
-method must move, divided by the measured step time); the per-op times from
-a breakdown pass with HIP events around every op (before the timed region)
-and from a cold pass (the Infinity Cache flushed by a 512 MiB read before
-each op); the rate of the step replayed from a captured hipGraph; the
-roofline of the dominant kernel (its events inside the timed region, its
-HBM bytes from stored rocprofv3 counters while the kernel sources match);
-and the CPU oracle's rate on a bounded sample as a reported baseline.
+    permute (+probs) -> fixed slot-order weighted unpermute
+
+and `value` is the roundtrip's bytes divided by the wall time per roundtrip
+over exactly K steps.  For a chunk workload (chunks8k, chunks32k) the step is
+sort-and-pad (+probs) -> unpad-and-restore (+probs).  Every call goes
+straight through the C ABI (ctypes, precomputed device pointers) on torch's
+current stream.
+
+Also printed in the same JSON line, all timed with HIP events on that stream:
+  per_op          every op of the whole routed path (row map, permute,
+                  unpermute, unpermute backward, permute backward), warm;
+  per_op_cold     the same ops, each after a 512 MiB read of an unrelated
+                  buffer (nothing of the op's inputs left in the Infinity
+                  Cache);
+  roundtrip_cold  the roundtrip after such a read, timed as one unit;
+  full_step       the whole routed path (all five ops) timed like the step;
+  graph_replay    the roundtrip captured in a hipGraph and replayed;
+  chunks32k       the 32768-token chunk sort-and-pad / restore roundtrip,
+                  warm and cold (with a routed workload);
+  extra_ops       the library's further operations (EP combine, router,
+                  mask-map form, FP8 rows) on the same input, warm and cold;
+  roofline        the dominant kernel of the step: its algorithmic bytes per
+                  launch over its event time in the timed region (warm) and
+                  in the cold pass, and its HBM bytes from stored rocprofv3
+                  counters while the kernel sources are unchanged;
+  cpu_baseline    the CPU oracle on the same roundtrip on the host's cores,
+                  one thread and all threads (a reported baseline only).
 """
 from __future__ import annotations
 
@@ -43,15 +56,21 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="finegrain",
+    ap.add_argument("--workload", default="skewed",
                     choices=["tiny", "finegrain", "skewed", "chunks8k", "chunks32k"])
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="CPU time per row of the oracle baseline (0 disables it)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip timing the step replayed from a captured hipGraph")
     ap.add_argument("--no-cold", dest="cold", action="store_false",
-                    help="skip the cold-cache per-op pass (keeps a kernel trace to the "
-                         "warm calls)")
+                    help="skip the cold-cache passes (keeps a kernel trace to the warm calls)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="run only the cold-cache passes after the warm-up (so a kernel trace "
+                         "holds the cold launches alone)")
+    ap.add_argument("--no-chunks", dest="chunks", action="store_false",
+                    help="with a routed workload, skip the 32768-token chunk roundtrip block")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="skip the library's further operations")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB three times "
                          "(a known-size reference for hardware byte counters)")
@@ -61,7 +80,7 @@ def parse():
 # --------------------------------------------------------------- bytes ----
 
 def routed_bytes(T, H, E, k):
-    """Algorithmic bytes per op of a routed step (bf16 rows, fp32 probs,
+    """Algorithmic bytes per op of the routed path (bf16 rows, fp32 probs,
     int32 indices; each (t, j) lookup reads topk_idx and row_id_map)."""
     row = 2 * H
     look = 8 * T * k
@@ -94,6 +113,9 @@ def chunk_bytes(N, H, cap, eb=2):
         "unpad_and_restore": N * row + N * row + 4 * cap + 4 * N + 4 * N,
     }
 
+
+ROUNDTRIP_OPS = {"routed": ("permute", "unpermute"),
+                 "chunks": ("sort_chunks_and_pad", "unpad_and_restore")}
 
 # Kernels each op launches (the op's events bracket all of them).
 OP_KERNELS = {
@@ -182,13 +204,11 @@ class HipEvents:
         import torch  # noqa: F401  (the HIP runtime is already loaded by torch)
         self.hip = ctypes.CDLL("libamdhip64.so.7")
         self.flags = flags
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
                                                      ctypes.c_uint]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self):
         ev = ctypes.c_void_p()
@@ -207,33 +227,33 @@ class HipEvents:
         return ms.value * 1e3
 
 
-class Step:
-    """A list of (name, fn, args) calls straight into the C ABI; the stream
-    argument (always last) is supplied at run time."""
+class Ops:
+    """Named calls straight into the C ABI; the stream argument (always last)
+    is supplied at run time."""
 
     def __init__(self):
-        self.ops = []
+        self.calls = {}      # name -> (fn, args)
         self.keep = []
-        self.extra = []   # (name, bytes, fn, args) timed outside the step
 
     def add(self, name, fn, *args):
-        self.ops.append((name, fn, args))
+        self.calls[name] = (fn, args)
 
-    def run(self, events=None, stream=None, hev=None):
-        import torch
-        s = ctypes.c_void_p(stream if stream is not None
-                            else torch.cuda.current_stream().cuda_stream)
-        for name, fn, args in self.ops:
+    def run(self, names, stream, events=None, hev=None):
+        for name in names:
+            fn, args = self.calls[name]
             if events is not None:
-                hev.record(events[name][0], s)
-            st = fn(*args, s)
+                hev.record(events[name][0], stream)
+            st = fn(*args, stream)
             if events is not None:
-                hev.record(events[name][1], s)
+                hev.record(events[name][1], stream)
             if st != 0:
                 raise RuntimeError(f"{name}: status {st}")
 
 
-def build_routed(m, w):
+def build_routed(m, w, extra=True):
+    """The whole routed path on workload w, plus (extra) the library's
+    further operations on the same routing.  Returns (ops, bytes per op,
+    extra op names)."""
     import torch
     import workloads
     dev = "cuda:0"
@@ -253,40 +273,53 @@ def build_routed(m, w):
     dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     dprob2 = torch.empty((T, k), dtype=torch.float32, device=dev)
     p = lambda t: ctypes.c_void_p(t.data_ptr())
-    step = Step()
-    step.keep = [x, idx, probs, dy, rm, off, ws, P, pp, y, dP, dprob, d_pp, dx, dprob2]
+    ops = Ops()
+    ops.keep = [x, idx, probs, dy, rm, off, ws, P, pp, y, dP, dprob, d_pp, dx, dprob2]
     n = T * k
-    step.add("row_map", lib.moe_make_row_id_map, p(idx), T, k, E, p(rm), p(off), None, p(ws),
-             ws_n,)
-    step.add("permute", lib.moe_permute, p(x), p(probs), p(idx), p(rm), T, H, k, E, n, p(P),
-             p(pp), None,)
-    step.add("unpermute", lib.moe_unpermute, p(P), p(probs), p(idx), p(rm), T, H, k, E, n, p(y),
-             None,)
-    step.add("unpermute_bwd", lib.moe_unpermute_bwd, p(dy), p(P), p(probs), p(idx), p(rm), T, H,
-             k, E, n, p(dP), p(dprob), None,)
-    step.add("permute_bwd", lib.moe_permute_bwd, p(dP), p(d_pp), p(idx), p(rm), T, H, k, E, n,
-             p(dx), p(dprob2), None,)
-    # The library's further operations (EP combine, router, mask-map form, FP8
-    # rows), timed on their own after the step.
+    ops.add("row_map", lib.moe_make_row_id_map, p(idx), T, k, E, p(rm), p(off), None, p(ws),
+            ws_n)
+    ops.add("permute", lib.moe_permute, p(x), p(probs), p(idx), p(rm), T, H, k, E, n, p(P),
+            p(pp), None)
+    ops.add("unpermute", lib.moe_unpermute, p(P), p(probs), p(idx), p(rm), T, H, k, E, n, p(y),
+            None)
+    ops.add("unpermute_bwd", lib.moe_unpermute_bwd, p(dy), p(P), p(probs), p(idx), p(rm), T, H,
+            k, E, n, p(dP), p(dprob), None)
+    ops.add("permute_bwd", lib.moe_permute_bwd, p(dP), p(d_pp), p(idx), p(rm), T, H, k, E, n,
+            p(dx), p(dprob2), None)
+    nbytes = routed_bytes(T, H, E, k)
+    if not extra:
+        return ops, nbytes, []
+    # The library's further operations, timed on their own after the step.
     y_ep = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     logits = w.logits.to(dev).contiguous()
     r_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     r_probs = torch.empty((T, k), dtype=torch.float32, device=dev)
     d_logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    step.keep += [y_ep, logits, r_idx, r_probs, d_logits]
-    ub = routed_bytes(T, H, E, k)["unpermute"]
+    ops.keep += [y_ep, logits, r_idx, r_probs, d_logits]
+    ub = nbytes["unpermute"]
     eb = logits.element_size()
-    step.extra = [
-        ("unpermute_ep8_bf16partials", ub, lib.moe_unpermute_ep,
-         (p(P), p(probs), p(idx), p(rm), T, H, k, E, n, 8, 1, p(y_ep), None)),
-        ("unpermute_ep8_bf16partials_fp64", ub, lib.moe_unpermute_ep,
-         (p(P), p(probs), p(idx), p(rm), T, H, k, E, n, 8, 3, p(y_ep), None)),
-        # router: logits in, k indices + k weights out; bwd: 3 k-vectors in, [T, E] out
-        ("topk_softmax", T * E * eb + T * k * 8, lib.moe_topk_softmax,
-         (p(logits), eb, T, E, k, p(r_idx), p(r_probs), 4)),
-        ("topk_softmax_bwd", T * k * 12 + T * E * 4, lib.moe_topk_softmax_bwd,
-         (p(dprob), p(probs), 4, p(idx), T, E, k, p(d_logits), 4, None)),
-    ]
+    ops.add("unpermute_ep8_bf16partials", lib.moe_unpermute_ep, p(P), p(probs), p(idx), p(rm),
+            T, H, k, E, n, 8, 1, p(y_ep), None)
+    ops.add("unpermute_ep8_bf16partials_fp64", lib.moe_unpermute_ep, p(P), p(probs), p(idx),
+            p(rm), T, H, k, E, n, 8, 3, p(y_ep), None)
+    # router: logits in, k indices + k weights out; bwd: 3 k-vectors in, [T, E] out
+    ops.add("topk_softmax", lib.moe_topk_softmax, p(logits), eb, T, E, k, p(r_idx), p(r_probs),
+            4)
+    ops.add("topk_softmax_bwd", lib.moe_topk_softmax_bwd, p(dprob), p(probs), 4, p(idx), T, E,
+            k, p(d_logits), 4, None)
+    nbytes.update({"unpermute_ep8_bf16partials": ub, "unpermute_ep8_bf16partials_fp64": ub,
+                   "topk_softmax": T * E * eb + T * k * 8,
+                   "topk_softmax_bwd": T * k * 12 + T * E * 4})
+    # Quantized rows: FP8 (E4M3FN) tokens with fp32 scales per 128 elements.
+    q8, sc8 = workloads.quantize_fp8_rows(w.x, 128)
+    q8, sc8 = q8.to(dev), sc8.to(dev)
+    S = sc8.shape[1]
+    qP = torch.empty((n, H), dtype=q8.dtype, device=dev)
+    qS = torch.empty((n, S), dtype=torch.float32, device=dev)
+    ops.keep += [q8, sc8, qP, qS]
+    ops.add("permute_fp8_scaled", lib.moe_permute_scaled, p(q8), 1, p(sc8), 4 * S, p(probs),
+            p(idx), p(rm), T, H, k, E, n, p(qP), p(qS), p(pp), None)
+    nbytes["permute_fp8_scaled"] = T * H + n * H + 4 * S * (T + n) + 8 * n + 4 * n + 4 * n
     # TransformerEngine mask-map form on the same routing.
     mask = torch.zeros((T, E), dtype=torch.bool, device=dev)
     mask.scatter_(1, idx.long(), True)
@@ -302,32 +335,20 @@ def build_routed(m, w):
     my = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     mdP = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
     mdp = torch.empty((T, E), dtype=torch.float32, device=dev)
-    step.keep += [mask, probs_te, mmap, moff, mws, mP, mpp, my, mdP, mdp]
-    # Quantized rows: FP8 (E4M3FN) tokens with fp32 scales per 128 elements.
-    q8, sc8 = workloads.quantize_fp8_rows(w.x, 128)
-    q8, sc8 = q8.to(dev), sc8.to(dev)
-    S = sc8.shape[1]
-    qP = torch.empty((n, H), dtype=q8.dtype, device=dev)
-    qS = torch.empty((n, S), dtype=torch.float32, device=dev)
-    step.keep += [q8, sc8, qP, qS]
-    fp8_bytes = T * H + n * H + 4 * S * (T + n) + 8 * n + 4 * n + 4 * n
-    mb = mask_bytes(T, H, E, k)
-    step.extra += [
-        ("permute_fp8_scaled", fp8_bytes, lib.moe_permute_scaled,
-         (p(q8), 1, p(sc8), 4 * S, p(probs), p(idx), p(rm), T, H, k, E, n, p(qP), p(qS), p(pp),
-          None)),
-    ]
-    step.extra += [
-        ("mask_row_map", mb["mask_row_map"], lib.moe_make_mask_row_id_map,
-         (p(mask), 1, T, E, -1, p(mmap), p(moff), p(mws), mws_n)),
-        ("mask_permute", mb["mask_permute"], lib.moe_permute_mask,
-         (p(x), p(probs_te), p(mmap), T, H, E, n, p(mP), p(mpp), None)),
-        ("mask_unpermute", mb["mask_unpermute"], lib.moe_unpermute_mask,
-         (p(mP), p(probs_te), None, p(mmap), T, H, E, n, p(my), None, None)),
-        ("mask_unpermute_bwd", mb["mask_unpermute_bwd"], lib.moe_unpermute_mask_bwd,
-         (p(dy), p(mP), p(probs_te), p(mmap), T, H, E, n, p(mdP), p(mdp), None)),
-    ]
-    return step, routed_bytes(T, H, E, k)
+    ops.keep += [mask, probs_te, mmap, moff, mws, mP, mpp, my, mdP, mdp]
+    ops.add("mask_row_map", lib.moe_make_mask_row_id_map, p(mask), 1, T, E, -1, p(mmap),
+            p(moff), p(mws), mws_n)
+    ops.add("mask_permute", lib.moe_permute_mask, p(x), p(probs_te), p(mmap), T, H, E, n, p(mP),
+            p(mpp), None)
+    ops.add("mask_unpermute", lib.moe_unpermute_mask, p(mP), p(probs_te), None, p(mmap), T, H,
+            E, n, p(my), None, None)
+    ops.add("mask_unpermute_bwd", lib.moe_unpermute_mask_bwd, p(dy), p(mP), p(probs_te),
+            p(mmap), T, H, E, n, p(mdP), p(mdp), None)
+    nbytes.update(mask_bytes(T, H, E, k))
+    extra_names = ["unpermute_ep8_bf16partials", "unpermute_ep8_bf16partials_fp64",
+                   "topk_softmax", "topk_softmax_bwd", "permute_fp8_scaled", "mask_row_map",
+                   "mask_permute", "mask_unpermute", "mask_unpermute_bwd"]
+    return ops, nbytes, extra_names
 
 
 def build_chunks(m, cw):
@@ -344,22 +365,22 @@ def build_chunks(m, cw):
     back = torch.empty_like(x)
     back_p = torch.empty_like(probs)
     p = lambda t: ctypes.c_void_p(t.data_ptr())
-    step = Step()
-    step.keep = [x, probs, sizes, order, out, out_p, rm, off, back, back_p]
+    ops = Ops()
+    ops.keep = [x, probs, sizes, order, out, out_p, rm, off, back, back_p]
     eb = x.element_size()
-    step.add("sort_chunks_and_pad", lib.moe_sort_chunks_and_pad, p(x), p(probs), eb, 4,
-             cw.N_cap, cw.H, p(sizes), p(order), cw.C, cw.chunks_per_group, cw.align, cw.out_cap,
-             p(out), p(out_p), p(rm), p(off), None,)
-    step.add("unpad_and_restore", lib.moe_unpad_and_restore_chunks, p(out), p(out_p), eb, 4,
-             p(rm), p(sizes), cw.C, cw.out_cap, cw.H, cw.N_cap, p(back), p(back_p), None,)
-    return step, chunk_bytes(int(cw.split_sizes.sum()), cw.H, cw.out_cap, eb)
+    ops.add("sort_chunks_and_pad", lib.moe_sort_chunks_and_pad, p(x), p(probs), eb, 4,
+            cw.N_cap, cw.H, p(sizes), p(order), cw.C, cw.chunks_per_group, cw.align, cw.out_cap,
+            p(out), p(out_p), p(rm), p(off), None)
+    ops.add("unpad_and_restore", lib.moe_unpad_and_restore_chunks, p(out), p(out_p), eb, 4,
+            p(rm), p(sizes), cw.C, cw.out_cap, cw.H, cw.N_cap, p(back), p(back_p), None)
+    return ops, chunk_bytes(int(cw.split_sizes.sum()), cw.H, cw.out_cap, eb)
 
 
-# --------------------------------------------------------- CPU baseline ----
+# -------------------------------------------------------------- timing ----
 
 def op_stats(times, nbytes):
-    """Mean, median, p10 / p90 of sorted event times (µs) and the rate at the
-    median."""
+    """Mean, median, p10 / p90 of event times (µs) and the rate at the median."""
+    times = sorted(times)
     n = len(times)
     mean = sum(times) / n
     med = times[n // 2]
@@ -369,56 +390,181 @@ def op_stats(times, nbytes):
             "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
 
 
-def cpu_baseline(name, w, target_s, step_bytes):
-    """The oracle, untuned and single-threaded, on a bounded sample of the
-    same workload: whole steps on a prefix of the tokens, repeated until
-    about target_s seconds of CPU work."""
-    import numpy as np
+class Timer:
+    """Event-timed passes over named ops on one stream."""
+
+    def __init__(self, ops, nbytes, stream):
+        import torch
+        self.torch = torch
+        self.ops, self.nbytes, self.s = ops, nbytes, stream
+        self.hev = HipEvents()
+        self._flush = None
+
+    def flush(self):
+        # A 512 MiB read of an unrelated buffer evicts the op's inputs from
+        # the Infinity Cache and writes back whatever was dirty, so the op
+        # starts from clean, unrelated cache contents.  (A write pass would
+        # leave 256 MB of dirty lines whose write-back the op would pay.)
+        if self._flush is None:
+            self._flush = self.torch.ones(512 << 18, dtype=self.torch.float32, device="cuda:0")
+        self._flush.sum()
+
+    def per_op(self, names, reps, cold=False):
+        """Every op of `names` in order, reps times, events around each op
+        (cold: a flush before each op, outside its events)."""
+        evs = [{n: (self.hev.create(), self.hev.create()) for n in names} for _ in range(reps)]
+        for i in range(reps):
+            for n in names:
+                if cold:
+                    self.flush()
+                self.ops.run([n], self.s, evs[i], self.hev)
+        self.torch.cuda.synchronize()
+        return {n: op_stats([self.hev.elapsed_us(*evs[i][n]) for i in range(reps)],
+                            self.nbytes[n]) for n in names}
+
+    def unit(self, names, reps, cold=False):
+        """The ops of `names` back to back, timed as one unit (cold: one
+        flush before the unit)."""
+        evs = [(self.hev.create(), self.hev.create()) for _ in range(reps)]
+        for i in range(reps):
+            if cold:
+                self.flush()
+            self.hev.record(evs[i][0], self.s)
+            self.ops.run(names, self.s)
+            self.hev.record(evs[i][1], self.s)
+        self.torch.cuda.synchronize()
+        return op_stats([self.hev.elapsed_us(a, b) for a, b in evs],
+                        sum(self.nbytes[n] for n in names))
+
+    def wall(self, names, steps, mark=None):
+        """Exactly `steps` passes over `names` bracketed by device
+        synchronizes; events around op `mark` only.  Returns (ms per pass,
+        mean event µs of `mark`)."""
+        evs = [(self.hev.create(), self.hev.create()) for _ in range(steps)]
+        calls = [(n, *self.ops.calls[n]) for n in names]
+        s = self.s
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            for n, fn, a in calls:
+                if n == mark:
+                    self.hev.record(evs[i][0], s)
+                st = fn(*a, s)
+                if n == mark:
+                    self.hev.record(evs[i][1], s)
+                if st != 0:
+                    raise RuntimeError(f"{n}: status {st}")
+        self.torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        us = sum(self.hev.elapsed_us(a, b) for a, b in evs) / steps if mark else None
+        return ms, us
+
+    def graph(self, names, steps):
+        """`names` captured GRAPH_STEPS times in one hipGraph, replayed until
+        `steps` passes have run; ms per pass."""
+        torch = self.torch
+        R = max(1, min(GRAPH_STEPS, steps))
+        reps = max(1, steps // R)
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        sv2 = ctypes.c_void_p(s2.cuda_stream)
+        with torch.cuda.stream(s2):
+            self.ops.run(names, sv2)
+        torch.cuda.current_stream().wait_stream(s2)
+        with torch.cuda.graph(g, stream=s2):
+            for _ in range(R):
+                self.ops.run(names, sv2)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / (reps * R) * 1e3, R
+
+
+def rate(nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return round(gbs, 1), round(100 * gbs / HBM_PEAK_GBS, 1)
+
+
+# --------------------------------------------------------- CPU baseline ----
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, w, target_s, rt_bytes):
+    """The oracle, as it stands, on the same roundtrip: one thread (pinned to
+    one core) and all the threads this process may use.  Each row repeats
+    whole roundtrips until about target_s seconds have run (at least one)."""
+    import numpy as np  # noqa: F401
     import oracle
     import workloads
     if name.startswith("chunks"):
         xb = workloads.bf16_bits(w.x)
-        p = w.probs.numpy()
-        s = w.split_sizes.numpy()
-        q = w.sorted_idx.numpy()
+        p, s, q = w.probs.numpy(), w.split_sizes.numpy(), w.sorted_idx.numpy()
 
         def one():
             out, op, rm, _ = oracle.sort_chunks_and_pad(xb, p, s, q, w.chunks_per_group,
                                                         w.align, w.out_cap)
             oracle.unpad_and_restore_chunks(out, op, rm, s, w.N_cap)
-        frac = 1.0
-        sample = f"whole {name} roundtrip"
+        what = f"whole {name} sort-and-pad + restore roundtrips"
     else:
-        T = w.T
-        Ts = min(T, max(64, int(T * 0.25)))          # a token prefix
-        idx = w.topk_idx.numpy()[:Ts]
-        pr = w.probs.numpy()[:Ts]
-        xb = workloads.bf16_bits(w.x[:Ts])
-        dyb = workloads.bf16_bits(w.dy[:Ts])
-        d_pp = np.linspace(-1, 1, Ts * w.k, dtype=np.float32)
+        idx, pr = w.topk_idx.numpy(), w.probs.numpy()
+        xb = workloads.bf16_bits(w.x)
+        rm, _ = oracle.row_id_map(idx, w.num_experts)   # the map is not part of the roundtrip
 
         def one():
-            rm, _ = oracle.row_id_map(idx, w.num_experts)
             P, _ = oracle.permute(xb, pr, idx, rm)
             oracle.unpermute(P, pr, idx, rm)
-            dP, _ = oracle.unpermute_bwd(dyb, P, pr, idx, rm)
-            oracle.permute_bwd(dP, d_pp, idx, rm)
-        frac = Ts / T
-        sample = f"whole steps on the first {Ts} of {T} tokens"
-    one()                                           # warm-up
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        one()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
-    per_step = el / reps
-    gbs = step_bytes * frac / per_step / 1e9
-    result = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-              "sample": f"{sample}, {reps} repetitions, {el:.1f} s, single thread",
-              "seconds_per_full_step": round(per_step / frac, 4)}
-    return result
+        what = f"whole {name} permute + unpermute roundtrips (T={w.T})"
+
+    def timed(n_threads, pin):
+        before_aff = os.sched_getaffinity(0)
+        before_thr = oracle.threads()
+        try:
+            if pin is not None:
+                os.sched_setaffinity(0, {pin})
+            used = oracle.set_threads(n_threads)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                one()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= target_s:
+                    break
+        finally:
+            oracle.set_threads(before_thr)
+            if pin is not None:
+                os.sched_setaffinity(0, before_aff)
+        per = el / reps
+        gbs = rt_bytes / per / 1e9
+        return {"value": round(gbs, 3), "unit": "GB/s", "cores": used,
+                "seconds_per_roundtrip": round(per, 4), "repetitions": reps,
+                "seconds": round(el, 1)}
+
+    aff = sorted(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    n_all = min(len(aff), int(omp)) if omp.isdigit() and int(omp) > 0 else len(aff)
+    oracle.set_threads(n_all)
+    one()                                               # warm-up: first touch of the buffers
+    one_thr = timed(1, aff[0])
+    all_thr = timed(n_all, None)
+    return {"value": all_thr["value"], "unit": "GB/s", "cores": all_thr["cores"],
+            "kind": "oracle", "sample": what,
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "cpus_allowed": len(aff),
+            "rows": [dict(one_thr, threads="1, pinned to one core"),
+                     dict(all_thr, threads="all allowed (OpenMP over tokens)")]}
 
 
 # ----------------------------------------------------------------- main ----
@@ -435,92 +581,59 @@ def main():
 
     torch.cuda.init()
     name = args.workload
-    if name in workloads.ROUTED:
+    K, W = args.steps, args.warmup
+    K2 = max(10, K // 2)            # samples of the per-op and cold passes
+    sv = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    routed = name in workloads.ROUTED
+    if routed:
         w = workloads.ROUTED[name]()
-        step, op_bytes = build_routed(m, w)
+        ops, nbytes, extra_names = build_routed(m, w, extra=args.extra and not args.cold_only)
+        path_ops = ["row_map", "permute", "unpermute", "unpermute_bwd", "permute_bwd"]
+        rt = list(ROUNDTRIP_OPS["routed"])
         cfg = {"workload": name, "T": w.T, "H": w.H, "E": w.num_experts, "k": w.k,
-               "step": "row_map+permute+unpermute+unpermute_bwd+permute_bwd",
-               "probs": "fp32", "launch": "eager, C ABI via ctypes"}
+               "step": "permute+unpermute", "probs": "fp32", "launch": "eager, C ABI via ctypes"}
     else:
         w = workloads.CHUNKED[name]()
-        step, op_bytes = build_chunks(m, w)
+        ops, nbytes = build_chunks(m, w)
+        extra_names = []
+        path_ops = list(ROUNDTRIP_OPS["chunks"])
+        rt = path_ops
         cfg = {"workload": name, "N": w.N_cap, "H": w.H, "chunks": w.C,
                "chunks_per_group": w.chunks_per_group, "align": w.align, "out_cap": w.out_cap,
                "step": "sort_chunks_and_pad+unpad_and_restore", "probs": "fp32",
                "launch": "eager, C ABI via ctypes"}
-    step_bytes = sum(op_bytes.values())
-
-    for _ in range(args.warmup):
-        step.run()
+    rt_bytes = sum(nbytes[n] for n in rt)
+    tm = Timer(ops, nbytes, sv)
+    for _ in range(W):
+        ops.run(path_ops, sv)
     torch.cuda.synchronize()
 
-    names = [n for n, _, _ in step.ops]
-    hev = HipEvents()
-    sv = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if args.cold_only:
+        # Only cold launches after the warm-up (for a kernel trace of them).
+        cold = tm.per_op(path_ops, K2, cold=True)
+        rtc = tm.unit(rt, K2, cold=True)
+        print(json.dumps({"workload": name, "per_op_cold": cold, "roundtrip_cold": rtc}),
+              flush=True)
+        return
 
-    # Breakdown pass: HIP events around every op (one marker pair per call).
-    K2 = max(10, args.steps // 2)
-    evs = [{n: (hev.create(), hev.create()) for n in names} for _ in range(K2)]
-    for i in range(K2):
-        step.run(evs[i], hev=hev)
-    torch.cuda.synchronize()
-    per_op = {}
-    for n in names:
-        times = sorted(hev.elapsed_us(evs[i][n][0], evs[i][n][1]) for i in range(K2))
-        per_op[n] = op_stats(times, op_bytes[n])
-    dom = max(names, key=lambda n: per_op[n]["us_mean"])
+    # Breakdown pass: HIP events around every op of the path.
+    per_op = tm.per_op(path_ops, K2)
+    dom = max(rt, key=lambda n: per_op[n]["us_mean"])
+    per_op_cold = tm.per_op(path_ops, K2, cold=True) if args.cold else None
+    rt_cold = tm.unit(rt, K2, cold=True) if args.cold else None
 
-    # Cold pass: a 512 MiB read of an unrelated buffer before every op
-    # (outside its events) evicts the op's inputs from the Infinity Cache and
-    # writes back whatever was dirty, so the op starts from clean, unrelated
-    # cache contents.  (A write pass would leave 256 MB of dirty lines whose
-    # write-back the op would then pay.)
-    K3 = K2 if args.cold else 0
-    flush = torch.ones(512 << 18 if K3 else 1, dtype=torch.float32, device="cuda:0")
-    evc = [{n: (hev.create(), hev.create()) for n in names} for _ in range(K3)]
-    for i in range(K3):
-        for n, fn, a in step.ops:
-            flush.sum()
-            hev.record(evc[i][n][0], sv)
-            st = fn(*a, sv)
-            hev.record(evc[i][n][1], sv)
-            if st != 0:
-                raise RuntimeError(f"{n}: status {st}")
-    torch.cuda.synchronize()
-    del flush
-    per_op_cold = {n: op_stats(sorted(hev.elapsed_us(evc[i][n][0], evc[i][n][1])
-                                      for i in range(K3)), op_bytes[n]) for n in names} \
-        if K3 else None
-
-    # Timed region: exactly K steps; events only around the dominant op.
-    K = args.steps
-    dev_ev = [(hev.create(), hev.create()) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        for n, fn, a in step.ops:
-            if n == dom:
-                hev.record(dev_ev[i][0], sv)
-            st = fn(*a, sv)
-            if n == dom:
-                hev.record(dev_ev[i][1], sv)
-            if st != 0:
-                raise RuntimeError(f"{n}: status {st}")
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / K * 1e3
-    dom_us = sum(hev.elapsed_us(a, b) for a, b in dev_ev) / K
-
-    achieved = op_bytes[dom] / (dom_us * 1e-6) / 1e9
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # Timed region: exactly K roundtrips; events only around the dominant op.
+    ms, dom_us = tm.wall(rt, K, mark=dom)
+    value = rt_bytes / (ms * 1e-3) / 1e9
+    achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "warmup": W,
+        "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -528,58 +641,64 @@ def main():
         "data": "synthetic",
         "config": cfg,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
-        "step_bytes": step_bytes,
+        "us_per_roundtrip": round(ms * 1e3, 1),
+        "step_bytes": rt_bytes,
+        "roundtrip_cold": rt_cold,
         "per_op": per_op,
         "per_op_cold": per_op_cold,
-        "roofline": {"bound": "hbm", "kernel": dom, "kernels": op_kernels(dom, cfg),
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "us_per_launch": round(dom_us, 2),
-                     "bytes_per_launch": op_bytes[dom],
-                     "traffic": pmc_traffic(name, dom)},
     }
+    roof = {"bound": "hbm", "kernel": dom, "kernels": op_kernels(dom, cfg),
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "us_per_launch": round(dom_us, 2),
+            "bytes_per_launch": nbytes[dom], "traffic": pmc_traffic(name, dom)}
+    if per_op_cold is not None:
+        cu = per_op_cold[dom]["us_median"]
+        roof.update({"us_per_launch_cold": cu,
+                     "achieved_cold": round(nbytes[dom] / (cu * 1e-6) / 1e9, 1),
+                     "frac_cold": round(nbytes[dom] / (cu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    result["roofline"] = roof
+    if routed:
+        fms, _ = tm.wall(path_ops, K)
+        fb = sum(nbytes[n] for n in path_ops)
+        result["full_step"] = {"ops": "+".join(path_ops), "bytes": fb, "ms": round(fms, 4),
+                               "GBps": rate(fb, fms * 1e3)[0],
+                               "pct_hbm_peak": rate(fb, fms * 1e3)[1]}
     if args.graph:
-        # The same step (same buffers) captured GRAPH_STEPS times in one
-        # hipGraph, so one host launch covers several steps, and replayed
-        # until K steps have run.
-        R = max(1, min(GRAPH_STEPS, K))
-        reps = max(1, K // R)
-        g = torch.cuda.CUDAGraph()
-        s2 = torch.cuda.Stream()
-        s2.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s2):
-            step.run(stream=s2.cuda_stream)
-        torch.cuda.current_stream().wait_stream(s2)
-        with torch.cuda.graph(g, stream=s2):
-            for _ in range(R):
-                step.run(stream=s2.cuda_stream)
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        gms = (time.perf_counter() - t0) / (reps * R) * 1e3
+        gms, R = tm.graph(rt, K)
         result["graph_replay"] = {"steps_per_graph": R, "ms_per_step": round(gms, 4),
-                                  "GBps": round(step_bytes / (gms * 1e-3) / 1e9, 1)}
-    if step.extra:
+                                  "GBps": rate(rt_bytes, gms * 1e3)[0]}
+    if extra_names:
         extra = {}
-        for n, nbytes, fn, a in step.extra:
+        for n in extra_names:
             for _ in range(3):
-                fn(*a, sv)
-            evx = [(hev.create(), hev.create()) for _ in range(K2)]
-            for e0, e1 in evx:
-                hev.record(e0, sv)
-                st = fn(*a, sv)
-                hev.record(e1, sv)
-                if st != 0:
-                    raise RuntimeError(f"{n}: status {st}")
-            torch.cuda.synchronize()
-            us = sum(hev.elapsed_us(e0, e1) for e0, e1 in evx) / K2
-            extra[n] = {"us_mean": round(us, 2), "bytes": nbytes,
-                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-                        "pct_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+                ops.run([n], sv)
+            warm = tm.per_op([n], K2)[n]
+            e = {"us_median": warm["us_median"], "bytes": nbytes[n], "GBps": warm["GBps"],
+                 "pct_hbm_peak": warm["pct_hbm_peak"]}
+            if args.cold:
+                c = tm.per_op([n], K2, cold=True)[n]
+                e.update({"us_median_cold": c["us_median"], "GBps_cold": c["GBps"],
+                          "pct_hbm_peak_cold": c["pct_hbm_peak"]})
+            extra[n] = e
         result["extra_ops"] = extra
+    if routed and args.chunks:
+        cw = workloads.chunks32k()
+        cops, cbytes = build_chunks(m, cw)
+        ct = Timer(cops, cbytes, sv)
+        cn = list(ROUNDTRIP_OPS["chunks"])
+        cb = sum(cbytes.values())
+        for _ in range(W):
+            cops.run(cn, sv)
+        cms, _ = ct.wall(cn, K)
+        cblk = {"N": cw.N_cap, "H": cw.H, "chunks": cw.C, "align": cw.align,
+                "out_cap": cw.out_cap, "bytes": cb, "us_per_roundtrip": round(cms * 1e3, 1),
+                "GBps": rate(cb, cms * 1e3)[0], "pct_hbm_peak": rate(cb, cms * 1e3)[1],
+                "per_op": ct.per_op(cn, K2)}
+        if args.cold:
+            cblk["per_op_cold"] = ct.per_op(cn, K2, cold=True)
+            cblk["roundtrip_cold"] = ct.unit(cn, K2, cold=True)
+        result["chunks32k"] = cblk
+        del cops, ct
     if args.copy_probe > 0:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -589,7 +708,7 @@ def main():
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = {"read": 4 * n, "write": 4 * n}
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(name, w, args.cpu_seconds, step_bytes)
+        result["cpu_baseline"] = cpu_baseline(name, w, args.cpu_seconds, rt_bytes)
     print(json.dumps(result), flush=True)
 
 

@@ -145,9 +145,10 @@ MOE_PERM_API int moe_permute(const void *x, const float *probs, const int32_t *t
  * (4) Unpermute -- token-owned, fixed-order combine.
  *
  * [MCORE-BI] unpermute_with_bf16_rank_partials / _rank_tree_unpermute_kernel
- * with BF16_RANK_PARTIALS (one EP rank): each output token adds its routed
- * rows in top-k slot order as fp32 fused multiply-adds of probability and
- * row, starting from zero, then rounds to bf16:
+ * with BF16_RANK_PARTIALS, on a single EP rank: an output token is the sum
+ * of its routed rows, each scaled by its probability, accumulated in fp32
+ * with one fused multiply-add per slot, slots taken in top-k order, the
+ * accumulator starting at zero; the sum is rounded once to bf16:
  *   acc = +0.0f; for j in 0..topk-1: acc = fmaf(probs[t][j], in[r(t,j)][h], acc)
  *   out[t][h] = bf16_round_nearest_even(acc)
  * probs == NULL uses unit weights (identical to plain fp32 adds).
@@ -439,6 +440,11 @@ MOE_PERM_API int moe_sort_chunks_and_pad(const void *in, const void *probs, int 
  *   split_sizes [num_chunks] device (gives the token total).
  *   out       [n_cap][hidden], out_probs [n_cap] or NULL.
  *   dev_status optional; MOE_DEV_BAD_ROW, MOE_DEV_BAD_CHUNKS, MOE_DEV_OVERFLOW.
+ * A row_map entry at or past the token total (a map saved for other split
+ * sizes) is dropped and sets MOE_DEV_BAD_ROW; the rest of out is still
+ * written as above (the zero tail included).  Two entries naming the same
+ * source row are outside the contract (a map from moe_sort_chunks_and_pad
+ * never has them): that row then holds one of the two padded rows.
  * ------------------------------------------------------------------------ */
 MOE_PERM_API int moe_unpad_and_restore_chunks(const void *in, const void *probs,
                                               int elem_bytes, int prob_bytes,
@@ -449,8 +455,8 @@ MOE_PERM_API int moe_unpad_and_restore_chunks(const void *in, const void *probs,
                                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
- * Chunk backwards.  [TE-3509] Changes: padding is zero-filled and contributes
- * zero gradient.
+ * Chunk backwards.  [TE-3509] Changes: padding rows hold zeros and pass no
+ * gradient back.
  *   moe_sort_chunks_and_pad_bwd: gradient of the sort-and-pad w.r.t. its
  *     input = the restore applied to the padded gradient (padding-row
  *     gradients are dropped, rows past the token total are zero).

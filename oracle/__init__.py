@@ -45,7 +45,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call([
-            "gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+            "gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
             "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm",
         ])
         os.replace(tmp, _LIB)
@@ -98,6 +98,8 @@ def _load():
         lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
         lib.oracle_fmaf.argtypes = [ctypes.c_float] * 3
         lib.oracle_fmaf.restype = ctypes.c_float
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -113,6 +115,18 @@ def _arr(a, dtype):
 def _check(code, where):
     if code != 0:
         raise OracleError(code, where)
+
+
+# ---- threads -------------------------------------------------------------
+
+def set_threads(n: int) -> int:
+    """Threads of the per-token loops (n < 1 leaves the setting); returns the
+    number the next such loop uses.  Results do not depend on it."""
+    return int(_load().oracle_set_threads(n))
+
+
+def threads() -> int:
+    return set_threads(0)
 
 
 # ---- scalar helpers ------------------------------------------------------
@@ -420,7 +434,11 @@ def sort_chunks_and_pad(inp, probs, split_sizes, sorted_idx, chunks_per_group, a
     return out, out_probs, row_map, pad_off
 
 
-def unpad_and_restore_chunks(inp, probs, row_map, split_sizes, n_cap):
+def unpad_and_restore_chunks(inp, probs, row_map, split_sizes, n_cap, with_status=False):
+    """Restore padded rows to their source rows.  with_status: return
+    (out, out_probs, status) instead of raising on a non-zero status (a map
+    entry at or past the token total is dropped and reported as status 4, the
+    rest of the output still defined)."""
     inp = np.ascontiguousarray(inp)
     rm = _arr(row_map, np.int32)
     s = _arr(split_sizes, np.int32)
@@ -432,13 +450,17 @@ def unpad_and_restore_chunks(inp, probs, row_map, split_sizes, n_cap):
         probs = np.ascontiguousarray(probs)
         pb = _ebytes(probs)
         out_probs = np.empty(n_cap, probs.dtype)
-    _check(_load().oracle_unpad_and_restore_chunks(
+    st = _load().oracle_unpad_and_restore_chunks(
         _p(inp), _p(probs), _ebytes(inp), pb, _p(rm), _p(s), s.size, out_cap, H, n_cap, _p(out),
-        _p(out_probs)), "unpad_and_restore_chunks")
+        _p(out_probs))
+    if with_status:
+        return out, out_probs, st
+    _check(st, "unpad_and_restore_chunks")
     return out, out_probs
 
 
-def sort_chunks_and_pad_bwd(d_out, d_out_probs, row_map, split_sizes, n_cap):
+def sort_chunks_and_pad_bwd(d_out, d_out_probs, row_map, split_sizes, n_cap,
+                            with_status=False):
     d_out = np.ascontiguousarray(d_out)
     rm = _arr(row_map, np.int32)
     s = _arr(split_sizes, np.int32)
@@ -450,9 +472,12 @@ def sort_chunks_and_pad_bwd(d_out, d_out_probs, row_map, split_sizes, n_cap):
         d_out_probs = np.ascontiguousarray(d_out_probs)
         pb = _ebytes(d_out_probs)
         d_in_probs = np.empty(n_cap, d_out_probs.dtype)
-    _check(_load().oracle_sort_chunks_and_pad_bwd(
+    st = _load().oracle_sort_chunks_and_pad_bwd(
         _p(d_out), _p(d_out_probs), _ebytes(d_out), pb, _p(rm), _p(s), s.size, out_cap, H, n_cap,
-        _p(d_in), _p(d_in_probs)), "sort_chunks_and_pad_bwd")
+        _p(d_in), _p(d_in_probs))
+    if with_status:
+        return d_in, d_in_probs, st
+    _check(st, "sort_chunks_and_pad_bwd")
     return d_in, d_in_probs
 
 

@@ -41,9 +41,16 @@
  * below are written from the IEEE 754 definitions: widening is exact, and
  * narrowing is round-to-nearest, ties-to-even on the 16 discarded bits.
  *
- * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -shared -fPIC.
- * -ffp-contract=off keeps every a*b+c that is not an explicit fmaf() as
- * two roundings.
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -fopenmp -shared
+ * -fPIC.  -ffp-contract=off keeps every a*b+c that is not an explicit fmaf()
+ * as two roundings.
+ *
+ * Threads: the per-token loops of the row copies, the combines and their
+ * backwards run their tokens on OpenMP threads (oracle_set_threads).  Each
+ * token's outputs are computed by one thread with the same scalar loop, and
+ * no two tokens write the same output, so the results do not depend on the
+ * thread count.  Those functions first check every slot in token order,
+ * serially, and return the first error before any output is written.
  *
  * Parity unpinned at the bit level: the prob-grad dot products of
  * oracle_unpermute_bwd and oracle_mask_unpermute_bwd (the pages leave the
@@ -57,6 +64,7 @@
  * Outputs are unspecified after an error.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -106,6 +114,14 @@ static uint16_t f32_to_bf16_rne(float f)
 }
 
 uint16_t oracle_f32_to_bf16(float f) { return f32_to_bf16_rne(f); }
+
+/* Threads of the per-token loops (n < 1 keeps the current setting); returns
+   the number the next such loop uses. */
+int oracle_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+}
 float oracle_bf16_to_f32(uint16_t b) { return bf16_to_f32(b); }
 float oracle_fmaf(float a, float b, float c) { return fmaf(a, b, c); }
 
@@ -207,6 +223,27 @@ static int slot_row(const int32_t *topk_idx, const int32_t *row_id_map,
     return ORC_OK;
 }
 
+/* The first bad slot in token order, walking (t, j) as the loops below do. */
+static int check_slots(const int32_t *topk_idx, const int32_t *row_id_map,
+                       int T, int k, int E, int64_t n_rows)
+{
+    for (int t = 0; t < T; t++) {
+        for (int j = 0; j < k; j++) {
+            int64_t r;
+            int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
+            if (s) return s;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Destination row of a slot that check_slots has accepted. */
+static int64_t dest_row(const int32_t *topk_idx, const int32_t *row_id_map, int T, int k,
+                        int t, int j)
+{
+    return row_id_map[(int64_t)topk_idx[(int64_t)t * k + j] * T + t];
+}
+
 /* ---- (2) permute -------------------------------------------------------- */
 
 /*
@@ -223,11 +260,12 @@ int oracle_permute(const uint16_t *x, const float *probs, const int32_t *topk_id
 {
     if (T < 0 || H < 1 || k < 1 || E < 1) return ORC_BAD_ARG;
     int64_t n_rows = (int64_t)T * k;
+    int status = check_slots(topk_idx, row_id_map, T, k, E, n_rows);
+    if (status) return status;
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
         for (int j = 0; j < k; j++) {
-            int64_t r;
-            int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
-            if (s) return s;
+            int64_t r = dest_row(topk_idx, row_id_map, T, k, t, j);
             for (int h = 0; h < H; h++) out[r * H + h] = x[(int64_t)t * H + h];
             if (probs && out_probs) out_probs[r] = probs[(int64_t)t * k + j];
         }
@@ -240,10 +278,11 @@ int oracle_permute(const uint16_t *x, const float *probs, const int32_t *topk_id
 /*
  * Megatron-core core.transformer.moe.batch_invariant,
  * unpermute_with_bf16_rank_partials (and _rank_tree_unpermute_kernel with
- * BF16_RANK_PARTIALS): the token's routes are added in the order of its
- * route rows ([tokens, topk], i.e. top-k slot order), as fp32 fused
- * multiply-adds of probability and row starting from zero, and the sum is
- * rounded to bf16.  With one EP rank that is the whole combine.
+ * BF16_RANK_PARTIALS): per output element, an fp32 accumulator begins at
+ * zero and takes one fused multiply-add per routed slot (probability times
+ * the slot's row value), slots visited in the column order of the [tokens,
+ * topk] routing; the final value is rounded once to bf16.  With a single EP
+ * rank this is the whole combine.
  *   acc = +0.0f
  *   for j = 0 .. k-1:  acc = fmaf(p[t][j], float(in[r_j][h]), acc)
  *   out[t][h] = bf16_rne(acc)
@@ -255,13 +294,14 @@ int oracle_unpermute(const uint16_t *in, const float *probs, const int32_t *topk
                      int64_t n_rows, uint16_t *out)
 {
     if (T < 0 || H < 1 || k < 1 || E < 1) return ORC_BAD_ARG;
+    int status = check_slots(topk_idx, row_id_map, T, k, E, n_rows);
+    if (status) return status;
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
         for (int h = 0; h < H; h++) {
             float acc = +0.0f;
             for (int j = 0; j < k; j++) {
-                int64_t r;
-                int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
-                if (s) return s;
+                int64_t r = dest_row(topk_idx, row_id_map, T, k, t, j);
                 float p = probs ? probs[(int64_t)t * k + j] : 1.0f;
                 acc = fmaf(p, bf16_to_f32(in[r * H + h]), acc);
             }
@@ -312,12 +352,12 @@ static uint16_t f64_to_bf16_rne(double d)
 uint16_t oracle_f64_to_bf16(double d) { return f64_to_bf16_rne(d); }
 
 /*
- * Megatron-core core.transformer.moe.batch_invariant: unpermute adds the
- * contributions by EP rank, then by top-k slot (_unpermute_loop, the loop
- * reference); with BF16_RANK_PARTIALS each rank's partial is the fp32
- * fused multiply-add chain of prob and row in slot order, from zero, rounded
- * to bf16 (unpermute_with_bf16_rank_partials); CROSS_RANK_FP64 adds the ranks
- * in fp64.  On one GPU the ranks are expert ranges: the E experts split into
+ * Megatron-core core.transformer.moe.batch_invariant: the loop reference
+ * (_unpermute_loop) walks EP ranks in order and, inside a rank, the token's
+ * slots in top-k order; in the BF16_RANK_PARTIALS form
+ * (unpermute_with_bf16_rank_partials) a rank's slots build an fp32 partial
+ * by fused multiply-adds from zero, and the partial is rounded to bf16
+ * before the ranks are summed; CROSS_RANK_FP64 sums the ranks in fp64.  On one GPU the ranks are expert ranges: the E experts split into
  * ep_size equal ranges, rank(e) = e / (E / ep_size).
  *   total = 0 (fp32, or fp64)
  *   for rank = 0 .. ep_size-1:
@@ -335,6 +375,9 @@ int oracle_unpermute_ep(const uint16_t *in, const float *probs, const int32_t *t
 {
     if (T < 0 || H < 1 || k < 1 || E < 1 || ep_size < 1 || E % ep_size != 0) return ORC_BAD_ARG;
     int per_rank = E / ep_size;
+    int status = check_slots(topk_idx, row_id_map, T, k, E, n_rows);
+    if (status) return status;
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
         for (int h = 0; h < H; h++) {
             float total32 = 0.0f;
@@ -342,9 +385,7 @@ int oracle_unpermute_ep(const uint16_t *in, const float *probs, const int32_t *t
             for (int rank = 0; rank < ep_size; rank++) {
                 float partial = +0.0f;
                 for (int j = 0; j < k; j++) {
-                    int64_t r;
-                    int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
-                    if (s) return s;
+                    int64_t r = dest_row(topk_idx, row_id_map, T, k, t, j);
                     if (topk_idx[(int64_t)t * k + j] / per_rank != rank) continue;
                     float p = probs ? probs[(int64_t)t * k + j] : 1.0f;
                     partial = fmaf(p, bf16_to_f32(in[r * H + h]), partial);
@@ -383,11 +424,12 @@ int oracle_unpermute_bwd(const uint16_t *d_out, const uint16_t *fwd_in, const fl
                          uint16_t *d_in, float *d_probs)
 {
     if (T < 0 || H < 1 || k < 1 || E < 1) return ORC_BAD_ARG;
+    int status = check_slots(topk_idx, row_id_map, T, k, E, n_rows);
+    if (status) return status;
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
         for (int j = 0; j < k; j++) {
-            int64_t r;
-            int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
-            if (s) return s;
+            int64_t r = dest_row(topk_idx, row_id_map, T, k, t, j);
             if (probs) {
                 float p = probs[(int64_t)t * k + j];
                 for (int h = 0; h < H; h++) {
@@ -427,22 +469,21 @@ int oracle_permute_bwd(const uint16_t *d_out, const float *d_out_probs, const in
                        uint16_t *d_x, float *d_probs)
 {
     if (T < 0 || H < 1 || k < 1 || E < 1) return ORC_BAD_ARG;
+    int status = check_slots(topk_idx, row_id_map, T, k, E, n_rows);
+    if (status) return status;
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
         for (int h = 0; h < H; h++) {
             float acc = +0.0f;
             for (int j = 0; j < k; j++) {
-                int64_t r;
-                int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
-                if (s) return s;
+                int64_t r = dest_row(topk_idx, row_id_map, T, k, t, j);
                 acc = acc + bf16_to_f32(d_out[r * H + h]);
             }
             d_x[(int64_t)t * H + h] = f32_to_bf16_rne(acc);
         }
         if (d_out_probs && d_probs) {
             for (int j = 0; j < k; j++) {
-                int64_t r;
-                int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);
-                if (s) return s;
+                int64_t r = dest_row(topk_idx, row_id_map, T, k, t, j);
                 d_probs[(int64_t)t * k + j] = d_out_probs[r];
             }
         }
@@ -920,6 +961,10 @@ static int pad_copy(const uint8_t *in, const uint8_t *probs, int elem_bytes, int
  * Unpad-and-restore copy (same PR): every mapped padded row goes back to its
  * source row; padding rows are dropped.  Rows of the restored buffer that no
  * chunk covers (from the token total up to N_cap) are all-zero bits.
+ * A map that does not belong to these split sizes (say, one saved for an
+ * earlier, larger routing) can name a source row at or past the token total;
+ * such an entry is dropped and reported as ORC_BAD_ROW, and the output is
+ * still defined: the zero tail, and every other mapped row copied.
  */
 static int restore_copy(const uint8_t *in, const uint8_t *probs, int elem_bytes, int prob_bytes,
                         const int32_t *row_map, int64_t n_act, int out_cap, int H, int N_cap,
@@ -930,16 +975,17 @@ static int restore_copy(const uint8_t *in, const uint8_t *probs, int elem_bytes,
         memset(out + s * row_bytes, 0, (size_t)row_bytes);
         if (probs && out_probs) memset(out_probs + s * prob_bytes, 0, (size_t)prob_bytes);
     }
+    int status = ORC_OK;
     for (int d = 0; d < out_cap; d++) {
         int32_t s = row_map[d];
-        if (s >= N_cap) return ORC_BAD_ROW;
         if (s < 0) continue;
+        if (s >= n_act) { status = ORC_BAD_ROW; continue; }
         memcpy(out + (int64_t)s * row_bytes, in + (int64_t)d * row_bytes, (size_t)row_bytes);
         if (probs && out_probs)
             memcpy(out_probs + (int64_t)s * prob_bytes, probs + (int64_t)d * prob_bytes,
                    (size_t)prob_bytes);
     }
-    return ORC_OK;
+    return status;
 }
 
 static int check_elem(int elem_bytes, int prob_bytes)
@@ -981,8 +1027,8 @@ int oracle_unpad_and_restore_chunks(const void *in, const void *probs, int elem_
 }
 
 /*
- * Backwards (same PR, Changes: padding is zero-filled and contributes zero
- * gradient).  The sort-and-pad copy is a row permutation plus zero rows, so
+ * Backwards (same PR, Changes: padding rows hold zeros and pass no gradient
+ * back).  The sort-and-pad copy is a row permutation plus zero rows, so
  * its gradient is the restore applied to the padded gradient (padding-row
  * gradients are dropped); the restore's gradient is the pad copy applied to
  * the restored gradient (padding rows get zero gradient).

@@ -8,9 +8,8 @@ with S = sum_h |fwd_in[r][h] * d_out[t][h]|.
 
 Outputs are pre-filled with sentinels (bf16 0x7FC1, int -2, a NaN payload
 for fp32) so an element the kernels fail to write shows up as a mismatch.
-Small workloads are compared in full; the 16384 x 7168 workload is compared
-in full where a torch gather/scatter can express the expected result on the
-GPU, and on a seeded sample of tokens run through the oracle otherwise.
+Every workload is compared with the oracle in full, the 16384 x 7168 one
+included (the oracle runs its tokens on all host cores).
 """
 import numpy as np
 import pytest
@@ -93,14 +92,18 @@ def sub_problem(idx, sample, E=None):
     return sidx, smap
 
 
-def dprob_ok(got, fwd_rows, dy_rows, ref):
-    """|got - ref| <= 1e-5 * sum_h |a*b| per (token, slot)."""
-    a = (fwd_rows.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    b = (dy_rows.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    scale = np.einsum("tjh,th->tj", np.abs(a), np.abs(b))
-    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
-    worst = float(np.max(err / np.maximum(scale, 1e-300)))
-    assert np.all(err <= 1e-5 * scale + 1e-37), f"prob grad off by {worst:.3g} of scale"
+def dprob_ok(got, fwd_rows, dy_rows, ref, chunk=256):
+    """|got - ref| <= 1e-5 * sum_h |a*b| per (token, slot); fwd_rows [T][k][H]
+    and dy_rows [T][H] bf16 bits, taken a chunk of tokens at a time."""
+    worst = 0.0
+    for t0 in range(0, got.shape[0], chunk):
+        sl = slice(t0, t0 + chunk)
+        a = (fwd_rows[sl].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        b = (dy_rows[sl].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        scale = np.einsum("tjh,th->tj", np.abs(a), np.abs(b))
+        err = np.abs(got[sl].astype(np.float64) - ref[sl].astype(np.float64))
+        worst = max(worst, float(np.max(err / np.maximum(scale, 1e-300))))
+        assert np.all(err <= 1e-5 * scale + 1e-37), f"prob grad off by {worst:.3g} of scale"
     return worst
 
 
@@ -265,21 +268,10 @@ def test_permute_configs(m, name):
     exp_p[rows.flatten()] = probs.flatten()
     assert torch.equal(out_p.view(torch.int32), exp_p.view(torch.int32))
     assert int(st.item()) == 0
-    # oracle on a sample of tokens (full for the small workloads)
-    sample = np.arange(T) if T <= 4096 else np.sort(
-        np.random.default_rng(0).choice(T, 512, replace=False))
-    if T <= 4096:
-        o, op = oracle.permute(workloads.bf16_bits(w.x), w.probs.numpy(), w.topk_idx.numpy(),
-                               ref_map)
-        assert_bits_equal(bits(out), o, "permute")
-        assert_bits_equal(out_p.cpu().numpy(), op, "permuted probs")
-    else:
-        r = oracle_rows(w.topk_idx.numpy(), ref_map)[sample].flatten()
-        sidx, smap = sub_problem(w.topk_idx.numpy(), sample)
-        o, op = oracle.permute(workloads.bf16_bits(w.x[sample]), w.probs.numpy()[sample], sidx,
-                               smap)
-        assert_bits_equal(bits(out[torch.from_numpy(r).to(DEV)]), o, "permute sample")
-        assert_bits_equal(out_p.cpu().numpy()[r], op, "permuted probs sample")
+    o, op = oracle.permute(workloads.bf16_bits(w.x), w.probs.numpy(), w.topk_idx.numpy(),
+                           ref_map)
+    assert_bits_equal(bits(out), o, "permute")
+    assert_bits_equal(out_p.cpu().numpy(), op, "permuted probs")
 
 
 @pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
@@ -294,16 +286,8 @@ def test_unpermute_configs(m, name, weighted):
     out = sentinel_bf16((T, H))
     m.moe_unpermute(P, idx, rm, probs if weighted else None, out=out)
     p_np = w.probs.numpy() if weighted else None
-    if T <= 4096:
-        ref = oracle.unpermute(bits(P), p_np, w.topk_idx.numpy(), ref_map)
-        assert_bits_equal(bits(out), ref, "unpermute")
-    else:
-        sample = np.sort(np.random.default_rng(1).choice(T, 512, replace=False))
-        r = oracle_rows(w.topk_idx.numpy(), ref_map)[sample].flatten()
-        sidx, smap = sub_problem(w.topk_idx.numpy(), sample)
-        rows = bits(P[torch.from_numpy(r).to(DEV)])
-        ref = oracle.unpermute(rows, None if p_np is None else p_np[sample], sidx, smap)
-        assert_bits_equal(bits(out)[sample], ref, "unpermute sample")
+    ref = oracle.unpermute(bits(P), p_np, w.topk_idx.numpy(), ref_map)
+    assert_bits_equal(bits(out), ref, "unpermute")
 
 
 @pytest.mark.parametrize("name,ep", [("tiny", 4), ("finegrain", 8), ("finegrain", 64),
@@ -318,17 +302,9 @@ def test_unpermute_ep_configs(m, name, ep, partials, fp64):
     P = workloads.random_rows(T * k, H, seed=81, device=DEV)
     out = sentinel_bf16((T, H))
     m.moe_unpermute_ep(P, idx, rm, ep, probs, bf16_partials=partials, fp64_cross=fp64, out=out)
-    if T <= 4096:
-        ref = oracle.unpermute_ep(bits(P), w.probs.numpy(), w.topk_idx.numpy(), ref_map, ep,
-                                  partials, fp64)
-        assert_bits_equal(bits(out), ref, "unpermute_ep")
-    else:
-        sample = np.sort(np.random.default_rng(5).choice(T, 384, replace=False))
-        r = oracle_rows(w.topk_idx.numpy(), ref_map)[sample].flatten()
-        sidx, smap = sub_problem(w.topk_idx.numpy(), sample, E)
-        rows = bits(P[torch.from_numpy(r).to(DEV)])
-        ref = oracle.unpermute_ep(rows, w.probs.numpy()[sample], sidx, smap, ep, partials, fp64)
-        assert_bits_equal(bits(out)[sample], ref, "unpermute_ep sample")
+    ref = oracle.unpermute_ep(bits(P), w.probs.numpy(), w.topk_idx.numpy(), ref_map, ep,
+                              partials, fp64)
+    assert_bits_equal(bits(out), ref, "unpermute_ep")
 
 
 def test_unpermute_ep_one_rank_equals_unpermute(m):
@@ -374,23 +350,14 @@ def test_unpermute_bwd_configs(m, name):
     d_p = sentinel_f32((T, k))
     m.moe_unpermute_bwd(dy, idx, rm, probs, fwd_in, d_in=d_in, d_probs=d_p)
     r_all = oracle_rows(w.topk_idx.numpy(), ref_map)
-    sample = np.arange(T) if T <= 4096 else np.sort(
-        np.random.default_rng(2).choice(T, 384, replace=False))
-    r = r_all[sample].flatten()
-    sidx, smap = sub_problem(w.topk_idx.numpy(), sample)
-    fin_rows = bits(fwd_in[torch.from_numpy(r).to(DEV)])
-    dy_rows = workloads.bf16_bits(w.dy[sample])
-    ref_in, ref_p = oracle.unpermute_bwd(dy_rows, fin_rows, w.probs.numpy()[sample], sidx, smap)
-    if T <= 4096:
-        # every row of d_in, in the oracle's own layout
-        full_in, _ = oracle.unpermute_bwd(workloads.bf16_bits(w.dy), bits(fwd_in),
-                                          w.probs.numpy(), w.topk_idx.numpy(), ref_map)
-        assert_bits_equal(bits(d_in), full_in, "unpermute_bwd act grad")
-    else:
-        assert_bits_equal(bits(d_in[torch.from_numpy(r).to(DEV)]), ref_in,
-                          "unpermute_bwd act grad sample")
-    got_p = d_p.cpu().numpy()[sample]
-    worst = dprob_ok(got_p, fin_rows.reshape(len(sample), k, H), dy_rows, ref_p)
+    dy_rows = workloads.bf16_bits(w.dy)
+    ref_in, ref_p = oracle.unpermute_bwd(dy_rows, bits(fwd_in), w.probs.numpy(),
+                                         w.topk_idx.numpy(), ref_map)
+    assert_bits_equal(bits(d_in), ref_in, "unpermute_bwd act grad")
+    del ref_in
+    # the forward rows of each (token, slot), for the prob-grad bound
+    fin_rows = bits(fwd_in[torch.from_numpy(r_all.flatten().astype(np.int64)).to(DEV)])
+    worst = dprob_ok(d_p.cpu().numpy(), fin_rows.reshape(T, k, H), dy_rows, ref_p)
     say(f"  prob-grad worst error / scale = {worst:.3g}")
     # unweighted: plain scatter of d_out
     d_in0 = sentinel_bf16((T * k, H))
@@ -413,19 +380,9 @@ def test_permute_bwd_configs(m, name):
     d_x = sentinel_bf16((T, H))
     d_p = sentinel_f32((T, k))
     m.moe_permute_bwd(dP, idx, rm, dpp, d_x=d_x, d_probs=d_p)
-    if T <= 4096:
-        ref_x, ref_p = oracle.permute_bwd(bits(dP), dpp.cpu().numpy(), w.topk_idx.numpy(),
-                                          ref_map)
-        assert_bits_equal(bits(d_x), ref_x, "permute_bwd")
-        assert_bits_equal(d_p.cpu().numpy(), ref_p, "permute_bwd probs")
-    else:
-        sample = np.sort(np.random.default_rng(3).choice(T, 512, replace=False))
-        r = oracle_rows(w.topk_idx.numpy(), ref_map)[sample].flatten()
-        sidx, smap = sub_problem(w.topk_idx.numpy(), sample)
-        ref_x, ref_p = oracle.permute_bwd(bits(dP[torch.from_numpy(r).to(DEV)]),
-                                          dpp.cpu().numpy()[r], sidx, smap)
-        assert_bits_equal(bits(d_x)[sample], ref_x, "permute_bwd sample")
-        assert_bits_equal(d_p.cpu().numpy()[sample], ref_p, "permute_bwd probs sample")
+    ref_x, ref_p = oracle.permute_bwd(bits(dP), dpp.cpu().numpy(), w.topk_idx.numpy(), ref_map)
+    assert_bits_equal(bits(d_x), ref_x, "permute_bwd")
+    assert_bits_equal(d_p.cpu().numpy(), ref_p, "permute_bwd probs")
 
 
 @pytest.mark.parametrize("T,H,E,k", [(1, 8, 2, 1), (37, 7, 9, 3), (100, 24, 16, 2),
@@ -871,6 +828,79 @@ def test_chunk_negative_size_sets_status(m):
         assert int(st.item()) & m.DEV_BAD_CHUNKS, H
         assert bool((rm == -1).all()) and bool((out.view(torch.int16) == 0).all()), H
         assert bool((off == 0).all()) and bool((out_p == 0).all()), H
+
+
+@pytest.mark.parametrize("H,N,bwd", [(64, 2100, False), (64, 2100, True),
+                                     (2048, 9000, False), (7168, 700, True)])
+def test_restore_stale_map(m, H, N, bwd):
+    """A row map saved for larger split sizes, restored with smaller ones: the
+    entries at or past the new token total are dropped and reported (a status
+    bit, no race with the zero tail), and every row matches the oracle's
+    defined output.  Also through the backward of the pad (the same copy)."""
+    say(f"restore stale map H={H} N={N} bwd={bwd}")
+    cw = workloads.chunked(N, seed=61, H=H, num_ranks=4, num_experts=6, align=16, num_empty=3)
+    x, probs = cw.x.to(DEV), cw.probs.to(DEV)
+    order = cw.sorted_idx.to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, out_p, rm, _ = _run_chunks(m, cw, x, probs, cw.split_sizes.to(DEV), order, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    small = workloads.chunk_sizes(N // 2, 4, 6, 3, torch.Generator().manual_seed(62))
+    nan_fill = sentinel_bf16((cw.N_cap, H))
+    nan_probs = sentinel_f32((cw.N_cap,))
+    st2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    call = m.moe_sort_chunks_and_pad_bwd if bwd else m.moe_unpad_and_restore_chunks
+    kw = {"d_in": nan_fill, "d_in_probs": nan_probs} if bwd else \
+        {"out": nan_fill, "out_probs": nan_probs}
+    back, back_p = call(out, rm, small.to(DEV), cw.N_cap, out_p, dev_status=st2, **kw)
+    torch.cuda.synchronize()
+    ref_b, ref_bp, ost = oracle.unpad_and_restore_chunks(
+        bits(out), out_p.cpu().numpy(), rm.cpu().numpy(), small.numpy(), cw.N_cap,
+        with_status=True)
+    assert ost == 4
+    assert int(st2.item()) & m.DEV_BAD_ROW
+    assert_bits_equal(bits(back), ref_b, "restored rows (stale map)")
+    assert_bits_equal(back_p.cpu().numpy(), ref_bp, "restored probs (stale map)")
+
+
+def test_binding_rejects_bad_shapes(m):
+    """Caller-given buffers of the wrong size or dtype are refused before any
+    launch (a short buffer would be read or written past its end)."""
+    say("binding shape checks")
+    w = workloads.random_routed(32, 64, 8, 2, seed=3)
+    x, idx, probs, dy = to_dev(w)
+    rm, _ = m.moe_make_row_id_map(idx, 8)
+    P, pp = m.moe_permute(x, idx, rm, probs)
+    with pytest.raises(ValueError):                          # d_out one token short
+        m.moe_unpermute_bwd(dy[:-1], idx, rm, probs, P)
+    cw = workloads.chunked(300, seed=4, H=64, num_ranks=2, num_experts=4, align=8,
+                           num_empty=1)
+    cx, cp = cw.x.to(DEV), cw.probs.to(DEV)
+    sz, order = cw.split_sizes.to(DEV), cw.sorted_idx.to(DEV)
+    with pytest.raises(TypeError):                           # bf16 slot for fp32 probs
+        m.moe_sort_chunks_and_pad(cx, sz, order, cw.chunks_per_group, cw.align, cw.out_cap, cp,
+                                  out_probs=torch.empty(cw.out_cap, dtype=torch.bfloat16,
+                                                        device=DEV))
+    out, out_p, rmap, _ = m.moe_sort_chunks_and_pad(cx, sz, order, cw.chunks_per_group,
+                                                    cw.align, cw.out_cap, cp)
+    with pytest.raises(TypeError):
+        m.moe_unpad_and_restore_chunks(out, rmap, sz, cw.N_cap, out_p,
+                                       out_probs=torch.empty(cw.N_cap, dtype=torch.bfloat16,
+                                                             device=DEV))
+    with pytest.raises(ValueError):                          # prob output too short
+        m.moe_unpad_and_restore_chunks(out, rmap, sz, cw.N_cap, out_p,
+                                       out_probs=torch.empty(cw.N_cap - 1, dtype=torch.float32,
+                                                             device=DEV))
+    with pytest.raises(ValueError):
+        m.moe_sort_chunks_and_pad_bwd(out, rmap, sz, cw.N_cap, out_p,
+                                      d_in_probs=torch.empty(3, dtype=torch.float32,
+                                                             device=DEV))
+    with pytest.raises(TypeError):
+        m.moe_unpad_and_restore_chunks_bwd(cx, rmap, cw.out_cap, cp,
+                                           d_in_probs=torch.empty(cw.out_cap,
+                                                                  dtype=torch.bfloat16,
+                                                                  device=DEV))
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("N", [8192, 32768])

@@ -25,9 +25,7 @@ PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
 
 _UNPERMUTE_SLOT = (
     "for (int j = 0; j < k; j++) {\n"
-    "                int64_t r;\n"
-    "                int s = slot_row(topk_idx, row_id_map, T, k, E, n_rows, t, j, &r);\n"
-    "                if (s) return s;\n"
+    "                int64_t r = dest_row(topk_idx, row_id_map, T, k, t, j);\n"
     "                float p = probs ? probs[(int64_t)t * k + j] : 1.0f;\n"
     "                acc = fmaf(")
 
@@ -142,6 +140,12 @@ MUTATIONS = [
     ("restore_overflow_accepted",
      "    if (n_act > N_cap) return ORC_OVERFLOW;\n    return restore_copy(",
      "    return restore_copy("),
+    ("restore_stale_entry_copied",
+     "if (s >= n_act) { status = ORC_BAD_ROW; continue; }",
+     "if (s >= N_cap) { status = ORC_BAD_ROW; continue; }"),
+    ("restore_stale_entry_unreported",
+     "if (s >= n_act) { status = ORC_BAD_ROW; continue; }",
+     "if (s >= n_act) continue;"),
 ]
 
 _RUNNER = (
@@ -157,7 +161,8 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
     mutant_c.write_text(src.replace(old, new, 1))
     mutant_so = tmp_path / "liboracle_mutant.so"
     subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
-                           "-shared", "-fPIC", str(mutant_c), "-o", str(mutant_so), "-lm"])
+                           "-fopenmp", "-shared", "-fPIC", str(mutant_c), "-o", str(mutant_so),
+                           "-lm"])
     r = subprocess.run([sys.executable, "-c", _RUNNER, ROOT, str(mutant_so), PINS],
                        capture_output=True, text=True, timeout=600, cwd=str(tmp_path))
     assert r.returncode == 1, (

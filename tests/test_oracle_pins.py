@@ -457,6 +457,73 @@ def test_chunk_restore_zero_tail_and_errors():
     np.testing.assert_array_equal(offs0, [0, 0, 4])
 
 
+
+def test_chunk_restore_stale_map():
+    """A row map saved for a larger routing, restored with smaller split sizes
+    (TransformerEngine PR "Fuse MoE chunk sorting and padding", Changes: the
+    restore reuses the saved map).  Entries that name a source row at or past
+    the new token total are dropped and reported (status 4); the restored
+    buffer is still the defined one, built here by a direct walk over the map:
+    zero rows from the token total on, every other mapped row copied."""
+    s_big = np.array([3, 2, 0, 4, 1, 2], np.int32)     # 12 tokens
+    q = np.array([1, 3, 5, 0, 2, 4], np.int32)
+    n_cap, out_cap = 14, 24
+    x = (np.arange(n_cap * 3, dtype=np.uint16).reshape(n_cap, 3) + 1)
+    padded, pp, rm, _ = oracle.sort_chunks_and_pad(x, np.arange(n_cap, dtype=np.float32) + 1,
+                                                   s_big, q, 2, 4, out_cap)
+    s_small = np.array([2, 1, 0, 2, 1, 1], np.int32)   # 7 tokens: a stale map
+    n_act = int(s_small.sum())
+    exp = np.zeros((n_cap, 3), np.uint16)
+    exp_p = np.zeros(n_cap, np.float32)
+    stale = 0
+    for d in range(out_cap):
+        src = int(rm[d])
+        if 0 <= src < n_act:
+            exp[src] = padded[d]
+            exp_p[src] = pp[d]
+        elif src >= n_act:
+            stale += 1
+    assert stale > 0
+    back, back_p, st = oracle.unpad_and_restore_chunks(padded, pp, rm, s_small, n_cap,
+                                                      with_status=True)
+    assert st == 4
+    np.testing.assert_array_equal(back, exp)
+    np.testing.assert_array_equal(back_p, exp_p)
+    # the backward of the pad is the same restore, with the same rule
+    d_in, d_in_p, st2 = oracle.sort_chunks_and_pad_bwd(padded, pp, rm, s_small, n_cap,
+                                                       with_status=True)
+    assert st2 == 4
+    np.testing.assert_array_equal(d_in, exp)
+    np.testing.assert_array_equal(d_in_p, exp_p)
+    # the map that belongs to the sizes restores without a status
+    back2, _, st3 = oracle.unpad_and_restore_chunks(padded, None, rm, s_big, n_cap,
+                                                    with_status=True)
+    assert st3 == 0
+    np.testing.assert_array_equal(back2[:12], x[:12])
+
+
+def test_thread_count_does_not_change_results():
+    """The per-token loops give the same bits on one thread and on many."""
+    w = workloads.random_routed(96, 40, 12, 3, seed=11)
+    idx, pr = w.topk_idx.numpy(), w.probs.numpy()
+    xb, dyb = workloads.bf16_bits(w.x), workloads.bf16_bits(w.dy)
+    rm, _ = oracle.row_id_map(idx, 12)
+    before = oracle.threads()
+    outs = []
+    try:
+        for n in (1, max(2, before)):
+            oracle.set_threads(n)
+            P, pp = oracle.permute(xb, pr, idx, rm)
+            y = oracle.unpermute(P, pr, idx, rm)
+            ye = oracle.unpermute_ep(P, pr, idx, rm, 4, True, True)
+            dP, dp = oracle.unpermute_bwd(dyb, P, pr, idx, rm)
+            dx, dpp = oracle.permute_bwd(dP, pp, idx, rm)
+            outs.append([P, pp, y, ye, dP, dp, dx, dpp])
+    finally:
+        oracle.set_threads(before)
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
 def _one_token_unpermute(x_vals, p_vals):
     """Unpermute of a single token whose k slots carry rows x_vals (exact
     bf16 values, one hidden element) with weights p_vals."""

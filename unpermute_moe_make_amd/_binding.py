@@ -255,6 +255,8 @@ def moe_unpermute_bwd(d_out: torch.Tensor, topk_idx: torch.Tensor, row_id_map: t
     _bf16_like_2d(d_out, "d_out")
     H = d_out.shape[1]
     n = T * k
+    if d_out.shape[0] != T:
+        raise ValueError("d_out must have num_tokens rows")
     _opt(probs, "probs", torch.float32, (T, k))
     _opt(fwd_in, "fwd_in", d_out.dtype, (n, H))
     d_in = torch.empty((n, H), dtype=d_out.dtype, device=d_out.device) if d_in is None else \
@@ -565,6 +567,14 @@ def _probs1d(t, name, n):
     return t
 
 
+def _prob_out(t, name, src, n):
+    """A caller-given prob output: the dtype of the probs it receives and n
+    entries (the kernels store src's element width into it)."""
+    if t is None:
+        return None
+    return _need(t, name, src.dtype if src is not None else None, (n,))
+
+
 def moe_sort_chunks_and_pad(inp: torch.Tensor, split_sizes: torch.Tensor,
                             sorted_idx: torch.Tensor, chunks_per_group: int, align: int,
                             out_cap: int, probs: Optional[torch.Tensor] = None, *, out=None,
@@ -583,8 +593,7 @@ def moe_sort_chunks_and_pad(inp: torch.Tensor, split_sizes: torch.Tensor,
         _need(out, "out", inp.dtype, (out_cap, H))
     if probs is not None and out_probs is None:
         out_probs = torch.empty(out_cap, dtype=probs.dtype, device=dev)
-    if out_probs is not None:
-        _need(out_probs, "out_probs", probs.dtype if probs is not None else None, (out_cap,))
+    _prob_out(out_probs, "out_probs", probs, out_cap)
     row_map = torch.empty(out_cap, dtype=torch.int32, device=dev) if row_map is None else \
         _need(row_map, "row_map", torch.int32, (out_cap,))
     padded_offsets = (torch.empty(G + 1, dtype=torch.int32, device=dev)
@@ -614,6 +623,7 @@ def moe_unpad_and_restore_chunks(inp: torch.Tensor, row_map: torch.Tensor,
         _need(out, "out", inp.dtype, (n_cap, H))
     if probs is not None and out_probs is None:
         out_probs = torch.empty(n_cap, dtype=probs.dtype, device=dev)
+    _prob_out(out_probs, "out_probs", probs, n_cap)
     pb = probs.element_size() if probs is not None else 4
     _check(_lib.moe_unpad_and_restore_chunks(
         _ptr(inp), _ptr(probs), inp.element_size(), pb, _ptr(row_map), _ptr(split_sizes),
@@ -637,6 +647,7 @@ def moe_sort_chunks_and_pad_bwd(d_out: torch.Tensor, row_map: torch.Tensor,
         _need(d_in, "d_in", d_out.dtype, (n_cap, H))
     if d_out_probs is not None and d_in_probs is None:
         d_in_probs = torch.empty(n_cap, dtype=d_out_probs.dtype, device=dev)
+    _prob_out(d_in_probs, "d_in_probs", d_out_probs, n_cap)
     pb = d_out_probs.element_size() if d_out_probs is not None else 4
     _check(_lib.moe_sort_chunks_and_pad_bwd(
         _ptr(d_out), _ptr(d_out_probs), d_out.element_size(), pb, _ptr(row_map),
@@ -658,6 +669,7 @@ def moe_unpad_and_restore_chunks_bwd(d_out: torch.Tensor, row_map: torch.Tensor,
         _need(d_in, "d_in", d_out.dtype, (out_cap, H))
     if d_out_probs is not None and d_in_probs is None:
         d_in_probs = torch.empty(out_cap, dtype=d_out_probs.dtype, device=dev)
+    _prob_out(d_in_probs, "d_in_probs", d_out_probs, out_cap)
     pb = d_out_probs.element_size() if d_out_probs is not None else 4
     _check(_lib.moe_unpad_and_restore_chunks_bwd(
         _ptr(d_out), _ptr(d_out_probs), d_out.element_size(), pb, _ptr(row_map), out_cap, H,

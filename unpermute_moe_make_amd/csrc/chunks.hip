@@ -609,6 +609,13 @@ __global__ __launch_bounds__(kCopyThreads) void restore_copy_kernel(
   if (n_act > n_cap) bad |= MOE_DEV_OVERFLOW;
 #pragma unroll
   for (int i = 0; i < kRestoreIlp; i++) {
+    // An entry at or past the token total (a map saved for other split
+    // sizes) would race the zero tail for its row: it is dropped and
+    // reported.  The row's load above was harmless (the unit's own slice).
+    if (s[i] >= n_act) {
+      bad |= MOE_DEV_BAD_ROW;
+      s[i] = -1;
+    }
     if (s[i] >= 0) {
       st_row<NTS>(v[i], out + (int64_t)s[i] * W + c[i]);
       if (c[i] == 0 && with_probs) {

@@ -52,6 +52,60 @@ template <bool NT, typename U> __device__ __forceinline__ void st_row(U v, U *p)
 #endif
 constexpr int64_t kStreamBytes = (int64_t)MOE_STREAM_MIB << 20;
 
+// Source-row prefetch of the streaming row scatters (the permutes).  When a
+// call's rows do not fit the Infinity Cache, the row a workgroup copies comes
+// from HBM while the rest of the chip streams its stores out, and every store
+// of the workgroup waits for that read.  So each workgroup also reads one
+// 16-byte piece of every 128-byte line of the row `ahead` tokens later; by
+// the time that row's own workgroup starts, its lines are cached.  The
+// distance is two dispatch rounds: twice the tokens the chip holds at once
+// (256 CUs, 32 wave slots each, one token per workgroup), a multiple of 8, so
+// under the round-robin dispatch over the 8 XCDs both workgroups run on the
+// same XCD.  Measured on the 16384 x 7168 bf16 permute (7-wave workgroups,
+// 2048 tokens ahead) with cold caches: 392-396 us against 420, the same warm
+// time; 1024 to 4096 ahead within 2%.  At one round ahead (FP8 rows of the
+// same size, 4-wave workgroups, 2048 ahead) it was slower: 228 us against
+// 198.  The lanes that issue the reads matter as well: the lanes whose own
+// units start a line (8 per wave, in every wave) give the gain, while one
+// read per lane on lanes 0..111 (64 lines per instruction) gave none.
+constexpr int kNumCUs = 256;
+constexpr int kWaveSlotsPerCU = 32;
+inline int prefetch_ahead(int threads) {
+  const int waves = (threads + kWave - 1) / kWave;
+  const int per_cu = kWaveSlotsPerCU / waves > 0 ? kWaveSlotsPerCU / waves : 1;
+  return 2 * kNumCUs * per_cu;
+}
+
+// All words of a unit folded into one.  (Keeping only one word of a 16-byte
+// load would free its other three registers at once, and the compiler then
+// waits for the load before reusing them.)
+template <typename U> __device__ __forceinline__ uint32_t fold_words(const U &v) {
+  if constexpr (sizeof(U) == 16) return v.x ^ v.y ^ v.z ^ v.w;
+  else return (uint32_t)v;
+}
+
+// Issue the prefetch of units [begin, end) of `row`, a workgroup's slice of
+// blockDim.x * VPT units (lane l's units: begin + l + i * blockDim.x): each
+// lane reads those of its units that start a 128-byte stretch of the row.
+// The other lanes (and all lanes when row == NULL) read `fallback`, an
+// address the workgroup reads anyway, so the load is not under a branch.
+// Returns the loaded words, to be passed to keep_loaded() after the
+// workgroup's stores, so the wave waits for them only at its end.
+template <typename U, int VPT>
+__device__ __forceinline__ uint32_t prefetch_lines(const U *__restrict__ row, int64_t begin,
+                                                   int64_t end, const U *__restrict__ fallback) {
+  constexpr int64_t kPerLine = 128 / (int64_t)sizeof(U);
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t u = (int64_t)threadIdx.x + (int64_t)i * blockDim.x;
+    const bool on = row != nullptr && begin + u < end && ((begin + u) % kPerLine) == 0;
+    w ^= fold_words(*(on ? row + begin + u : fallback));
+  }
+  return w;
+}
+__device__ __forceinline__ void keep_loaded(uint32_t w) { asm volatile("" ::"v"(w)); }
+
 // bf16 -> fp32 is exact: the bf16 pattern is the top half of the binary32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -136,6 +190,33 @@ __device__ __forceinline__ void report(int32_t *status, int bits) {
   if (status != nullptr && bits != 0) atomicOr(status, bits);
 }
 
+// A token's side row held in registers while it is stored to each of the
+// token's destinations: lane l of the first wave keeps words 4l .. 4l+3, when
+// the row is whole 4-byte words and has at most 256 of them (FP8 rows of 7168
+// elements with fp32 scales per 128 have 56).  Reading the row inside the
+// destination loop makes each read wait for the stores issued before it (the
+// vector memory counter counts both in issue order), one destination's
+// stores at a time.
+constexpr int kSideRegs = 4;
+constexpr int64_t kSideHeldWords = (int64_t)kSideRegs * kWave;
+struct SideCache {
+  uint32_t w[kSideRegs];
+  bool held;
+};
+
+__device__ __forceinline__ SideCache load_side_row(const SideRows &s, int64_t from) {
+  SideCache c;
+  const int64_t n = s.bytes / 4;
+  c.held = s.words && n <= kSideHeldWords;
+  const uint32_t *a = reinterpret_cast<const uint32_t *>(s.src) + from * n;
+#pragma unroll
+  for (int i = 0; i < kSideRegs; i++) {
+    const int64_t idx = (int64_t)threadIdx.x * kSideRegs + i;
+    c.w[i] = (c.held && idx < n) ? a[idx] : 0u;
+  }
+  return c;
+}
+
 // Row `from` of a side tensor to row `to`, by the whole workgroup.
 __device__ __forceinline__ void copy_side_row(const SideRows &s, int64_t from, int64_t to) {
   if (s.words) {
@@ -147,6 +228,23 @@ __device__ __forceinline__ void copy_side_row(const SideRows &s, int64_t from, i
     const uint8_t *a = s.src + from * s.bytes;
     uint8_t *b = s.dst + to * s.bytes;
     for (int64_t i = threadIdx.x; i < s.bytes; i += blockDim.x) b[i] = a[i];
+  }
+}
+
+// The side row of load_side_row to row `to` (copied from row `from` when it
+// was not held).
+__device__ __forceinline__ void store_side_row(const SideRows &s, const SideCache &c, int64_t from,
+                                               int64_t to) {
+  if (!c.held) {
+    copy_side_row(s, from, to);
+    return;
+  }
+  const int64_t n = s.bytes / 4;
+  uint32_t *b = reinterpret_cast<uint32_t *>(s.dst) + to * n;
+#pragma unroll
+  for (int i = 0; i < kSideRegs; i++) {
+    const int64_t idx = (int64_t)threadIdx.x * kSideRegs + i;
+    if (idx < n) b[idx] = c.w[i];
   }
 }
 

@@ -61,7 +61,7 @@ template <typename U, int VPT, int NTM, bool SIDE>
 __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
     const U *__restrict__ x, const float *__restrict__ probs, const int32_t *__restrict__ map,
     int T, int64_t V, int E, int n_rows, U *__restrict__ out, float *__restrict__ out_probs,
-    SideRows side, int32_t *__restrict__ dev_status) {
+    SideRows side, int32_t *__restrict__ dev_status, int ahead) {
   __shared__ int64_t srow[kSlotChunk];
   __shared__ int szero[kSlotChunk];
   const int64_t tb = spill_block();
@@ -77,9 +77,13 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
     const int64_t c = c0 + (int64_t)i * blockDim.x;
     if (c < V) v[i] = ld_row<(NTM & 1) != 0>(xr + c);
   }
+  SideCache sc{};
+  if (SIDE && blockIdx.y == 0) sc = load_side_row(side, t);
   U zero;
   zero = U{};
   int bad = 0;
+  constexpr bool kPrefetch = NTM != 0 && !SIDE;   // as in the top-k permute
+  uint32_t pf = 0;
   const int n = mask_count(mrow, E, &bad);
   for (int j0 = 0; j0 < n; j0 += kSlotChunk) {
     const int nj = min(kSlotChunk, n - j0);
@@ -95,6 +99,14 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
       srow[threadIdx.x] = r;
       szero[threadIdx.x] = z;
     }
+    // A streaming call also prefetches this slice of a later token's row
+    // (after the first slot loads, which wait in issue order).
+    if (kPrefetch && j0 == 0) {
+      const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
+      pf = prefetch_lines<U, VPT>((int64_t)t + ahead < T ? x + (int64_t)(t + ahead) * V
+                                                         : nullptr,
+                                  s0, min(V, s0 + (int64_t)blockDim.x * VPT), xr + s0);
+    }
     __syncthreads();
     for (int j = 0; j < nj; j++) {
       const int64_t r = srow[j];
@@ -106,10 +118,11 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
         const int64_t c = c0 + (int64_t)i * blockDim.x;
         if (c < V) st_row<(NTM & 2) != 0>(z ? zero : v[i], orow + c);
       }
-      if (SIDE && blockIdx.y == 0) copy_side_row(side, t, r);
+      if (SIDE && blockIdx.y == 0) store_side_row(side, sc, t, r);
     }
     __syncthreads();
   }
+  if (kPrefetch) keep_loaded(pf);
   if (blockIdx.y == 0) report(dev_status, bad);
 }
 
@@ -326,7 +339,7 @@ void mask_permute_dispatch(const void *x, const float *probs, const int32_t *map
   U *op = static_cast<U *>(out);
 #define MOE_MASK_PERMUTE(VPTV)                                                                 \
   hipLaunchKernelGGL((mask_permute_kernel<U, VPTV, NTM, SIDE>), grid, block, 0, s, xp, probs, \
-                     map, T, V, E, n_rows, op, out_probs, side, st)
+                     map, T, V, E, n_rows, op, out_probs, side, st, prefetch_ahead(sh.threads))
   switch (sh.vpt) {
     case 1: MOE_MASK_PERMUTE(1); break;
     case 2: MOE_MASK_PERMUTE(2); break;

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
     const U *__restrict__ x, const float *__restrict__ probs,
     const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
     int64_t V, int k, int E, int n_rows, U *__restrict__ out, float *__restrict__ out_probs,
-    SideRows side, int32_t *__restrict__ dev_status) {
+    SideRows side, int32_t *__restrict__ dev_status, int ahead) {
   __shared__ int64_t srow[kMaxTopk];
   const int64_t tb = spill_block();
   if (tb >= T) return;  // a workgroup past the last token
@@ -93,11 +93,25 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
     const int64_t c = c0 + (int64_t)i * blockDim.x;
     if (c < V) v[i] = ld_row<(NTM & 1) != 0>(xr + c);
   }
+  SideCache sc{};
+  if (SIDE && blockIdx.y == 0) sc = load_side_row(side, t);
   const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
   if (blockIdx.y == 0 && threadIdx.x < k) {
     report(dev_status, bad);
     const int64_t r = srow[threadIdx.x];
     if (r >= 0 && out_probs != nullptr) out_probs[r] = probs[(int64_t)t * k + threadIdx.x];
+  }
+  // A streaming call also prefetches this slice of a later token's row,
+  // after the slot loads (the vector memory counter retires in issue order,
+  // so a wait for an earlier load never waits for it).  Not with side rows:
+  // on the 16384 x 7168 FP8 permute (4-wave workgroups) it made the cold
+  // call slower, 213 us against 197 (199 at twice the distance).
+  constexpr bool kPrefetch = NTM != 0 && !SIDE;
+  uint32_t pf = 0;
+  if constexpr (kPrefetch) {
+    const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
+    pf = prefetch_lines<U, VPT>((int64_t)t + ahead < T ? x + (int64_t)(t + ahead) * V : nullptr,
+                                s0, min(V, s0 + (int64_t)blockDim.x * VPT), xr + s0);
   }
   __syncthreads();
 
@@ -110,8 +124,9 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
       const int64_t c = c0 + (int64_t)i * blockDim.x;
       if (c < V) st_row<(NTM & 2) != 0>(v[i], orow + c);
     }
-    if (SIDE && blockIdx.y == 0) copy_side_row(side, t, r);
+    if (SIDE && blockIdx.y == 0) store_side_row(side, sc, t, r);
   }
+  if (kPrefetch) keep_loaded(pf);
 }
 
 // ---------------------------------------------------------------- combine --
@@ -441,7 +456,8 @@ hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *to
   U *op = static_cast<U *>(out);
 #define MOE_PERMUTE(VPTV)                                                                     \
   hipLaunchKernelGGL((permute_kernel<U, VPTV, NTM, SIDE>), grid, block, 0, s, xp, probs,       \
-                     topk_idx, row_id_map, T, V, k, E, n_rows, op, out_probs, side, dev_status)
+                     topk_idx, row_id_map, T, V, k, E, n_rows, op, out_probs, side, dev_status, \
+                     prefetch_ahead(sh.threads))
   switch (sh.vpt) {
     case 1: MOE_PERMUTE(1); break;
     case 2: MOE_PERMUTE(2); break;
