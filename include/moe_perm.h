@@ -120,6 +120,30 @@ MOE_PERM_API int moe_make_row_id_map(const int32_t *topk_idx, int num_tokens, in
                                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Row map without a workspace argument, for callers that cannot allocate
+ * device memory: code being captured into a hipGraph, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus the workspace),
+ * checks and results as moe_make_row_id_map.  The scratch is a fixed array
+ * of MOE_NOALLOC_SCRATCH_BYTES in the library's device data: one copy per
+ * GPU, held until the process ends; this call allocates and frees nothing.
+ *   MOE_ERR_WORKSPACE  when moe_make_row_id_map_workspace_bytes(...) exceeds
+ *                      MOE_NOALLOC_SCRATCH_BYTES (about 0.14 * num_tokens *
+ *                      num_experts bytes are needed: e.g. 65536 tokens with
+ *                      up to 896 experts fit).
+ *   MOE_ERR_HIP        when the array's device address cannot be looked up.
+ * Every call on one GPU uses that GPU's array: two calls that can run at the
+ * same time on one GPU (unordered streams) race and give unspecified maps.
+ * The array needs no clearing (each call writes every scratch byte it reads).
+ * The first call on a device looks up the array's address (a host call, no
+ * stream work); make it once before capturing a graph.
+ * ------------------------------------------------------------------------ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+MOE_PERM_API int moe_make_row_id_map_noalloc(const int32_t *topk_idx, int num_tokens, int topk,
+                                             int num_experts, int32_t *row_id_map,
+                                             int32_t *expert_offsets, int32_t *dev_status,
+                                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * (2) Permute -- gather-copy of each token row to its top-k rows.
  *
  * [TE-mask] _permute_kernel: a token's hidden row is stored unchanged to each

@@ -31,7 +31,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     dyn = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in dyn.splitlines() if " T " in line}
@@ -77,6 +77,19 @@ def test_row_map_host_errors(lib):
     assert f(P(FAKE), 16, 4, 32, P(FAKE), P(FAKE), None, P(FAKE + 16), need,
              None) == MOE_ERR_ALIGN
     assert f(P(MIS), 16, 4, 32, P(FAKE), P(FAKE), None, P(FAKE), need, None) == MOE_ERR_ALIGN
+
+
+def test_row_map_noalloc_host_errors(lib):
+    f = lib.moe_make_row_id_map_noalloc
+    P = ctypes.c_void_p
+    assert f(P(FAKE), 16, 0, 32, P(FAKE), P(FAKE), None, None) == MOE_ERR_SHAPE
+    assert f(P(FAKE), 16, 65, 100, P(FAKE), P(FAKE), None, None) == MOE_ERR_UNSUPPORTED
+    assert f(None, 16, 4, 32, P(FAKE), P(FAKE), None, None) == MOE_ERR_NULL
+    assert f(P(FAKE), 16, 4, 32, P(FAKE), None, None, None) == MOE_ERR_NULL
+    assert f(P(MIS), 16, 4, 32, P(FAKE), P(FAKE), None, None) == MOE_ERR_ALIGN
+    # a routing whose scratch need exceeds the library's fixed array
+    assert lib.moe_make_row_id_map_workspace_bytes(200000, 2, 512) > 8 << 20
+    assert f(P(FAKE), 200000, 2, 512, P(FAKE), P(FAKE), None, None) == MOE_ERR_WORKSPACE
 
 
 def test_permute_family_host_errors(lib):

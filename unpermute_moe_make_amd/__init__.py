@@ -4,6 +4,7 @@ Hand-written HIP kernels for gfx950 behind a C ABI (include/moe_perm.h),
 with a thin ctypes binding whose functions carry the C names:
 
   moe_make_row_id_map                 stable counting-sort routing row map
+  moe_make_row_id_map_noalloc         the same with the library's fixed scratch
   moe_permute / moe_permute_bwd       row scatter-copy and its gradient
   moe_unpermute / moe_unpermute_bwd   fixed slot-order FMA combine, gradient
   moe_unpermute_ep                    the combine with EP rank-ordered partials
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     MoeError,
     library_path,
     moe_make_row_id_map,
+    moe_make_row_id_map_noalloc,
     moe_make_row_id_map_workspace_bytes,
     moe_make_mask_row_id_map,
     moe_make_mask_row_id_map_workspace_bytes,

@@ -33,6 +33,7 @@ _SIGS = {
     "moe_status_string": ([_I], ctypes.c_char_p),
     "moe_make_row_id_map_workspace_bytes": ([_I, _I, _I], _Z),
     "moe_make_row_id_map": ([_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
+    "moe_make_row_id_map_noalloc": ([_P, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_permute": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "moe_unpermute": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_unpermute_ep": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
@@ -165,6 +166,28 @@ def moe_make_row_id_map(topk_idx: torch.Tensor, num_experts: int, *, row_id_map=
         _ptr(topk_idx), T, k, num_experts, _ptr(row_id_map), _ptr(expert_offsets),
         _ptr(_status_arg(dev_status)), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)), "moe_make_row_id_map")
+    return row_id_map, expert_offsets
+
+
+def moe_make_row_id_map_noalloc(topk_idx: torch.Tensor, num_experts: int, *, row_id_map=None,
+                                expert_offsets=None, dev_status=None,
+                                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The row map with the library's fixed device scratch instead of a
+    workspace (the C call allocates nothing; given outputs are used as is)."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [num_tokens, topk]")
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    row_id_map = (torch.empty((num_experts, T), dtype=torch.int32, device=dev)
+                  if row_id_map is None else _need(row_id_map, "row_id_map", torch.int32,
+                                                   (num_experts, T)))
+    expert_offsets = (torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+                      if expert_offsets is None else
+                      _need(expert_offsets, "expert_offsets", torch.int32, (num_experts + 1,)))
+    _check(_lib.moe_make_row_id_map_noalloc(
+        _ptr(topk_idx), T, k, num_experts, _ptr(row_id_map), _ptr(expert_offsets),
+        _ptr(_status_arg(dev_status)), _stream(stream)), "moe_make_row_id_map_noalloc")
     return row_id_map, expert_offsets
 
 

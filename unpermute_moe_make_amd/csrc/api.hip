@@ -4,6 +4,8 @@
 // frees, synchronises or reads device memory.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "launch.h"
 #include "moe_perm.h"
 
@@ -96,12 +98,11 @@ MOE_PERM_API size_t moe_make_row_id_map_workspace_bytes(int num_tokens, int topk
   return moe::rowmap_workspace_bytes(num_tokens, topk, num_experts);
 }
 
-MOE_PERM_API int moe_make_row_id_map(const int32_t *topk_idx, int num_tokens, int topk,
-                                     int num_experts, int32_t *row_id_map,
-                                     int32_t *expert_offsets, int32_t *dev_status,
-                                     void *workspace, size_t workspace_bytes,
-                                     hipStream_t stream) {
-  const int T = num_tokens, k = topk, E = num_experts;
+namespace {
+
+// Checks of the row map calls, before any HIP call.
+int check_row_id_map(const int32_t *topk_idx, int T, int k, int E, const int32_t *row_id_map,
+                     const int32_t *expert_offsets, const int32_t *dev_status) {
   if (T < 0 || k < 1 || E < 1 || k > E) return MOE_ERR_SHAPE;
   if (k > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * k > INT32_MAX || (int64_t)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
@@ -110,6 +111,19 @@ MOE_PERM_API int moe_make_row_id_map(const int32_t *topk_idx, int num_tokens, in
   if (!aligned(topk_idx, 4) || !aligned(row_id_map, 4) || !aligned(expert_offsets, 4) ||
       !aligned(dev_status, 4))
     return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_PERM_API int moe_make_row_id_map(const int32_t *topk_idx, int num_tokens, int topk,
+                                     int num_experts, int32_t *row_id_map,
+                                     int32_t *expert_offsets, int32_t *dev_status,
+                                     void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  const int T = num_tokens, k = topk, E = num_experts;
+  const int st = check_row_id_map(topk_idx, T, k, E, row_id_map, expert_offsets, dev_status);
+  if (st) return st;
   if (T > 0) {
     const size_t need = moe::rowmap_workspace_bytes(T, k, E);
     if (workspace == nullptr || workspace_bytes < need) return MOE_ERR_WORKSPACE;
@@ -117,6 +131,52 @@ MOE_PERM_API int moe_make_row_id_map(const int32_t *topk_idx, int num_tokens, in
   }
   return hip_status(moe::launch_rowmap(topk_idx, T, k, E, row_id_map, expert_offsets,
                                        dev_status, workspace, stream));
+}
+
+// Scratch of the allocation-free row map: a file-scope device array, one copy
+// per GPU in the library's device data.  On the host `noalloc_scratch` names a
+// host-side stand-in, not device memory, so kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up on the
+// device's first call and kept.
+static __device__ __align__(256) unsigned char noalloc_scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_noalloc_scratch[kMaxScratchDevices];
+
+int noalloc_scratch_ptr(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+  void *p = g_noalloc_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_noalloc_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_PERM_API int moe_make_row_id_map_noalloc(const int32_t *topk_idx, int num_tokens, int topk,
+                                             int num_experts, int32_t *row_id_map,
+                                             int32_t *expert_offsets, int32_t *dev_status,
+                                             hipStream_t stream) {
+  const int T = num_tokens, k = topk, E = num_experts;
+  int st = check_row_id_map(topk_idx, T, k, E, row_id_map, expert_offsets, dev_status);
+  if (st) return st;
+  void *ws = nullptr;
+  if (T > 0) {
+    if (moe::rowmap_workspace_bytes(T, k, E) > MOE_NOALLOC_SCRATCH_BYTES)
+      return MOE_ERR_WORKSPACE;
+    st = noalloc_scratch_ptr(&ws);
+    if (st) return st;
+  }
+  return hip_status(moe::launch_rowmap(topk_idx, T, k, E, row_id_map, expert_offsets,
+                                       dev_status, ws, stream));
 }
 
 MOE_PERM_API int moe_permute(const void *x, const float *probs, const int32_t *topk_idx,
