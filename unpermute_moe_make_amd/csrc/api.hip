@@ -68,7 +68,9 @@ int side_rows(const void *scale, int scale_row_bytes, void *out_scale, moe::Side
   side->src = static_cast<const uint8_t *>(scale);
   side->dst = static_cast<uint8_t *>(out_scale);
   side->bytes = scale != nullptr ? scale_row_bytes : 0;
-  side->words = scale_row_bytes % 4 == 0 && aligned(scale, 4) && aligned(out_scale, 4);
+  side->words = scale_row_bytes % 16 == 0 && aligned(scale, 16) && aligned(out_scale, 16) ? 2
+                : scale_row_bytes % 4 == 0 && aligned(scale, 4) && aligned(out_scale, 4) ? 1
+                                                                                          : 0;
   if (scale == nullptr) return MOE_OK;
   if (scale_row_bytes < 1) return MOE_ERR_SHAPE;
   if (out_scale == nullptr) return MOE_ERR_NULL;

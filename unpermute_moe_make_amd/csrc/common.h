@@ -134,7 +134,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 // Round to odd from the hardware's nearest conversion: when it was inexact,
 // step one place toward zero if it rounded away (the truncated value; at
 // overflow, infinity becomes the largest finite fp32) and set the last bit.
-__device__ __forceinline__ uint32_t f64_to_bf16(double d) {
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
   const float f = (float)d;
   uint32_t u = __float_as_uint(f);
   const double back = (double)f;
@@ -142,7 +142,7 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double d) {
     if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1u;
     u |= 1u;
   }
-  return f32_to_bf16(__uint_as_float(u));
+  return __uint_as_float(u);
 }
 // Round an fp32 value to bf16 precision, keeping it as fp32.
 __device__ __forceinline__ float round_to_bf16(float f) {
@@ -209,9 +209,16 @@ __device__ __forceinline__ SideCache load_side_row(const SideRows &s, int64_t fr
   const int64_t n = s.bytes / 4;
   c.held = s.words && n <= kSideHeldWords;
   const uint32_t *a = reinterpret_cast<const uint32_t *>(s.src) + from * n;
+  const int64_t idx0 = (int64_t)threadIdx.x * kSideRegs;
+  if (s.words == 2 && c.held && idx0 < n) {
+    // rows of whole 16-byte units on 16-byte aligned bases: one access
+    const v4u q = *reinterpret_cast<const v4u *>(a + idx0);
+    c.w[0] = q.x; c.w[1] = q.y; c.w[2] = q.z; c.w[3] = q.w;
+    return c;
+  }
 #pragma unroll
   for (int i = 0; i < kSideRegs; i++) {
-    const int64_t idx = (int64_t)threadIdx.x * kSideRegs + i;
+    const int64_t idx = idx0 + i;
     c.w[i] = (c.held && idx < n) ? a[idx] : 0u;
   }
   return c;
@@ -241,9 +248,14 @@ __device__ __forceinline__ void store_side_row(const SideRows &s, const SideCach
   }
   const int64_t n = s.bytes / 4;
   uint32_t *b = reinterpret_cast<uint32_t *>(s.dst) + to * n;
+  const int64_t idx0 = (int64_t)threadIdx.x * kSideRegs;
+  if (s.words == 2) {
+    if (idx0 < n) *reinterpret_cast<v4u *>(b + idx0) = v4u{c.w[0], c.w[1], c.w[2], c.w[3]};
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kSideRegs; i++) {
-    const int64_t idx = (int64_t)threadIdx.x * kSideRegs + i;
+    const int64_t idx = idx0 + i;
     if (idx < n) b[idx] = c.w[i];
   }
 }

@@ -13,7 +13,8 @@ struct SideRows {
   const uint8_t *src;   // [rows][bytes]
   uint8_t *dst;         // [out rows][bytes]
   int64_t bytes;        // bytes per row
-  int words;            // 1: copy 4-byte words (bytes % 4 == 0, both bases aligned)
+  int words;            // 1: copy 4-byte words (bytes % 4 == 0, both bases aligned);
+                        // 2: 16-byte units as well (bytes % 16 == 0, bases 16-aligned)
 };
 
 // Row map (stable counting sort).
