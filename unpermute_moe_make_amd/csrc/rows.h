@@ -69,10 +69,18 @@ inline RowShape row_shape(int64_t V, bool allow_split) {
 }
 
 // Shape of the combine (unpermute, permute backward): MOE_GATHER_VPT (two)
-// units per lane when the row fits one pass of up to kRowThreads lanes, else
-// row_shape.
+// units per lane while that takes at most 256 lanes, else four units per lane
+// when the row fits one pass of up to kRowThreads lanes, else row_shape.
+// Measured: 4 KiB rows (256 units) 19.3 us with two units per lane against
+// 19.7 with four; 14 KiB rows (896 units, the 16384-token top-8 unpermute)
+// 341-344 us warm and 344-346 cold with four units on 224 lanes, against
+// 355-358 and 345-351 with two on 448 (one on 896: 350-353 and 338).
 inline RowShape gather_shape(int64_t V) {
   RowShape sh = row_shape_vpt(V, MOE_GATHER_VPT, kRowThreads);
+  if (sh.threads > 256) {
+    const RowShape four = row_shape_vpt(V, 4, kRowThreads);
+    if (four.threads != 0) sh = four;
+  }
   if (sh.threads == 0) sh = row_shape(V, true);
   return sh;
 }
