@@ -387,6 +387,7 @@ def test_permute_bwd_configs(m, name):
 
 @pytest.mark.parametrize("T,H,E,k", [(1, 8, 2, 1), (37, 7, 9, 3), (100, 24, 16, 2),
                                      (64, 64, 12, 9), (40, 136, 80, 64), (33, 2056, 12, 5),
+                                     (29, 4104, 12, 5), (19, 8200, 10, 3),
                                      (20, 7168, 16, 4), (9, 20480, 8, 8), (17, 20481, 4, 2),
                                      (300, 512, 32, 1), (50, 96, 6, 6), (3, 8, 64, 64),
                                      (17, 1, 4, 2)])
@@ -424,6 +425,28 @@ def test_row_kernels_edges(m, T, H, E, k):
     rx, rp = oracle.permute_bwd(bits(P), dpp.cpu().numpy(), ib, ref_map)
     assert_bits_equal(bits(d_x), rx, "permute_bwd")
     assert_bits_equal(d_pp.cpu().numpy(), rp, "permute_bwd probs")
+
+
+def test_permute_streaming_unaligned_rows(m):
+    """A call large enough to stream (and prefetch the source row of the token
+    two dispatch rounds ahead), with rows that are not whole 128-byte lines
+    (7176 bf16 = 14352 bytes), in full against the oracle."""
+    T, H, E, k = 6000, 7176, 40, 4
+    say(f"permute streaming unaligned rows T={T} H={H} E={E} k={k}")
+    w = workloads.random_routed(T, H, E, k, seed=71, with_dy=False)
+    ref_map, _ = oracle.row_id_map(w.topk_idx.numpy(), E)
+    x, idx, probs, _ = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    assert 2 * H * (T * k + T) > 256 << 20                  # the streaming path
+    out, out_p = m.moe_permute(x, idx, rm, probs, out=sentinel_bf16((T * k, H)),
+                               out_probs=sentinel_f32((T * k,)))
+    o, op = oracle.permute(workloads.bf16_bits(w.x), w.probs.numpy(), w.topk_idx.numpy(),
+                           ref_map)
+    assert_bits_equal(bits(out), o, "permute")
+    assert_bits_equal(out_p.cpu().numpy(), op, "permuted probs")
+    y = m.moe_unpermute(out, idx, rm, probs, out=sentinel_bf16((T, H)))
+    assert_bits_equal(bits(y), oracle.unpermute(o, w.probs.numpy(), w.topk_idx.numpy(),
+                                                ref_map), "unpermute")
 
 
 def test_row_kernels_misaligned_views(m):
