@@ -411,8 +411,9 @@ int oracle_unpermute_ep(const uint16_t *in, const float *probs, const int32_t *t
  *              (an fp32 product rounded to fp32, then cast to bf16; there is
  *              no addition, so no fused operation),
  *   prob grad: d_probs[t][j] = sum_h float(fwd_in[r_j][h]) * float(d_out[t][h]).
- * Megatron batch_invariant, _rank_tree_unpermute_bwd_kernel: each permuted
- * row belongs to one (token, slot), so the scatter has one writer per row.
+ * Megatron batch_invariant, _rank_tree_unpermute_bwd_kernel: a permuted row
+ * is owned by exactly one (token, slot) pair, hence one write per row in the
+ * scatter.
  * The pages leave the order of the prob-grad sum open; here each product of
  * two bf16 values is exact in fp64 and the products are summed in fp64, with
  * one final rounding to fp32 (a tolerance covers any fp32 order).
