@@ -62,8 +62,8 @@ constexpr int64_t kStreamBytes = (int64_t)MOE_STREAM_MIB << 20;
 // (256 CUs, 32 wave slots each, one token per workgroup), a multiple of 8, so
 // under the round-robin dispatch over the 8 XCDs both workgroups run on the
 // same XCD.  Measured on the 16384 x 7168 bf16 permute (7-wave workgroups,
-// 2048 tokens ahead) with cold caches: 392-396 us against 420, the same warm
-// time; 1024 to 4096 ahead within 2%.  At one round ahead (FP8 rows of the
+// 2048 tokens ahead) with cold caches: 385 us against 420 (issued after the
+// workgroup's stores), the same warm time; 1024 to 4096 ahead within 2%.  At one round ahead (FP8 rows of the
 // same size, 4-wave workgroups, 2048 ahead) it was slower: 228 us against
 // 198.  The lanes that issue the reads matter as well: the lanes whose own
 // units start a line (8 per wave, in every wave) give the gain, while one
@@ -89,8 +89,8 @@ template <typename U> __device__ __forceinline__ uint32_t fold_words(const U &v)
 // lane reads those of its units that start a 128-byte stretch of the row.
 // The other lanes (and all lanes when row == NULL) read `fallback`, an
 // address the workgroup reads anyway, so the load is not under a branch.
-// Returns the loaded words, to be passed to keep_loaded() after the
-// workgroup's stores, so the wave waits for them only at its end.
+// Returns the loaded words, to be passed to keep_loaded(): the wave waits
+// for them at its end.
 template <typename U, int VPT>
 __device__ __forceinline__ uint32_t prefetch_lines(const U *__restrict__ row, int64_t begin,
                                                    int64_t end, const U *__restrict__ fallback) {

@@ -82,8 +82,6 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
   U zero;
   zero = U{};
   int bad = 0;
-  constexpr bool kPrefetch = NTM != 0 && !SIDE;   // as in the top-k permute
-  uint32_t pf = 0;
   const int n = mask_count(mrow, E, &bad);
   for (int j0 = 0; j0 < n; j0 += kSlotChunk) {
     const int nj = min(kSlotChunk, n - j0);
@@ -98,14 +96,6 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
       }
       srow[threadIdx.x] = r;
       szero[threadIdx.x] = z;
-    }
-    // A streaming call also prefetches this slice of a later token's row
-    // (after the first slot loads, which wait in issue order).
-    if (kPrefetch && j0 == 0) {
-      const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
-      pf = prefetch_lines<U, VPT>((int64_t)t + ahead < T ? x + (int64_t)(t + ahead) * V
-                                                         : nullptr,
-                                  s0, min(V, s0 + (int64_t)blockDim.x * VPT), xr + s0);
     }
     __syncthreads();
     for (int j = 0; j < nj; j++) {
@@ -122,7 +112,14 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
     }
     __syncthreads();
   }
-  if (kPrefetch) keep_loaded(pf);
+  // A streaming call prefetches this slice of a later token's row after its
+  // stores, as the top-k permute does.
+  if constexpr (NTM != 0 && !SIDE) {
+    const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
+    keep_loaded(prefetch_lines<U, VPT>(
+        (int64_t)t + ahead < T ? x + (int64_t)(t + ahead) * V : nullptr, s0,
+        min(V, s0 + (int64_t)blockDim.x * VPT), xr + s0));
+  }
   if (blockIdx.y == 0) report(dev_status, bad);
 }
 

@@ -101,18 +101,6 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
     const int64_t r = srow[threadIdx.x];
     if (r >= 0 && out_probs != nullptr) out_probs[r] = probs[(int64_t)t * k + threadIdx.x];
   }
-  // A streaming call also prefetches this slice of a later token's row,
-  // after the slot loads (the vector memory counter retires in issue order,
-  // so a wait for an earlier load never waits for it).  Not with side rows:
-  // on the 16384 x 7168 FP8 permute (4-wave workgroups) it made the cold
-  // call slower, 213 us against 197 (199 at twice the distance).
-  constexpr bool kPrefetch = NTM != 0 && !SIDE;
-  uint32_t pf = 0;
-  if constexpr (kPrefetch) {
-    const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
-    pf = prefetch_lines<U, VPT>((int64_t)t + ahead < T ? x + (int64_t)(t + ahead) * V : nullptr,
-                                s0, min(V, s0 + (int64_t)blockDim.x * VPT), xr + s0);
-  }
   __syncthreads();
 
   for (int j = 0; j < k; j++) {
@@ -126,7 +114,20 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
     }
     if (SIDE && blockIdx.y == 0) store_side_row(side, sc, t, r);
   }
-  if (kPrefetch) keep_loaded(pf);
+  // A streaming call then prefetches this slice of a later token's row.
+  // Issued after the stores: before a loop of stores alone the compiler
+  // waits for every load in flight (gfx9 counts stores and loads on one
+  // counter), so an earlier prefetch held up this token's stores (cold
+  // 16384 x 7168 permute: 398 us with the prefetch before the stores, 385
+  // after them, 420 without).  Not with side rows: on the FP8 permute of
+  // that size (4-wave workgroups) it made the cold call slower, 213 us
+  // against 197 (199 at twice the distance).
+  if constexpr (NTM != 0 && !SIDE) {
+    const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
+    keep_loaded(prefetch_lines<U, VPT>(
+        (int64_t)t + ahead < T ? x + (int64_t)(t + ahead) * V : nullptr, s0,
+        min(V, s0 + (int64_t)blockDim.x * VPT), xr + s0));
+  }
 }
 
 // ---------------------------------------------------------------- combine --
