@@ -110,7 +110,11 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
       }
       if (SIDE && blockIdx.y == 0) store_side_row(side, sc, t, r);
     }
-    __syncthreads();
+    // Before the next chunk overwrites the slots in LDS.  Only then: a
+    // barrier after the last stores, which no later LDS access needs, holds
+    // every wave until the slowest has issued its stores (the 16384 x 7168
+    // top-8 mask permute took 415-420 us cold with it, 392-394 without).
+    if (j0 + kSlotChunk < n) __syncthreads();
   }
   // A streaming call prefetches this slice of a later token's row after its
   // stores, as the top-k permute does.
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kRowThreads) void mask_unpermute_kernel(
         }
       }
     }
-    __syncthreads();
+    if (j0 + kSlotChunk < n) __syncthreads();   // slots in LDS reused by the next chunk
   }
 
   U *orow = out + (int64_t)t * V;
@@ -317,7 +321,9 @@ __global__ __launch_bounds__(MAXT) void mask_unpermute_bwd_kernel(
         __syncthreads();
       }
     }
-    __syncthreads();
+    // slots in LDS reused by the next chunk; sdp was last written before the
+    // barrier that ends each batch with want_dot
+    if (j0 + kSlotChunk < n) __syncthreads();
   }
   if (want_dot)
     for (int e = threadIdx.x; e < E; e += blockDim.x)

@@ -446,7 +446,7 @@ __global__ __launch_bounds__(MAXT) void combine_bwd_kernel(
         for (int w = 0; w < nwaves; w++) s += sred[w][threadIdx.x];
         d_probs[(int64_t)t * k + j0 + threadIdx.x] = s;
       }
-      __syncthreads();
+      if (j0 + KB < k) __syncthreads();   // sred reused by the next batch
     }
   }
 }
