@@ -241,6 +241,14 @@ __global__ __launch_bounds__(MAXT) void mask_unpermute_bwd_kernel(
   const int nwaves = blockDim.x / kWave;
   const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
   const U *grow = d_out + (int64_t)t * V;
+  // First pass of the token's upstream gradient, issued before the slots are
+  // resolved (as in the top-k backward): its read overlaps the map reads.
+  U graw[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = cfirst + (int64_t)i * blockDim.x;
+    graw[i] = c < V ? ld_row<NT>(grow + c) : Unit::zero();
+  }
   const bool want_dot = d_merging_probs != nullptr;
   if (want_dot)
     for (int e = threadIdx.x; e < E; e += blockDim.x) sdp[e] = 0.0f;
@@ -263,11 +271,12 @@ __global__ __launch_bounds__(MAXT) void mask_unpermute_bwd_kernel(
 #pragma unroll
       for (int jj = 0; jj < kBatch; jj++) part[jj] = 0.0f;
       for (int64_t cb = cfirst; cb < V; cb += stride) {
-        U graw[VPT];
+        if (!(j0 == 0 && jb == 0 && cb == cfirst)) {
 #pragma unroll
-        for (int i = 0; i < VPT; i++) {
-          const int64_t c = cb + (int64_t)i * blockDim.x;
-          graw[i] = c < V ? ld_row<NT>(grow + c) : Unit::zero();
+          for (int i = 0; i < VPT; i++) {
+            const int64_t c = cb + (int64_t)i * blockDim.x;
+            graw[i] = c < V ? ld_row<NT>(grow + c) : Unit::zero();
+          }
         }
         U fin[kBatch][VPT];
         if (want_dot) {
