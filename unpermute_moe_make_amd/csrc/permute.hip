@@ -38,6 +38,11 @@ constexpr int kMaxTopk = MOE_MAX_TOPK;
 #ifndef MOE_COMBINE_BWD_STREAM
 #define MOE_COMBINE_BWD_STREAM 3
 #endif
+// Streaming unpermute backward with prob gradients as two launches (scatter,
+// then dot products) when the row fits one pass; 0 keeps the fused kernel.
+#ifndef MOE_BWD_SPLIT
+#define MOE_BWD_SPLIT 1
+#endif
 // Units per lane of the permute when a row fits one pass; build-time tuning.
 #ifndef MOE_PERMUTE_VPT
 #define MOE_PERMUTE_VPT 2
@@ -451,6 +456,199 @@ __global__ __launch_bounds__(MAXT) void combine_bwd_kernel(
   }
 }
 
+// ------------------------------------ unpermute backward in two launches --
+
+// When the row fits one workgroup pass, the backward of the weighted
+// unpermute runs as two kernels of the library's two access patterns: a
+// gather that only reads (the prob-gradient dot products) and a scatter that
+// reads one row per token and writes k (the activation gradient).  Fused, one
+// kernel interleaves 1.88 GB of gathers with 1.88 GB of scattered stores
+// (16384 x 7168 top-8), which the memory system serves more slowly than the
+// two streams one after the other.
+
+// d_probs[t][j] = <fwd_in[r_j], d_out[t]>: each lane runs an fmaf chain over
+// its units and their elements in order; the lanes of a wave are then summed
+// by a fixed DPP tree, and the waves in order.  All KB slots' loads are in
+// flight before the arithmetic, as in the unpermute.
+template <int VPT, int KB, int NTM, int MAXT>
+__global__ __launch_bounds__(MAXT) void dot_gather_kernel(
+    const v4u *__restrict__ d_out, const v4u *__restrict__ fwd_in,
+    const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
+    int64_t V, int k, int E, int n_rows, float *__restrict__ d_probs,
+    int32_t *__restrict__ dev_status) {
+  using Unit = Bf16Unit<8>;
+  __shared__ int64_t srow[kMaxTopk];
+  __shared__ float sred[MAXT / kWave][KB];
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+
+  // The token's upstream gradient, issued before the slots are resolved.
+  v4u g[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = (int64_t)threadIdx.x + (int64_t)i * blockDim.x;
+    g[i] = c < V ? ld_row<(NTM & 1) != 0>(d_out + (int64_t)t * V + c) : Unit::zero();
+  }
+  const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
+  if (threadIdx.x < k) report(dev_status, bad);
+  __syncthreads();
+
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    v4u vals[KB][VPT];
+#pragma unroll
+    for (int jj = 0; jj < KB; jj++) {
+      const int j = j0 + jj;
+      const int64_t r = (j < k) ? srow[j] : -1;
+#pragma unroll
+      for (int i = 0; i < VPT; i++) {
+        const int64_t c = (int64_t)threadIdx.x + (int64_t)i * blockDim.x;
+        vals[jj][i] = (r >= 0 && c < V) ? ld_row<(NTM & 1) != 0>(fwd_in + r * V + c)
+                                        : Unit::zero();
+      }
+    }
+    float part[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; jj++) {
+      part[jj] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VPT; i++) {
+        float f[8], gf[8];
+        Unit::unpack(vals[jj][i], f);
+        Unit::unpack(g[i], gf);
+#pragma unroll
+        for (int e = 0; e < 8; e++) part[jj] = __builtin_fmaf(f[e], gf[e], part[jj]);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < KB; jj++) {
+      const float sum = wave_sum(part[jj]);
+      if (lane == 0) sred[wv][jj] = sum;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < KB && j0 + (int)threadIdx.x < k) {
+      float sum = 0.0f;
+      for (int w = 0; w < nwaves; w++) sum += sred[w][threadIdx.x];
+      d_probs[(int64_t)t * k + j0 + threadIdx.x] = sum;
+    }
+    if (j0 + KB < k) __syncthreads();   // sred reused by the next batch
+  }
+}
+
+// d_in[r_j] = bf16(fp32(d_out[t]) * p_j): the permute's shape and source
+// prefetch, with one fp32 product and one rounding per element.
+template <int VPT, int NTM>
+__global__ __launch_bounds__(kRowThreads) void scale_scatter_kernel(
+    const v4u *__restrict__ d_out, const float *__restrict__ probs,
+    const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ row_id_map, int T,
+    int64_t V, int k, int E, int n_rows, v4u *__restrict__ d_in,
+    int32_t *__restrict__ dev_status, int ahead) {
+  using Unit = Bf16Unit<8>;
+  __shared__ int64_t srow[kMaxTopk];
+  __shared__ float sp[kMaxTopk];
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
+  const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
+  const v4u *grow = d_out + (int64_t)t * V;
+  v4u v[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = s0 + threadIdx.x + (int64_t)i * blockDim.x;
+    v[i] = c < V ? ld_row<(NTM & 1) != 0>(grow + c) : Unit::zero();
+  }
+  const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
+  if (threadIdx.x < k) {
+    sp[threadIdx.x] = probs[(int64_t)t * k + threadIdx.x];
+    if (blockIdx.y == 0) report(dev_status, bad);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < k; j++) {
+    const int64_t r = srow[j];
+    if (r < 0) continue;
+    const float p = sp[j];
+    v4u *orow = d_in + r * V;
+#pragma unroll
+    for (int i = 0; i < VPT; i++) {
+      const int64_t c = s0 + threadIdx.x + (int64_t)i * blockDim.x;
+      float f[8];
+      Unit::unpack(v[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; e++) f[e] = f[e] * p;   // one fp32 rounding
+      if (c < V) st_row<(NTM & 2) != 0>(Unit::pack(f), orow + c);
+    }
+  }
+  if constexpr (NTM != 0)   // as in the permute
+    keep_loaded(prefetch_lines<v4u, VPT>(
+        (int64_t)t + ahead < T ? d_out + (int64_t)(t + ahead) * V : nullptr, s0,
+        min(V, s0 + (int64_t)blockDim.x * VPT), grow + s0));
+}
+
+template <int VPT, int NTM, int MAXT = kRowThreads>
+void dot_gather_k(const RowShape &sh, int T, const void *d_out, const void *fwd_in,
+                  const int32_t *topk_idx, const int32_t *row_id_map, int64_t V, int k, int E,
+                  int n_rows, float *d_probs, int32_t *st, hipStream_t s) {
+  const dim3 grid = spill_grid(T, 1), block(sh.threads);
+  const v4u *gp = static_cast<const v4u *>(d_out);
+  const v4u *fp = static_cast<const v4u *>(fwd_in);
+#define MOE_DOT(KBV)                                                                           \
+  hipLaunchKernelGGL((dot_gather_kernel<VPT, KBV, NTM, MAXT>), grid, block, 0, s, gp, fp,     \
+                     topk_idx, row_id_map, T, V, k, E, n_rows, d_probs, st)
+  switch (k) {
+    case 1: MOE_DOT(1); break;
+    case 2: MOE_DOT(2); break;
+    case 3: MOE_DOT(3); break;
+    case 4: MOE_DOT(4); break;
+    case 5: MOE_DOT(5); break;
+    case 6: MOE_DOT(6); break;
+    case 7: MOE_DOT(7); break;
+    default: MOE_DOT(8); break;
+  }
+#undef MOE_DOT
+}
+
+template <int NTM>
+void scale_scatter_dispatch(const void *d_out, const float *probs, const int32_t *topk_idx,
+                            const int32_t *row_id_map, int T, int64_t V, int k, int E,
+                            int n_rows, void *d_in, int32_t *st, hipStream_t s) {
+  RowShape sh = row_shape_vpt(V, MOE_PERMUTE_VPT, kRowThreads);   // as the permute
+  if (sh.threads == 0) sh = row_shape(V, true);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
+  const v4u *gp = static_cast<const v4u *>(d_out);
+  v4u *dp = static_cast<v4u *>(d_in);
+#define MOE_SCATTER(VPTV)                                                                      \
+  hipLaunchKernelGGL((scale_scatter_kernel<VPTV, NTM>), grid, block, 0, s, gp, probs, topk_idx, \
+                     row_id_map, T, V, k, E, n_rows, dp, st, prefetch_ahead(sh.threads))
+  switch (sh.vpt) {
+    case 1: MOE_SCATTER(1); break;
+    case 2: MOE_SCATTER(2); break;
+    default: MOE_SCATTER(4); break;
+  }
+#undef MOE_SCATTER
+}
+
+// sh: one pass over the row (ysplit 1); more than kRowThreads lanes only
+// with one unit per lane.
+template <int NTM>
+void dot_gather_dispatch(const RowShape &sh, const void *d_out, const void *fwd_in,
+                         const int32_t *topk_idx, const int32_t *row_id_map, int T, int64_t V,
+                         int k, int E, int n_rows, float *d_probs, int32_t *st, hipStream_t s) {
+  if (sh.threads > kRowThreads) {
+    dot_gather_k<1, NTM, kBwdThreads>(sh, T, d_out, fwd_in, topk_idx, row_id_map, V, k, E, n_rows,
+                                      d_probs, st, s);
+    return;
+  }
+  switch (sh.vpt) {
+    case 1: dot_gather_k<1, NTM>(sh, T, d_out, fwd_in, topk_idx, row_id_map, V, k, E, n_rows, d_probs, st, s); break;
+    case 2: dot_gather_k<2, NTM>(sh, T, d_out, fwd_in, topk_idx, row_id_map, V, k, E, n_rows, d_probs, st, s); break;
+    default: dot_gather_k<4, NTM>(sh, T, d_out, fwd_in, topk_idx, row_id_map, V, k, E, n_rows, d_probs, st, s); break;
+  }
+}
+
 template <typename U, int NTM, bool SIDE>
 hipError_t permute_dispatch(const void *x, const float *probs, const int32_t *topk_idx,
                             const int32_t *row_id_map, int T, int64_t V, int k, int E,
@@ -650,6 +848,40 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
                               int k, int E, int n_rows, void *d_in, float *d_probs,
                               int32_t *dev_status, bool vec, hipStream_t s) {
   const int64_t bytes = 2ll * H * ((int64_t)n_rows * (d_probs ? 2 : 1) + T);
+  if (vec) {
+    const int64_t V = H / 8;
+    const bool stream_rows = 2ll * H * ((int64_t)n_rows + T) > kStreamBytes;
+    if (d_probs == nullptr) {
+      // The activation gradient alone is the scaled scatter (16384 x 7168
+      // top-8: 344 us warm and 385 cold, against 447 and 411 for the fused
+      // kernel without its dot products; 4096 x 2048 top-6: 19.9 / 21.5
+      // against 20.6 / 25.7).
+      if (stream_rows)
+        scale_scatter_dispatch<MOE_PERMUTE_STREAM>(d_out, probs, topk_idx, row_id_map, T, V, k, E,
+                                                   n_rows, d_in, dev_status, s);
+      else
+        scale_scatter_dispatch<0>(d_out, probs, topk_idx, row_id_map, T, V, k, E, n_rows, d_in,
+                                  dev_status, s);
+      return hipGetLastError();
+    }
+    // Streaming calls run as the scatter, then the dot products (one unit per
+    // lane on up to 1024 lanes): 685 us warm and 679 cold at 16384 x 7168
+    // top-8, against 722 and 707 fused (dot products first: 704 / 707; two
+    // or four units per lane: 691 / 681 and 704 / 694).  Smaller calls keep
+    // the fused kernel: 35.3 us against 39.3 split at 4096 x 2048 top-6,
+    // where the second launch and the second read of d_out cost more.
+    if (MOE_BWD_SPLIT && bytes > kStreamBytes) {
+      RowShape ds = row_shape_vpt(V, 1, kBwdThreads);
+      if (ds.threads == 0) ds = gather_shape(V);
+      if (ds.ysplit == 1) {
+        scale_scatter_dispatch<MOE_PERMUTE_STREAM>(d_out, probs, topk_idx, row_id_map, T, V, k, E,
+                                                   n_rows, d_in, dev_status, s);
+        dot_gather_dispatch<MOE_COMBINE_STREAM>(ds, d_out, fwd_in, topk_idx, row_id_map, T, V, k,
+                                                E, n_rows, d_probs, dev_status, s);
+        return hipGetLastError();
+      }
+    }
+  }
   if (vec && bytes > kStreamBytes)
     combine_bwd_dispatch<8, MOE_COMBINE_BWD_STREAM>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
                                   n_rows, d_in, d_probs, dev_status, s);
