@@ -137,6 +137,12 @@ FUSED_PAD_MAX_BYTES = 128 << 20
 ROWMAP_SINGLE_MAX_ENTRIES = 4096
 ROWMAP_SINGLE_MAX_EXPERTS = 512
 ROWMAP_FUSED_MAX_BLOCKS = 64
+# An unpermute backward with prob gradients that moves more than
+# STREAM_BYTES, on rows of whole 16-byte units that fit one workgroup pass
+# (at most BWD_SPLIT_MAX_UNITS units), runs as a scaled scatter and then a
+# dot-product gather.
+STREAM_BYTES = 256 << 20
+BWD_SPLIT_MAX_UNITS = 2048
 
 
 def op_kernels(op, cfg):
@@ -144,6 +150,11 @@ def op_kernels(op, cfg):
     if op == "sort_chunks_and_pad" and cfg.get("out_cap", 0) * cfg.get("H", 0) * 2 <= \
             FUSED_PAD_MAX_BYTES:
         return ["pad_fused_kernel"]
+    if op == "unpermute_bwd":
+        T, H, k = cfg.get("T", 0), cfg.get("H", 0), cfg.get("k", 0)
+        if H % 8 == 0 and H // 8 <= BWD_SPLIT_MAX_UNITS and \
+                2 * H * (2 * T * k + T) > STREAM_BYTES:
+            return ["scale_scatter_kernel", "dot_gather_kernel"]
     if op == "row_map":
         T, k, E = cfg.get("T", 0), cfg.get("k", 0), cfg.get("E", 0)
         if T * k <= ROWMAP_SINGLE_MAX_ENTRIES and E <= ROWMAP_SINGLE_MAX_EXPERTS:

@@ -23,6 +23,7 @@ namespace {
 #define MOE_MASK_PERMUTE_STREAM 2
 #endif
 
+
 constexpr int kSlotChunk = 64;   // slots resolved into LDS at a time
 constexpr int kBatch = 8;        // rows loaded together in the combine
 
@@ -453,6 +454,210 @@ void mask_unpermute_bwd_dispatch(const void *d_out, const void *fwd_in, const fl
 #undef MOE_MASK_BWD
 }
 
+// ------------------------------------ unpermute backward in two launches --
+
+// As the top-k backward: a streaming call with merging-prob gradients runs as
+// a scaled scatter and then a gather of dot products, one pattern per launch.
+
+// d_in[row] = bf16(fp32(d_out[t]) * merging_probs[t][e]) for each slot: the
+// mask permute's shape and source prefetch, one product per element.
+template <int VPT, int NTM>
+__global__ __launch_bounds__(kRowThreads) void mask_scale_scatter_kernel(
+    const v4u *__restrict__ d_out, const float *__restrict__ merging_probs,
+    const int32_t *__restrict__ map, int T, int64_t V, int E, int n_rows,
+    v4u *__restrict__ d_in, int32_t *__restrict__ dev_status, int ahead) {
+  using Unit = Bf16Unit<8>;
+  __shared__ int64_t srow[kSlotChunk];
+  __shared__ float sp[kSlotChunk];
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
+  const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
+  const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
+  const v4u *grow = d_out + (int64_t)t * V;
+  v4u v[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = s0 + threadIdx.x + (int64_t)i * blockDim.x;
+    v[i] = c < V ? ld_row<(NTM & 1) != 0>(grow + c) : Unit::zero();
+  }
+  int bad = 0;
+  const int n = mask_count(mrow, E, &bad);
+  for (int j0 = 0; j0 < n; j0 += kSlotChunk) {
+    const int nj = min(kSlotChunk, n - j0);
+    if ((int)threadIdx.x < nj) {
+      int e;
+      const int64_t r = mask_slot(mrow, E, n_rows, j0 + threadIdx.x, &e, &bad);
+      srow[threadIdx.x] = r;
+      sp[threadIdx.x] = r >= 0 ? merging_probs[(int64_t)t * E + e] : 0.0f;
+    }
+    __syncthreads();
+    for (int j = 0; j < nj; j++) {
+      const int64_t r = srow[j];
+      if (r < 0) continue;
+      const float p = sp[j];
+      v4u *orow = d_in + r * V;
+#pragma unroll
+      for (int i = 0; i < VPT; i++) {
+        const int64_t c = s0 + threadIdx.x + (int64_t)i * blockDim.x;
+        float f[8];
+        Unit::unpack(v[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; e++) f[e] = f[e] * p;   // one fp32 rounding
+        if (c < V) st_row<(NTM & 2) != 0>(Unit::pack(f), orow + c);
+      }
+    }
+    if (j0 + kSlotChunk < n) __syncthreads();   // slots in LDS reused by the next chunk
+  }
+  if constexpr (NTM != 0)   // as in the permute
+    keep_loaded(prefetch_lines<v4u, VPT>(
+        (int64_t)t + ahead < T ? d_out + (int64_t)(t + ahead) * V : nullptr, s0,
+        min(V, s0 + (int64_t)blockDim.x * VPT), grow + s0));
+  if (blockIdx.y == 0) report(dev_status, bad);
+}
+
+// d_merging_probs[t][e] = <fwd_in[row], d_out[t]> at the routed experts, 0
+// elsewhere: the dot products of the mask backward with nothing stored but
+// the prob row.  Per lane an fmaf chain over its units and their elements
+// in order, then a fixed wave tree and the waves in order.  The row is one
+// pass of the workgroup.
+template <int VPT, int NTM, int MAXT>
+__global__ __launch_bounds__(MAXT) void mask_dot_gather_kernel(
+    const v4u *__restrict__ d_out, const v4u *__restrict__ fwd_in,
+    const int32_t *__restrict__ map, int T, int64_t V, int E, int n_rows,
+    float *__restrict__ d_merging_probs, int32_t *__restrict__ dev_status) {
+  using Unit = Bf16Unit<8>;
+  __shared__ int64_t srow[kSlotChunk];
+  __shared__ int se[kSlotChunk];
+  __shared__ float sred[MAXT / kWave][kBatch];
+  __shared__ float sdp[MOE_MAX_EXPERTS];
+  const int64_t tb = spill_block();
+  if (tb >= T) return;  // a workgroup past the last token
+  const int t = (int)tb;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
+  v4u g[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; i++) {
+    const int64_t c = (int64_t)threadIdx.x + (int64_t)i * blockDim.x;
+    g[i] = c < V ? ld_row<(NTM & 1) != 0>(d_out + (int64_t)t * V + c) : Unit::zero();
+  }
+  // the first chunk's map entries read with the count, as in the fused kernel
+  int e_ahead = 0, r_ahead = 0;
+  if ((int)threadIdx.x < min(E, kSlotChunk)) {
+    e_ahead = mrow[E + threadIdx.x];
+    r_ahead = mrow[threadIdx.x];
+  }
+  int bad = 0;
+  const int n = mask_count(mrow, E, &bad);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) sdp[e] = 0.0f;
+  __syncthreads();
+
+  for (int j0 = 0; j0 < n; j0 += kSlotChunk) {
+    const int nj = min(kSlotChunk, n - j0);
+    if ((int)threadIdx.x < nj) {
+      int e;
+      int64_t r;
+      if (j0 == 0) {
+        e = e_ahead;
+        r = checked_slot(e, r_ahead, E, n_rows, &bad);
+      } else {
+        r = mask_slot(mrow, E, n_rows, j0 + threadIdx.x, &e, &bad);
+      }
+      srow[threadIdx.x] = r;
+      se[threadIdx.x] = r >= 0 ? e : -1;
+    }
+    __syncthreads();
+    for (int jb = 0; jb < nj; jb += kBatch) {
+      v4u vals[kBatch][VPT];
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) {
+        const int64_t r = jb + jj < nj ? srow[jb + jj] : -1;
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+          const int64_t c = (int64_t)threadIdx.x + (int64_t)i * blockDim.x;
+          vals[jj][i] = (r >= 0 && c < V) ? ld_row<(NTM & 1) != 0>(fwd_in + r * V + c)
+                                          : Unit::zero();
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+          float f[8], gf[8];
+          Unit::unpack(vals[jj][i], f);
+          Unit::unpack(g[i], gf);
+#pragma unroll
+          for (int e = 0; e < 8; e++) part = __builtin_fmaf(f[e], gf[e], part);
+        }
+        const float sum = wave_sum(part);
+        if (lane == 0) sred[wv][jj] = sum;
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < kBatch && jb + (int)threadIdx.x < nj) {
+        float sum = 0.0f;
+        for (int w = 0; w < nwaves; w++) sum += sred[w][threadIdx.x];
+        const int e = se[jb + threadIdx.x];
+        if (e >= 0) sdp[e] = sum;
+      }
+      // sred reused by the next batch; also ends this chunk's reads of the
+      // slots and orders the sdp writes before the row is written out
+      __syncthreads();
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    d_merging_probs[(int64_t)t * E + e] = sdp[e];
+  report(dev_status, bad);
+}
+
+template <int NTM>
+void mask_scale_scatter_dispatch(const void *d_out, const float *mp, const int32_t *map, int T,
+                                 int64_t V, int E, int n_rows, void *d_in, int32_t *st,
+                                 hipStream_t s) {
+  RowShape sh = row_shape_vpt(V, 2, kRowThreads);   // as the mask permute
+  if (sh.threads == 0) sh = row_shape(V, true);
+  const dim3 grid = spill_grid(T, sh.ysplit), block(sh.threads);
+  const v4u *gp = static_cast<const v4u *>(d_out);
+  v4u *dp = static_cast<v4u *>(d_in);
+#define MOE_MASK_SCATTER(VPTV)                                                                 \
+  hipLaunchKernelGGL((mask_scale_scatter_kernel<VPTV, NTM>), grid, block, 0, s, gp, mp, map, T, \
+                     V, E, n_rows, dp, st, prefetch_ahead(sh.threads))
+  switch (sh.vpt) {
+    case 1: MOE_MASK_SCATTER(1); break;
+    case 2: MOE_MASK_SCATTER(2); break;
+    default: MOE_MASK_SCATTER(4); break;
+  }
+#undef MOE_MASK_SCATTER
+}
+
+// sh: one pass over the row; more than kRowThreads lanes only with one unit
+// per lane.
+template <int NTM>
+void mask_dot_gather_dispatch(const RowShape &sh, const void *d_out, const void *fwd_in,
+                              const int32_t *map, int T, int64_t V, int E, int n_rows,
+                              float *dmp, int32_t *st, hipStream_t s) {
+  const dim3 grid = spill_grid(T, 1), block(sh.threads);
+  const v4u *gp = static_cast<const v4u *>(d_out);
+  const v4u *fp = static_cast<const v4u *>(fwd_in);
+  if (sh.threads > kRowThreads) {
+    hipLaunchKernelGGL((mask_dot_gather_kernel<1, NTM, 1024>), grid, block, 0, s, gp, fp, map, T,
+                       V, E, n_rows, dmp, st);
+    return;
+  }
+#define MOE_MASK_DOT(VPTV)                                                                     \
+  hipLaunchKernelGGL((mask_dot_gather_kernel<VPTV, NTM, kRowThreads>), grid, block, 0, s, gp, \
+                     fp, map, T, V, E, n_rows, dmp, st)
+  switch (sh.vpt) {
+    case 1: MOE_MASK_DOT(1); break;
+    case 2: MOE_MASK_DOT(2); break;
+    default: MOE_MASK_DOT(4); break;
+  }
+#undef MOE_MASK_DOT
+}
+
 }  // namespace
 
 hipError_t launch_mask_permute(const void *x, const float *probs, const int32_t *map, int T,
@@ -522,6 +727,35 @@ hipError_t launch_mask_unpermute_bwd(const void *d_out, const void *fwd_in,
                                      hipStream_t s) {
   const bool stream =
       2ll * H * ((int64_t)n_rows * (d_merging_probs ? 2 : 1) + T) > kStreamBytes;
+  if (vec) {
+    // As the top-k backward: the activation gradient alone is the scaled
+    // scatter (16384 x 7168 top-8: 363 us warm and 392 cold against 446 and
+    // 448 fused; 4096 x 2048 top-6: 19.9 / 22.6 against 20.3 / 25.4); a
+    // streaming call with prob gradients is the scatter, then the dot
+    // products (720 / 717 against 725 / 729 fused).
+    const int64_t V = H / 8;
+    const bool stream_rows = 2ll * H * ((int64_t)n_rows + T) > kStreamBytes;
+    if (d_merging_probs == nullptr) {
+      if (stream_rows)
+        mask_scale_scatter_dispatch<MOE_MASK_PERMUTE_STREAM>(d_out, merging_probs, map, T, V, E,
+                                                             n_rows, d_in, dev_status, s);
+      else
+        mask_scale_scatter_dispatch<0>(d_out, merging_probs, map, T, V, E, n_rows, d_in,
+                                       dev_status, s);
+      return hipGetLastError();
+    }
+    if (MOE_BWD_SPLIT && stream && d_merging_probs != nullptr) {
+      RowShape ds = row_shape_vpt(V, 1, 1024);
+      if (ds.threads == 0) ds = gather_shape(V);
+      if (ds.ysplit == 1) {
+        mask_scale_scatter_dispatch<MOE_MASK_PERMUTE_STREAM>(d_out, merging_probs, map, T, V, E,
+                                                             n_rows, d_in, dev_status, s);
+        mask_dot_gather_dispatch<1>(ds, d_out, fwd_in, map, T, V, E, n_rows, d_merging_probs,
+                                    dev_status, s);
+        return hipGetLastError();
+      }
+    }
+  }
   if (vec && stream)
     mask_unpermute_bwd_dispatch<8, true>(d_out, fwd_in, merging_probs, map, T, H / 8, E, n_rows,
                                          d_in, d_merging_probs, dev_status, s);

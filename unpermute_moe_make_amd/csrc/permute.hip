@@ -38,11 +38,6 @@ constexpr int kMaxTopk = MOE_MAX_TOPK;
 #ifndef MOE_COMBINE_BWD_STREAM
 #define MOE_COMBINE_BWD_STREAM 3
 #endif
-// Streaming unpermute backward with prob gradients as two launches (scatter,
-// then dot products) when the row fits one pass; 0 keeps the fused kernel.
-#ifndef MOE_BWD_SPLIT
-#define MOE_BWD_SPLIT 1
-#endif
 // Units per lane of the permute when a row fits one pass; build-time tuning.
 #ifndef MOE_PERMUTE_VPT
 #define MOE_PERMUTE_VPT 2
@@ -125,8 +120,8 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
   // counter), so an earlier prefetch held up this token's stores (cold
   // 16384 x 7168 permute: 398 us with the prefetch before the stores, 385
   // after them, 420 without).  Not with side rows: on the FP8 permute of
-  // that size (4-wave workgroups) it made the cold call slower, 213 us
-  // against 197 (199 at twice the distance).
+  // that size (4-wave workgroups) it made the cold call slower, 207 us
+  // against 196 (issued before the stores: 213 against 197).
   if constexpr (NTM != 0 && !SIDE) {
     const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
     keep_loaded(prefetch_lines<U, VPT>(

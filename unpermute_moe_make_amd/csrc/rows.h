@@ -14,6 +14,12 @@
 #ifndef MOE_GATHER_VPT
 #define MOE_GATHER_VPT 2
 #endif
+// Streaming unpermute backwards with prob gradients (top-k and mask-map
+// forms) as two launches, a scaled scatter and then the dot products, when
+// the row fits one workgroup pass; 0 keeps the fused kernels.
+#ifndef MOE_BWD_SPLIT
+#define MOE_BWD_SPLIT 1
+#endif
 
 namespace moe {
 
