@@ -157,19 +157,6 @@ SMALL = [(37, 7, 9, 0.4), (64, 64, 16, 0.5), (40, 136, 160, 0.6), (9, 20480, 8, 
          (50, 24, 6, 0.0), (33, 72, 2048, 0.02)]
 
 
-def _sub_map(ref_map, E, sample):
-    """The sampled tokens' map rows with their rows renumbered 0.. in order,
-    and the original rows in that order (for gathering inputs)."""
-    sub = ref_map[sample].copy()
-    rows = []
-    for i in range(len(sample)):
-        n = sub[i, 2 * E]
-        for j in range(n):
-            rows.append(sub[i, j])
-            sub[i, j] = len(rows) - 1
-    return sub, np.array(rows, np.int64)
-
-
 @pytest.mark.parametrize("case", ["finegrain", "skewed"] + SMALL)
 @pytest.mark.parametrize("with_probs", [True, False])
 def test_mask_permute(m, case, with_probs):
@@ -177,7 +164,7 @@ def test_mask_permute(m, case, with_probs):
     T, H = x.shape
     E = mask.shape[1]
     say(f"mask permute {case if isinstance(case, str) else (T, H, E)} probs={with_probs}")
-    if with_probs and not isinstance(case, str):
+    if with_probs:
         probs[::5] = 0.0          # padded slots: zero rows
     ref_map, _ = oracle.mask_row_id_map(oracle_mask(mask))
     R = int(mask.sum())
@@ -198,11 +185,20 @@ def test_mask_permute(m, case, with_probs):
                                           ref_p[:R].view(np.uint32))
     else:
         # full check by a gather on the GPU: row map entries -> source token
+        # and expert; a zero prob gives a zero row
         src = np.full(R, -1, np.int64)
+        exp_e = np.full(R, -1, np.int64)
         for lo in range(E):
             used = ref_map[:, 2 * E] > lo
             src[ref_map[used, lo]] = np.nonzero(used)[0]
+            exp_e[ref_map[used, lo]] = ref_map[used, E + lo]
+        assert np.all(src >= 0)
         exp = x.to(DEV)[torch.from_numpy(src).to(DEV)]
+        if with_probs:
+            p_row = probs.numpy()[src, exp_e]
+            exp[torch.from_numpy(p_row == 0.0).to(DEV)] = 0
+            np.testing.assert_array_equal(out_p.cpu().numpy()[:R].view(np.uint32),
+                                          p_row.view(np.uint32))
         assert torch.equal(out[:R].view(torch.int16), exp.view(torch.int16))
 
 
@@ -222,34 +218,34 @@ def test_mask_unpermute(m, case, merge, scatter):
     out = sentinel_bf16((T, H))
     y, up = m.moe_unpermute_mask(P, rm, probs.to(DEV) if merge else None,
                                  pp.to(DEV) if scatter else None, out=out)
-    if T * H <= (1 << 24):
-        ref, ref_up = oracle.mask_unpermute(bits(P), probs.numpy() if merge else None, ref_map,
-                                            pp.numpy() if scatter else None)
-        np.testing.assert_array_equal(bits(y), ref)
-        if scatter:
-            np.testing.assert_array_equal(up.cpu().numpy().view(np.uint32),
-                                          ref_up.view(np.uint32))
-    else:
-        sample = np.sort(np.random.default_rng(6).choice(T, 256, replace=False))
-        sub, rows = _sub_map(ref_map, E, sample)
-        Pr = bits(P[torch.from_numpy(rows).to(DEV)])
-        ref, ref_up = oracle.mask_unpermute(Pr, probs.numpy()[sample] if merge else None, sub,
-                                            pp.numpy()[rows] if scatter else None)
-        np.testing.assert_array_equal(bits(y)[sample], ref)
-        if scatter:
-            np.testing.assert_array_equal(up.cpu().numpy()[sample].view(np.uint32),
-                                          ref_up.view(np.uint32))
+    ref, ref_up = oracle.mask_unpermute(bits(P), probs.numpy() if merge else None, ref_map,
+                                        pp.numpy() if scatter else None)
+    np.testing.assert_array_equal(bits(y), ref)
+    if scatter:
+        np.testing.assert_array_equal(up.cpu().numpy().view(np.uint32), ref_up.view(np.uint32))
 
 
-def _dot_ok(got, fwd_rows, dy, ref_map, E, ref, sample=None):
+def _f64(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _dot_ok(got, fwd_bits, dy_bits, ref_map, E, ref, chunk=1024):
+    """|got - ref| <= 1e-5 * sum_h |a*b| at every routed (token, expert);
+    fwd_bits [rows][H] and dy_bits [T][H] bf16 bits, a chunk of tokens at a
+    time."""
     T = ref_map.shape[0]
-    toks = range(T) if sample is None else range(len(sample))
-    for i in toks:
-        n = ref_map[i, 2 * E]
-        for j in range(n):
-            r, e = ref_map[i, j], ref_map[i, E + j]
-            S = float(np.sum(np.abs(fwd_rows[r].astype(np.float64) * dy[i].astype(np.float64))))
-            assert abs(float(got[i, e]) - float(ref[i, e])) <= 1e-5 * S + 1e-37, (i, e)
+    n = ref_map[:, 2 * E]
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        b = np.abs(_f64(dy_bits[t0:t1]))
+        for j in range(int(n[t0:t1].max(initial=0))):
+            toks = np.nonzero(n[t0:t1] > j)[0]
+            r = ref_map[t0 + toks, j]
+            e = ref_map[t0 + toks, E + j]
+            scale = np.einsum("uh,uh->u", np.abs(_f64(fwd_bits[r])), b[toks])
+            err = np.abs(got[t0 + toks, e].astype(np.float64) -
+                         ref[t0 + toks, e].astype(np.float64))
+            assert np.all(err <= 1e-5 * scale + 1e-37), (t0, j)
 
 
 @pytest.mark.parametrize("case", ["finegrain", "skewed"] + SMALL)
@@ -269,29 +265,51 @@ def test_mask_unpermute_bwd(m, case, want_dot):
     db = bits(d_in)
     assert np.all(db[R:] == S_BF16)
     fv = workloads.bf16_bits(fin.cpu())
-    fvals = (fv.astype(np.uint32) << 16).view(np.float32)
-    dyv = (bits(dy).astype(np.uint32) << 16).view(np.float32)
-    if T * H <= (1 << 24):
-        ref_din, ref_dmp = oracle.mask_unpermute_bwd(bits(dy), fv, probs.numpy(), ref_map,
-                                                     d_in=db.copy())
-        np.testing.assert_array_equal(db, ref_din)
-        if want_dot:
-            got = dmp.cpu().numpy()
-            sel = np.zeros((T, E), bool)
-            for lo in range(E):
-                used = ref_map[:, 2 * E] > lo
-                sel[np.nonzero(used)[0], ref_map[used, E + lo]] = True
-            assert np.all(got[~sel].view(np.uint32) == 0)
-            _dot_ok(got, fvals, dyv, ref_map, E, ref_dmp)
-    else:
-        sample = np.sort(np.random.default_rng(7).choice(T, 192, replace=False))
-        sub, rows = _sub_map(ref_map, E, sample)
-        ref_din, ref_dmp = oracle.mask_unpermute_bwd(bits(dy)[sample], fv[rows],
-                                                     probs.numpy()[sample], sub)
-        np.testing.assert_array_equal(db[rows], ref_din)
-        if want_dot:
-            got = dmp.cpu().numpy()[sample]
-            _dot_ok(got, fvals[rows], dyv[sample], sub, E, ref_dmp, sample)
+    dyb = bits(dy)
+    ref_din, ref_dmp = oracle.mask_unpermute_bwd(dyb, fv, probs.numpy(), ref_map,
+                                                 d_in=db.copy())
+    np.testing.assert_array_equal(db, ref_din)
+    del ref_din
+    if want_dot:
+        got = dmp.cpu().numpy()
+        sel = np.zeros((T, E), bool)
+        for lo in range(E):
+            used = ref_map[:, 2 * E] > lo
+            sel[np.nonzero(used)[0], ref_map[used, E + lo]] = True
+        assert np.all(got[~sel].view(np.uint32) == 0)
+        _dot_ok(got, fv, dyb, ref_map, E, ref_dmp)
+
+
+@pytest.mark.parametrize("T,H,E,density", [(4096, 4096, 64, 0.25), (2048, 4104, 256, 0.3)])
+def test_mask_unpermute_bwd_streaming_shapes(m, T, H, E, density):
+    """Calls past the streaming threshold, in full: the two-launch backward
+    with many slots per token (several batches of dot products; more than 64
+    slots, two chunks, at 256 experts; rows of 513 16-byte units), and the
+    scatter alone without merging-prob gradients."""
+    x, mask, probs, dy = _case((T, H, E, density), seed=E)
+    say(f"mask unpermute bwd streaming {(T, H, E, density)}")
+    ref_map, _ = oracle.mask_row_id_map(oracle_mask(mask))
+    R = int(mask.sum())
+    rm = torch.from_numpy(ref_map).to(DEV)
+    fin = workloads.random_rows(R, H, seed=43, device=DEV)
+    d_in = sentinel_bf16((R, H))
+    d_in, dmp = m.moe_unpermute_mask_bwd(dy.to(DEV), fin, probs.to(DEV), rm, d_in=d_in)
+    fv = workloads.bf16_bits(fin.cpu())
+    dyb = bits(dy)
+    ref_din, ref_dmp = oracle.mask_unpermute_bwd(dyb, fv, probs.numpy(), ref_map)
+    np.testing.assert_array_equal(bits(d_in), ref_din)
+    got = dmp.cpu().numpy()
+    sel = np.zeros((T, E), bool)
+    for lo in range(E):
+        used = ref_map[:, 2 * E] > lo
+        sel[np.nonzero(used)[0], ref_map[used, E + lo]] = True
+    assert np.all(got[~sel].view(np.uint32) == 0)
+    _dot_ok(got, fv, dyb, ref_map, E, ref_dmp)
+    d_in1 = sentinel_bf16((R, H))
+    d_in1, none = m.moe_unpermute_mask_bwd(dy.to(DEV), fin, probs.to(DEV), rm, d_in=d_in1,
+                                           want_probs_grad=False)
+    assert none is None
+    np.testing.assert_array_equal(bits(d_in1), ref_din)
 
 
 def test_mask_roundtrip_identity_one_expert(m):

@@ -368,6 +368,37 @@ def test_unpermute_bwd_configs(m, name):
     assert torch.equal(d_in0.view(torch.int16), exp.view(torch.int16))
 
 
+@pytest.mark.parametrize("T,H,E,k", [(4096, 4096, 64, 16), (4096, 7176, 32, 8),
+                                     (2048, 20480, 16, 4)])
+def test_unpermute_bwd_streaming_shapes(m, T, H, E, k):
+    """Calls past the streaming threshold, in full: the two-launch backward
+    with 16 slots (two batches of dot products) and with rows of 897 16-byte
+    units, the fused kernel for rows longer than one workgroup pass, and the
+    scatter alone when no prob gradient is asked for (row slices at 20480)."""
+    say(f"unpermute_bwd streaming T={T} H={H} E={E} k={k}")
+    w = workloads.random_routed(T, H, E, k, seed=H + 3 * k)
+    ref_map, _ = oracle.row_id_map(w.topk_idx.numpy(), E)
+    _, idx, probs, dy = to_dev(w)
+    rm = torch.from_numpy(ref_map).to(DEV)
+    fwd_in = workloads.random_rows(T * k, H, seed=H + 5, device=DEV)
+    d_in = sentinel_bf16((T * k, H))
+    d_p = sentinel_f32((T, k))
+    m.moe_unpermute_bwd(dy, idx, rm, probs, fwd_in, d_in=d_in, d_probs=d_p)
+    dy_rows = workloads.bf16_bits(w.dy)
+    ref_in, ref_p = oracle.unpermute_bwd(dy_rows, bits(fwd_in), w.probs.numpy(),
+                                         w.topk_idx.numpy(), ref_map)
+    assert_bits_equal(bits(d_in), ref_in, "unpermute_bwd act grad")
+    r_all = oracle_rows(w.topk_idx.numpy(), ref_map)
+    fin_rows = bits(fwd_in[torch.from_numpy(r_all.flatten().astype(np.int64)).to(DEV)])
+    worst = dprob_ok(d_p.cpu().numpy(), fin_rows.reshape(T, k, H), dy_rows, ref_p)
+    say(f"  prob-grad worst error / scale = {worst:.3g}")
+    del fin_rows
+    d_in1 = sentinel_bf16((T * k, H))
+    _, none = m.moe_unpermute_bwd(dy, idx, rm, probs, fwd_in, probs_grad=False, d_in=d_in1)
+    assert none is None
+    assert_bits_equal(bits(d_in1), ref_in, "unpermute_bwd act grad without prob grads")
+
+
 @pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
 def test_permute_bwd_configs(m, name):
     w, ref_map, _ = routed(name)
