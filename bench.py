@@ -17,7 +17,9 @@ current stream.
 
 Also printed in the same JSON line, all timed with HIP events on that stream:
   per_op          every op of the whole routed path (row map, permute,
-                  unpermute, unpermute backward, permute backward), warm;
+                  unpermute, unpermute backward, permute backward), warm:
+                  each op called back to back, so its inputs are as its
+                  own previous call left them;
   per_op_cold     the same ops, each after a 512 MiB read of an unrelated
                   buffer (nothing of the op's inputs left in the Infinity
                   Cache);
@@ -71,6 +73,9 @@ def parse():
                     help="with a routed workload, skip the 32768-token chunk roundtrip block")
     ap.add_argument("--no-extra", dest="extra", action="store_false",
                     help="skip the library's further operations")
+    ap.add_argument("--no-full-step", dest="full_step", action="store_false",
+                    help="skip timing the whole routed path (so a kernel trace of the warm "
+                         "calls holds the roundtrip's calls and the per-op calls only)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB three times "
                          "(a known-size reference for hardware byte counters)")
@@ -421,11 +426,11 @@ class Timer:
         self._flush.sum()
 
     def per_op(self, names, reps, cold=False):
-        """Every op of `names` in order, reps times, events around each op
-        (cold: a flush before each op, outside its events)."""
+        """Each op of `names` reps times back to back, events around each
+        call (cold: a flush before each call, outside its events)."""
         evs = [{n: (self.hev.create(), self.hev.create()) for n in names} for _ in range(reps)]
-        for i in range(reps):
-            for n in names:
+        for n in names:
+            for i in range(reps):
                 if cold:
                     self.flush()
                 self.ops.run([n], self.s, evs[i], self.hev)
@@ -668,7 +673,7 @@ def main():
                      "achieved_cold": round(nbytes[dom] / (cu * 1e-6) / 1e9, 1),
                      "frac_cold": round(nbytes[dom] / (cu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     result["roofline"] = roof
-    if routed:
+    if routed and args.full_step:
         fms, _ = tm.wall(path_ops, K)
         fb = sum(nbytes[n] for n in path_ops)
         result["full_step"] = {"ops": "+".join(path_ops), "bytes": fb, "ms": round(fms, 4),
