@@ -457,7 +457,7 @@ void mask_unpermute_bwd_dispatch(const void *d_out, const void *fwd_in, const fl
 // ------------------------------------ unpermute backward in two launches --
 
 // As the top-k backward: a streaming call with merging-prob gradients runs as
-// a scaled scatter and then a gather of dot products, one pattern per launch.
+// a gather of dot products and then a scaled scatter, one pattern per launch.
 
 // d_in[row] = bf16(fp32(d_out[t]) * merging_probs[t][e]) for each slot: the
 // mask permute's shape and source prefetch, one product per element.
@@ -538,11 +538,12 @@ __global__ __launch_bounds__(MAXT) void mask_dot_gather_kernel(
   const int wv = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
   const int32_t *mrow = map + (int64_t)t * (2 * (int64_t)E + 1);
+  // plain loads of the upstream gradient: the scatter launched next reads it
   v4u g[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = (int64_t)threadIdx.x + (int64_t)i * blockDim.x;
-    g[i] = c < V ? ld_row<(NTM & 1) != 0>(d_out + (int64_t)t * V + c) : Unit::zero();
+    g[i] = c < V ? d_out[(int64_t)t * V + c] : Unit::zero();
   }
   // the first chunk's map entries read with the count, as in the fused kernel
   int e_ahead = 0, r_ahead = 0;
@@ -731,8 +732,8 @@ hipError_t launch_mask_unpermute_bwd(const void *d_out, const void *fwd_in,
     // As the top-k backward: the activation gradient alone is the scaled
     // scatter (16384 x 7168 top-8: 363 us warm and 392 cold against 446 and
     // 448 fused; 4096 x 2048 top-6: 19.9 / 22.6 against 20.3 / 25.4); a
-    // streaming call with prob gradients is the scatter, then the dot
-    // products (720 / 717 against 725 / 729 fused).
+    // streaming call with prob gradients is the dot products, then the
+    // scatter.
     const int64_t V = H / 8;
     const bool stream_rows = 2ll * H * ((int64_t)n_rows + T) > kStreamBytes;
     if (d_merging_probs == nullptr) {
@@ -748,10 +749,10 @@ hipError_t launch_mask_unpermute_bwd(const void *d_out, const void *fwd_in,
       RowShape ds = row_shape_vpt(V, 1, 1024);
       if (ds.threads == 0) ds = gather_shape(V);
       if (ds.ysplit == 1) {
-        mask_scale_scatter_dispatch<MOE_MASK_PERMUTE_STREAM>(d_out, merging_probs, map, T, V, E,
-                                                             n_rows, d_in, dev_status, s);
         mask_dot_gather_dispatch<1>(ds, d_out, fwd_in, map, T, V, E, n_rows, d_merging_probs,
                                     dev_status, s);
+        mask_scale_scatter_dispatch<MOE_MASK_PERMUTE_STREAM>(d_out, merging_probs, map, T, V, E,
+                                                             n_rows, d_in, dev_status, s);
         return hipGetLastError();
       }
     }

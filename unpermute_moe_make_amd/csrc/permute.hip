@@ -455,8 +455,8 @@ __global__ __launch_bounds__(MAXT) void combine_bwd_kernel(
 
 // When the row fits one workgroup pass, the backward of the weighted
 // unpermute runs as two kernels of the library's two access patterns: a
-// gather that only reads (the prob-gradient dot products) and a scatter that
-// reads one row per token and writes k (the activation gradient).  Fused, one
+// gather that only reads (the prob-gradient dot products), then a scatter
+// that reads one row per token and writes k (the activation gradient).  Fused, one
 // kernel interleaves 1.88 GB of gathers with 1.88 GB of scattered stores
 // (16384 x 7168 top-8), which the memory system serves more slowly than the
 // two streams one after the other.
@@ -481,12 +481,13 @@ __global__ __launch_bounds__(MAXT) void dot_gather_kernel(
   const int wv = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
 
-  // The token's upstream gradient, issued before the slots are resolved.
+  // The token's upstream gradient, issued before the slots are resolved;
+  // always a plain load, so the scatter launched next finds it cached.
   v4u g[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; i++) {
     const int64_t c = (int64_t)threadIdx.x + (int64_t)i * blockDim.x;
-    g[i] = c < V ? ld_row<(NTM & 1) != 0>(d_out + (int64_t)t * V + c) : Unit::zero();
+    g[i] = c < V ? d_out[(int64_t)t * V + c] : Unit::zero();
   }
   const int bad = resolve_slots(topk_idx, row_id_map, t, T, k, E, n_rows, srow);
   if (threadIdx.x < k) report(dev_status, bad);
@@ -859,20 +860,23 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
                                   dev_status, s);
       return hipGetLastError();
     }
-    // Streaming calls run as the scatter, then the dot products (one unit per
-    // lane on up to 1024 lanes): 685 us warm and 679 cold at 16384 x 7168
-    // top-8, against 722 and 707 fused (dot products first: 704 / 707; two
-    // or four units per lane: 691 / 681 and 704 / 694).  Smaller calls keep
-    // the fused kernel: 35.3 us against 39.3 split at 4096 x 2048 top-6,
-    // where the second launch and the second read of d_out cost more.
+    // Streaming calls run as the dot products (one unit per lane on up to
+    // 1024 lanes, d_out read with plain loads and the forward rows streamed),
+    // then the scatter, which finds d_out in the Infinity Cache: 636-639 us
+    // warm and 654-657 cold at 16384 x 7168 top-8, against 722 and 707
+    // fused.  Scatter first: 684-688 / 677 (635-639 / 676 with the dot
+    // kernel's plain d_out loads); two or four units per lane in the dot
+    // kernel were slower.  Smaller calls keep the fused kernel: 35.3 us
+    // against 39.3 split at 4096 x 2048 top-6, where the second launch and
+    // the second read of d_out cost more.
     if (MOE_BWD_SPLIT && bytes > kStreamBytes) {
       RowShape ds = row_shape_vpt(V, 1, kBwdThreads);
       if (ds.threads == 0) ds = gather_shape(V);
       if (ds.ysplit == 1) {
-        scale_scatter_dispatch<MOE_PERMUTE_STREAM>(d_out, probs, topk_idx, row_id_map, T, V, k, E,
-                                                   n_rows, d_in, dev_status, s);
         dot_gather_dispatch<MOE_COMBINE_STREAM>(ds, d_out, fwd_in, topk_idx, row_id_map, T, V, k,
                                                 E, n_rows, d_probs, dev_status, s);
+        scale_scatter_dispatch<MOE_PERMUTE_STREAM>(d_out, probs, topk_idx, row_id_map, T, V, k, E,
+                                                   n_rows, d_in, dev_status, s);
         return hipGetLastError();
       }
     }
