@@ -88,6 +88,9 @@ def test_permute_scaled_configs(m, name, sdt):
         exp_s = torch.empty_like(out_s)
         exp_s.view(torch.uint8)[rows] = sc.to(DEV).view(torch.uint8)[src]
         assert torch.equal(out_s.view(torch.uint8), exp_s.view(torch.uint8))
+        exp_p = torch.empty_like(out_p)
+        exp_p[rows] = w.probs.to(DEV).reshape(-1)
+        assert torch.equal(out_p.view(torch.int32), exp_p.view(torch.int32))
     # what a consumer sees: dequantized permuted rows are the source rows
     rows = rm_ref[w.topk_idx.numpy().astype(np.int64), np.arange(T)[:, None]].ravel()
     sample = np.random.default_rng(1).choice(T * k, min(T * k, 512), replace=False)
