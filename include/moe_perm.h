@@ -227,8 +227,9 @@ MOE_PERM_API int moe_unpermute_ep(const void *in, const float *probs, const int3
  *                                                            then bf16 RNE)
  *   d_probs[t][j]   = sum_h fp32(fwd_in[r(t,j)][h]) * fp32(d_out[t][h])
  * The order of the prob-grad sum is not fixed by the pages; here it is an
- * fp32 blocked tree that depends only on hidden and the launch shape chosen
- * for it, so results are bitwise reproducible.
+ * fp32 blocked tree that depends only on the call's sizes (through the
+ * launch shape chosen for them: a call moving more than 256 MiB computes the
+ * sums in a launch of their own), so results are bitwise reproducible.
  * With probs == NULL, d_in[r(t,j)] = d_out[t] bitwise and d_probs must be
  * NULL.  fwd_in may be NULL only when d_probs is NULL.
  *
