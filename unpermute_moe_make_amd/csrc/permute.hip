@@ -120,8 +120,9 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
   // counter), so an earlier prefetch held up this token's stores (cold
   // 16384 x 7168 permute: 398 us with the prefetch before the stores, 385
   // after them, 420 without).  Not with side rows: on the FP8 permute of
-  // that size (4-wave workgroups) it made the cold call slower, 207 us
-  // against 196 (issued before the stores: 213 against 197).
+  // that size (4-wave workgroups) it made the cold call slower at every
+  // distance, 201-211 us from 1024 to 8192 tokens ahead against 195
+  // (issued before the stores: 213 against 197).
   if constexpr (NTM != 0 && !SIDE) {
     const int64_t s0 = (int64_t)blockIdx.y * blockDim.x * VPT;
     keep_loaded(prefetch_lines<U, VPT>(
