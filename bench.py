@@ -169,14 +169,41 @@ def op_kernels(op, cfg):
     return OP_KERNELS[op]
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with whitespace runs folded, so
+    that a comment edit does not count as a kernel change.  String and
+    character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources, to tell whether stored counters still apply."""
+    """sha256 over the HIP sources' code (comments and layout left out), to
+    tell whether stored counters still apply."""
     import hashlib
     d = os.path.join(ROOT, "unpermute_moe_make_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(d, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -63,11 +63,12 @@ constexpr int64_t kStreamBytes = (int64_t)MOE_STREAM_MIB << 20;
 // under the round-robin dispatch over the 8 XCDs both workgroups run on the
 // same XCD.  Measured on the 16384 x 7168 bf16 permute (7-wave workgroups,
 // 2048 tokens ahead) with cold caches: 385 us against 420 (issued after the
-// workgroup's stores), the same warm time; 1024 to 4096 ahead within 2%.  At one round ahead (FP8 rows of the
-// same size, 4-wave workgroups, 2048 ahead) it was slower: 228 us against
-// 198.  The lanes that issue the reads matter as well: the lanes whose own
-// units start a line (8 per wave, in every wave) give the gain, while one
-// read per lane on lanes 0..111 (64 lines per instruction) gave none.
+// workgroup's stores), the same warm time; 1024 to 4096 ahead within 1%.
+// The FP8 rows of the same size (4-wave workgroups) were slower with it at
+// every distance, so the scaled permute goes without.  The lanes that issue
+// the reads matter as well: the lanes whose own units start a line (8 per
+// wave, in every wave) give the gain, while one read per lane on lanes
+// 0..111 (64 lines per instruction) gave none.
 constexpr int kNumCUs = 256;
 constexpr int kWaveSlotsPerCU = 32;
 inline int prefetch_ahead(int threads) {

@@ -15,7 +15,7 @@
 #define MOE_GATHER_VPT 2
 #endif
 // Streaming unpermute backwards with prob gradients (top-k and mask-map
-// forms) as two launches, a scaled scatter and then the dot products, when
+// forms) as two launches, the dot products and then a scaled scatter, when
 // the row fits one workgroup pass; 0 keeps the fused kernels.
 #ifndef MOE_BWD_SPLIT
 #define MOE_BWD_SPLIT 1
