@@ -347,6 +347,91 @@ def test_mask_chain_on_gpu_with_dropping(m):
     np.testing.assert_array_equal(up.cpu().numpy().view(np.uint32), ref_up.view(np.uint32))
 
 
+@pytest.mark.parametrize("T,H,E,density", [(64, 64, 16, 0.5), (4096, 4096, 64, 0.25)])
+def test_mask_bad_map_row_ops(m, T, H, E, density):
+    """Map faults only the device sees, at a small and a streaming size (the
+    two-launch backward): an expert out of range in one token's slot, a row
+    past the rows in another's, a slot count past E in a third (the whole
+    token is skipped).  Each op reports both status bits, leaves the faulty
+    slots' rows unwritten and matches the oracle (on the sound map) on every
+    other row and token."""
+    say(f"mask bad map row ops {(T, H, E, density)}")
+    x, mask, probs, dy = _case((T, H, E, density), seed=E + 5)
+    ref_map, _ = oracle.mask_row_id_map(oracle_mask(mask))
+    R = int(mask.sum())
+    n = ref_map[:, 2 * E]
+    cand = np.nonzero(n >= 2)[0]
+    a, b, c = int(cand[0]), int(cand[len(cand) // 2]), int(cand[-1])
+    bad = ref_map.copy()
+    bad[a, E] = E + 1
+    bad[b, 1] = R + 5
+    bad[c, 2 * E] = E + 1
+    skip_rows = np.array([ref_map[a, 0], ref_map[b, 1]] + list(ref_map[c, :n[c]]))
+    keep_rows = np.setdiff1d(np.arange(R), skip_rows)
+    ok_tok = np.setdiff1d(np.arange(T), [a, b, c])
+    rm = torch.from_numpy(bad).to(DEV)
+    xd, pd, dyd = x.to(DEV), probs.to(DEV), dy.to(DEV)
+    pn = probs.numpy()
+
+    def status(call):
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        out = call(st)
+        torch.cuda.synchronize()
+        s = int(st.item())
+        assert s & m.DEV_BAD_EXPERT and s & m.DEV_BAD_ROW, s
+        return out
+
+    def rows_ok(got, ref, what):
+        np.testing.assert_array_equal(got[keep_rows], ref[keep_rows], what)
+        assert np.all(got[skip_rows] == S_BF16), f"{what}: a faulty slot's row was written"
+
+    P = sentinel_bf16((R, H))
+    P, pp = status(lambda st: m.moe_permute_mask(xd, rm, R, pd, out=P, dev_status=st))
+    ref_P, ref_pp = oracle.mask_permute(bits(x), pn, ref_map, R)
+    rows_ok(bits(P), ref_P, "mask permute")
+    np.testing.assert_array_equal(pp.cpu().numpy()[keep_rows].view(np.uint32),
+                                  ref_pp[keep_rows].view(np.uint32))
+
+    fin = workloads.random_rows(R, H, seed=H + 2, device=DEV)
+    fv = workloads.bf16_bits(fin.cpu())
+    y = sentinel_bf16((T, H))
+    y, _ = status(lambda st: m.moe_unpermute_mask(fin, rm, pd, out=y, dev_status=st))
+    ref_y, _ = oracle.mask_unpermute(fv, pn, ref_map)
+    np.testing.assert_array_equal(bits(y)[ok_tok], ref_y[ok_tok])
+
+    dyb = bits(dy)
+    ref_din, ref_dmp = oracle.mask_unpermute_bwd(dyb, fv, pn, ref_map)
+    for want in (True, False):
+        d_in = sentinel_bf16((R, H))
+        d_in, dmp = status(lambda st: m.moe_unpermute_mask_bwd(
+            dyd, fin, pd, rm, d_in=d_in, want_probs_grad=want, dev_status=st))
+        rows_ok(bits(d_in), ref_din, f"mask bwd act grad (prob grads {want})")
+        if want:
+            got = dmp.cpu().numpy()[ok_tok]
+            sub = ref_map[ok_tok]
+            sel = np.zeros(got.shape, bool)
+            for lo in range(E):
+                used = sub[:, 2 * E] > lo
+                sel[np.nonzero(used)[0], sub[used, E + lo]] = True
+            assert np.all(got[~sel].view(np.uint32) == 0)
+            _dot_ok(got, fv, dyb[ok_tok], sub, E, ref_dmp[ok_tok])
+
+    q, sc = workloads.quantize_fp8_rows(x, 128 if H % 128 == 0 else 8)
+    qo = torch.empty((R, H), dtype=q.dtype, device=DEV)
+    qo.view(torch.uint8).fill_(0x5A)
+    so = torch.full((R, sc.shape[1]), -7.0, device=DEV)
+    status(lambda st: m.moe_permute_mask_scaled(q.to(DEV), rm, R, sc.to(DEV), out=qo,
+                                                out_scale=so, dev_status=st))
+    ref_q, ref_s, _ = oracle.mask_permute_scaled(q.view(torch.uint8).numpy(),
+                                                 sc.view(torch.uint8).numpy(), None, ref_map, R)
+    got_q = qo.view(torch.uint8).cpu().numpy()
+    np.testing.assert_array_equal(got_q[keep_rows], ref_q[keep_rows])
+    assert np.all(got_q[skip_rows] == 0x5A)
+    got_s = so.view(torch.uint8).cpu().numpy()
+    np.testing.assert_array_equal(got_s[keep_rows], ref_s[keep_rows])
+    assert np.all(so.cpu().numpy()[skip_rows] == -7.0)
+
+
 def test_mask_bad_map_sets_status(m):
     say("mask bad map entries")
     T, H, E = 8, 16, 4

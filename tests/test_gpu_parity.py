@@ -247,6 +247,113 @@ def test_row_map_bad_routing_sets_status(m):
     assert int(st.item()) & m.DEV_BAD_EXPERT
 
 
+@pytest.mark.parametrize("T,H,E,k", [(50, 136, 16, 4), (4096, 4096, 64, 8)])
+def test_bad_routing_row_ops(m, T, H, E, k):
+    """Routing faults only the device sees -- an expert index out of range,
+    and map entries past the rows or -1 for a routed token -- in every top-k
+    row op.  Each op reports both status bits, leaves the faulty slots'
+    rows unwritten, and matches the oracle (run on the sound routing) on
+    every other slot and on every token the faults do not touch.  The second
+    size takes the streaming paths (the two-launch backward included)."""
+    say(f"bad routing row ops T={T} H={H} E={E} k={k}")
+    w = workloads.random_routed(T, H, E, k, seed=T + H)
+    idx_np = w.topk_idx.numpy()
+    ref_map, _ = oracle.row_id_map(idx_np, E)
+    n = T * k
+    r_all = oracle_rows(idx_np, ref_map)
+    a, b, c = 3, T // 2, T - 2
+    bad_idx = idx_np.copy()
+    bad_idx[a, 1] = E + 3
+    bad_map = ref_map.copy()
+    bad_map[idx_np[b, 2], b] = n + 11
+    bad_map[idx_np[c, 0], c] = -1
+    skipped = [(a, 1), (b, 2), (c, 0)]
+    skip_rows = np.array([r_all[t, j] for t, j in skipped])
+    keep_rows = np.setdiff1d(np.arange(n), skip_rows)
+    ok_tok = np.setdiff1d(np.arange(T), [a, b, c])
+    x, _, probs, dy = to_dev(w)
+    idx = torch.from_numpy(bad_idx).to(DEV)
+    rm = torch.from_numpy(bad_map).to(DEV)
+    xb, pb = workloads.bf16_bits(w.x), w.probs.numpy()
+
+    def status(call):
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        call(st)
+        torch.cuda.synchronize()
+        s = int(st.item())
+        assert s & m.DEV_BAD_EXPERT and s & m.DEV_BAD_ROW, s
+
+    def rows_ok(got, ref, what):
+        assert_bits_equal(got[keep_rows], ref[keep_rows], what)
+        assert np.all(got[skip_rows] == S_BF16), f"{what}: a faulty slot's row was written"
+
+    # permute (+probs)
+    out, out_p = sentinel_bf16((n, H)), sentinel_f32((n,))
+    status(lambda st: m.moe_permute(x, idx, rm, probs, out=out, out_probs=out_p, dev_status=st))
+    o, op = oracle.permute(xb, pb, idx_np, ref_map)
+    rows_ok(bits(out), o, "permute")
+    assert_bits_equal(out_p.cpu().numpy()[keep_rows], op[keep_rows], "permuted probs")
+    assert np.all(f32_bits(out_p.cpu().numpy()[skip_rows]) == f32_bits(np.array([S_F32])))
+
+    # weighted unpermute, and the EP combine
+    P = workloads.random_rows(n, H, seed=H + 1, device=DEV)
+    Pb = bits(P)
+    y = sentinel_bf16((T, H))
+    status(lambda st: m.moe_unpermute(P, idx, rm, probs, out=y, dev_status=st))
+    ref = oracle.unpermute(Pb, pb, idx_np, ref_map)
+    assert_bits_equal(bits(y)[ok_tok], ref[ok_tok], "unpermute")
+    y = sentinel_bf16((T, H))
+    status(lambda st: m.moe_unpermute_ep(P, idx, rm, 4, probs, out=y, dev_status=st))
+    ref = oracle.unpermute_ep(Pb, pb, idx_np, ref_map, 4)
+    assert_bits_equal(bits(y)[ok_tok], ref[ok_tok], "unpermute_ep")
+
+    # unpermute backward, with and without prob gradients
+    d_in, d_p = sentinel_bf16((n, H)), sentinel_f32((T, k))
+    status(lambda st: m.moe_unpermute_bwd(dy, idx, rm, probs, P, d_in=d_in, d_probs=d_p,
+                                          dev_status=st))
+    dyb = workloads.bf16_bits(w.dy)
+    ref_in, ref_p = oracle.unpermute_bwd(dyb, Pb, pb, idx_np, ref_map)
+    rows_ok(bits(d_in), ref_in, "unpermute_bwd act grad")
+    got_p = d_p.cpu().numpy().copy()
+    for t, j in skipped:
+        got_p[t, j] = ref_p[t, j]
+    dprob_ok(got_p, Pb[r_all.reshape(-1)].reshape(T, k, H), dyb, ref_p)
+    d_in = sentinel_bf16((n, H))
+    status(lambda st: m.moe_unpermute_bwd(dy, idx, rm, probs, P, probs_grad=False, d_in=d_in,
+                                          dev_status=st))
+    rows_ok(bits(d_in), ref_in, "unpermute_bwd act grad without prob grads")
+
+    # permute backward
+    dpp = torch.randn(n, generator=torch.Generator().manual_seed(H)).to(DEV)
+    d_x, d_p = sentinel_bf16((T, H)), sentinel_f32((T, k))
+    status(lambda st: m.moe_permute_bwd(P, idx, rm, dpp, d_x=d_x, d_probs=d_p, dev_status=st))
+    ref_x, ref_pp = oracle.permute_bwd(Pb, dpp.cpu().numpy(), idx_np, ref_map)
+    assert_bits_equal(bits(d_x)[ok_tok], ref_x[ok_tok], "permute_bwd")
+    keep = np.ones((T, k), bool)
+    for t, j in skipped:
+        keep[t, j] = False
+    assert_bits_equal(d_p.cpu().numpy()[keep], ref_pp[keep], "permute_bwd probs")
+
+    # FP8 rows with their scales
+    q, sc = workloads.quantize_fp8_rows(w.x, 128 if H % 128 == 0 else 8)
+    qo = torch.empty((n, H), dtype=q.dtype, device=DEV)
+    qo.view(torch.uint8).fill_(0x5A)
+    so = torch.full((n, sc.shape[1]), -7.0, device=DEV)
+    status(lambda st: m.moe_permute_scaled(q.to(DEV), idx, rm, sc.to(DEV), out=qo, out_scale=so,
+                                           dev_status=st))
+    src = r_all.reshape(-1).astype(np.int64)
+    tok = np.repeat(np.arange(T), k)
+    keep_flat = np.isin(src, keep_rows)
+    qb = q.view(torch.uint8).numpy()
+    got = qo.view(torch.uint8).cpu().numpy()
+    np.testing.assert_array_equal(got[src[keep_flat]], qb[tok[keep_flat]])
+    assert np.all(got[skip_rows] == 0x5A)
+    got_s = so.cpu().numpy()
+    np.testing.assert_array_equal(got_s[src[keep_flat]].view(np.uint32),
+                                  sc.numpy()[tok[keep_flat]].view(np.uint32))
+    assert np.all(got_s[skip_rows] == -7.0)
+
+
 # --------------------------------------------- (2) permute, (4) unpermute --
 
 @pytest.mark.parametrize("name", ["tiny", "finegrain", "skewed"])
