@@ -726,6 +726,88 @@ def test_graph_replay_routing(m):
         assert_bits_equal(bits(y), ref_y, f"replay {rep} unpermute")
 
 
+def test_graph_replay_streaming_path(m):
+    """The whole routed path at a size where every op streams (the two-launch
+    backward included), captured once and replayed with three routings.
+    Each replay equals an eager run of the same path bit for bit, prob
+    gradients included, and the oracle (prob gradients within their bound)."""
+    T, H, E, k = 4096, 4096, 64, 8
+    n = T * k
+    say(f"graph replay, streaming path T={T} H={H} E={E} k={k}")
+
+    def buf(shape, dt):
+        return torch.empty(shape, dtype=dt, device=DEV)
+
+    idx_s, probs_s = buf((T, k), torch.int32), buf((T, k), torch.float32)
+    x_s, dy_s = buf((T, H), torch.bfloat16), buf((T, H), torch.bfloat16)
+    rm, off = buf((E, T), torch.int32), buf((E + 1,), torch.int32)
+    ws = buf((m.moe_make_row_id_map_workspace_bytes(T, k, E),), torch.uint8)
+
+    def outs():
+        return dict(P=buf((n, H), torch.bfloat16), pp=buf((n,), torch.float32),
+                    y=buf((T, H), torch.bfloat16), d_in=buf((n, H), torch.bfloat16),
+                    d_p=buf((T, k), torch.float32), d_x=buf((T, H), torch.bfloat16),
+                    d_pp=buf((T, k), torch.float32))
+
+    def step(o):
+        m.moe_make_row_id_map(idx_s, E, row_id_map=rm, expert_offsets=off, workspace=ws)
+        m.moe_permute(x_s, idx_s, rm, probs_s, out=o["P"], out_probs=o["pp"])
+        m.moe_unpermute(o["P"], idx_s, rm, probs_s, out=o["y"])
+        m.moe_unpermute_bwd(dy_s, idx_s, rm, probs_s, o["P"], d_in=o["d_in"], d_probs=o["d_p"])
+        m.moe_permute_bwd(o["d_in"], idx_s, rm, o["pp"], d_x=o["d_x"], d_probs=o["d_pp"])
+
+    def load(w):
+        idx_s.copy_(w.topk_idx)
+        probs_s.copy_(w.probs)
+        x_s.copy_(w.x)
+        dy_s.copy_(w.dy)
+
+    def host(o):
+        return {key: (bits(t) if t.dtype == torch.bfloat16 else f32_bits(t.cpu().numpy()))
+                for key, t in o.items()}
+
+    g_out, e_out = outs(), outs()
+    load(workloads.random_routed(T, H, E, k, seed=2000))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(g_out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(g_out)
+    for rep in range(3):
+        w = workloads.random_routed(T, H, E, k, seed=2001 + rep, zipf_s=0.6 * rep)
+        load(w)
+        for t in g_out.values():
+            t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).fill_(-3)
+        g.replay()
+        torch.cuda.synchronize()
+        got, rm_g, off_g = host(g_out), rm.cpu().numpy(), off.cpu().numpy()
+        step(e_out)
+        torch.cuda.synchronize()
+        eager = host(e_out)
+        for key in got:
+            assert_bits_equal(got[key], eager[key], f"replay {rep} {key} against eager")
+        idx_np, p_np = w.topk_idx.numpy(), w.probs.numpy()
+        ref_map, ref_off = oracle.row_id_map(idx_np, E)
+        assert_bits_equal(rm_g, ref_map, f"replay {rep} row map")
+        assert_bits_equal(off_g, ref_off, f"replay {rep} offsets")
+        o, op = oracle.permute(workloads.bf16_bits(w.x), p_np, idx_np, ref_map)
+        assert_bits_equal(got["P"], o, f"replay {rep} permute")
+        assert_bits_equal(got["pp"], f32_bits(op), f"replay {rep} permuted probs")
+        assert_bits_equal(got["y"], oracle.unpermute(o, p_np, idx_np, ref_map),
+                          f"replay {rep} unpermute")
+        dyb = workloads.bf16_bits(w.dy)
+        ref_in, ref_p = oracle.unpermute_bwd(dyb, o, p_np, idx_np, ref_map)
+        assert_bits_equal(got["d_in"], ref_in, f"replay {rep} unpermute_bwd act grad")
+        r_all = oracle_rows(idx_np, ref_map).reshape(-1)
+        dprob_ok(got["d_p"].view(np.float32), o[r_all].reshape(T, k, H), dyb, ref_p)
+        ref_x, ref_pp = oracle.permute_bwd(ref_in, op, idx_np, ref_map)
+        assert_bits_equal(got["d_x"], ref_x, f"replay {rep} permute_bwd")
+        assert_bits_equal(got["d_pp"], f32_bits(ref_pp), f"replay {rep} permute_bwd probs")
+
+
 # ------------------------------------------------ (3) chunk sort / restore --
 
 def _chunk_ref(cw, sizes=None):
