@@ -105,7 +105,11 @@ __global__ __launch_bounds__(kRowThreads) void mask_permute_kernel(
       const int64_t r = mask_slot(mrow, E, n_rows, j0 + threadIdx.x, &e, &bad);
       int z = 0;
       if (probs != nullptr && r >= 0) {
-        const float p = probs[(int64_t)t * E + e];
+        // A streaming call reads the probs past the caches: at 16384 tokens
+        // x 256 experts the [T][E] probs (16.8 MB, one line per slot) would
+        // otherwise push part of the token rows out of the Infinity Cache
+        // between back-to-back calls (357 us warm against 361-363).
+        const float p = ld_row<NTM != 0>(probs + (int64_t)t * E + e);
         z = p == 0.0f;
         if (blockIdx.y == 0 && out_probs != nullptr) out_probs[r] = p;
       }
@@ -489,7 +493,7 @@ __global__ __launch_bounds__(kRowThreads) void mask_scale_scatter_kernel(
       int e;
       const int64_t r = mask_slot(mrow, E, n_rows, j0 + threadIdx.x, &e, &bad);
       srow[threadIdx.x] = r;
-      sp[threadIdx.x] = r >= 0 ? merging_probs[(int64_t)t * E + e] : 0.0f;
+      sp[threadIdx.x] = r >= 0 ? ld_row<NTM != 0>(merging_probs + (int64_t)t * E + e) : 0.0f;
     }
     __syncthreads();
     for (int j = 0; j < nj; j++) {
@@ -609,8 +613,13 @@ __global__ __launch_bounds__(MAXT) void mask_dot_gather_kernel(
       __syncthreads();
     }
   }
+  // A streaming call stores the prob-gradient row past the caches: left
+  // there (16.8 MB at 16384 tokens x 256 experts) it pushed part of d_out,
+  // which the scatter launched next reads, out of the Infinity Cache (the
+  // backward took 688-690 us warm and 697 cold, 664-666 and 686-689 with
+  // these stores and the scatter's prob reads streamed).
   for (int e = threadIdx.x; e < E; e += blockDim.x)
-    d_merging_probs[(int64_t)t * E + e] = sdp[e];
+    st_row<NTM != 0>(sdp[e], d_merging_probs + (int64_t)t * E + e);
   report(dev_status, bad);
 }
 
