@@ -883,14 +883,15 @@ hipError_t launch_combine_bwd(const void *d_out, const void *fwd_in, const float
     }
   }
   if (vec && bytes > kStreamBytes)
-    combine_bwd_dispatch<8, MOE_COMBINE_BWD_STREAM>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
-                                  n_rows, d_in, d_probs, dev_status, s);
+    combine_bwd_dispatch<8, MOE_COMBINE_BWD_STREAM>(d_out, fwd_in, probs, topk_idx, row_id_map,
+                                                    T, H / 8, k, E, n_rows, d_in, d_probs,
+                                                    dev_status, s);
   else if (vec)
     combine_bwd_dispatch<8, 0>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H / 8, k, E,
-                                   n_rows, d_in, d_probs, dev_status, s);
+                               n_rows, d_in, d_probs, dev_status, s);
   else
-    combine_bwd_dispatch<1, 0>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H, k, E,
-                                   n_rows, d_in, d_probs, dev_status, s);
+    combine_bwd_dispatch<1, 0>(d_out, fwd_in, probs, topk_idx, row_id_map, T, H, k, E, n_rows,
+                               d_in, d_probs, dev_status, s);
   return hipGetLastError();
 }
 
