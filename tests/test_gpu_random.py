@@ -102,6 +102,21 @@ def test_random_routed_chain(m, T, H, E, k, zipf, ep, seed):
     assert int(st.item()) == 0
 
 
+# Calls past the 256 MiB streaming threshold (non-temporal rows, the permute's
+# prefetch, the two-launch backward), with hidden sizes that are not powers of
+# two and rows longer than one workgroup pass.
+STREAMING = [(2048, 8200, 64, 8, 0.0, 4, 6000), (1024, 7168, 256, 16, 1.1, 8, 6001),
+             (4096, 4096, 32, 8, 0.0, 32, 6002), (3000, 5120, 100, 6, 1.1, 4, 6003),
+             (1500, 12288, 16, 8, 0.0, 2, 6004), (2048, 7168, 512, 12, 1.1, 16, 6005),
+             (640, 20488, 24, 8, 0.0, 3, 6006)]
+
+
+@pytest.mark.parametrize("T,H,E,k,zipf,ep,seed", STREAMING)
+def test_random_routed_chain_streaming(m, T, H, E, k, zipf, ep, seed):
+    assert 2 * H * (2 * T * k + T) > 256 << 20
+    test_random_routed_chain(m, T, H, E, k, zipf, ep, seed)
+
+
 @pytest.mark.parametrize("N,H,ranks,experts,align,empty,extra,fp32,half_probs,seed",
                          _chunk_cases())
 def test_random_chunk_chain(m, N, H, ranks, experts, align, empty, extra, fp32, half_probs,
