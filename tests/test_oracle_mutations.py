@@ -146,6 +146,9 @@ MUTATIONS = [
     ("restore_stale_entry_unreported",
      "if (s >= n_act) { status = ORC_BAD_ROW; continue; }",
      "if (s >= n_act) continue;"),
+    ("bf16_widening_drops_sign",
+     "uint32_t u = ((uint32_t)b) << 16;",
+     "uint32_t u = ((uint32_t)(b & 0x7FFFu)) << 16;"),
 ]
 
 _RUNNER = (

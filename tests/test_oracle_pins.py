@@ -231,6 +231,20 @@ def test_bf16_rounding_matches_torch_cast():
         assert (b & 0x7F80) == 0x7F80 and (b & 0x0040) and (b >> 15) == (pattern >> 31)
 
 
+def test_bf16_widening_matches_torch_for_every_pattern():
+    """The oracle's bf16 -> fp32 widening, the input side of every combine and
+    dot product, against torch's bf16 -> float32 conversion for all 2^16 bit
+    patterns: equal bits for numbers, signed zeros, subnormals and infinities;
+    NaN stays NaN with its sign (payloads pass through a Python float here)."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(pats.view(np.int16)).view(torch.bfloat16).float().numpy()
+    got = np.array([oracle.bf16_to_f32(int(b)) for b in pats], np.float32)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127 and np.array_equal(np.isnan(got), nan)   # 7-bit payloads, two signs
+    np.testing.assert_array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    np.testing.assert_array_equal(np.signbit(got[nan]), np.signbit(ref[nan]))
+
+
 def test_unpermute_k1_is_single_rounded_product():
     """k = 1: out = bf16(RN32(p * x)); torch's fp32 multiply and bf16 cast."""
     w = _routed(64, 40, 8, 1, seed=3)
