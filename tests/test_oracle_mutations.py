@@ -146,6 +146,14 @@ MUTATIONS = [
     ("restore_stale_entry_unreported",
      "if (s >= n_act) { status = ORC_BAD_ROW; continue; }",
      "if (s >= n_act) continue;"),
+    ("permute_rows_of_reversed_tokens",
+     "for (int h = 0; h < H; h++) out[r * H + h] = x[(int64_t)t * H + h];",
+     "for (int h = 0; h < H; h++) out[r * H + h] = x[(int64_t)(T - 1 - t) * H + h];"),
+    ("permute_probs_of_first_slot",
+     "            for (int h = 0; h < H; h++) out[r * H + h] = x[(int64_t)t * H + h];\n"
+     "            if (probs && out_probs) out_probs[r] = probs[(int64_t)t * k + j];",
+     "            for (int h = 0; h < H; h++) out[r * H + h] = x[(int64_t)t * H + h];\n"
+     "            if (probs && out_probs) out_probs[r] = probs[(int64_t)t * k];"),
     ("bf16_widening_drops_sign",
      "uint32_t u = ((uint32_t)b) << 16;",
      "uint32_t u = ((uint32_t)(b & 0x7FFFu)) << 16;"),
