@@ -154,6 +154,18 @@ MUTATIONS = [
      "            if (probs && out_probs) out_probs[r] = probs[(int64_t)t * k + j];",
      "            for (int h = 0; h < H; h++) out[r * H + h] = x[(int64_t)t * H + h];\n"
      "            if (probs && out_probs) out_probs[r] = probs[(int64_t)t * k];"),
+    ("permute_bwd_slots_reversed",
+     "                int64_t r = dest_row(topk_idx, row_id_map, T, k, t, j);\n"
+     "                acc = acc + bf16_to_f32(d_out[r * H + h]);",
+     "                int64_t r = dest_row(topk_idx, row_id_map, T, k, t, k - 1 - j);\n"
+     "                acc = acc + bf16_to_f32(d_out[r * H + h]);"),
+    ("router_softmax_without_max",
+     "        for (int j = 0; j < k; j++) sum += exp(lv[j] - lv[0]);\n"
+     "        for (int j = 0; j < k; j++) {\n"
+     "            double w = exp(lv[j] - lv[0]) / sum;",
+     "        for (int j = 0; j < k; j++) sum += exp(lv[j]);\n"
+     "        for (int j = 0; j < k; j++) {\n"
+     "            double w = exp(lv[j]) / sum;"),
     ("bf16_widening_drops_sign",
      "uint32_t u = ((uint32_t)b) << 16;",
      "uint32_t u = ((uint32_t)(b & 0x7FFFu)) << 16;"),

@@ -358,6 +358,16 @@ def test_permute_bwd_slot_order_sum():
     dP_copy, _ = oracle.permute(_bits(w.dy), None, idx, m)
     dx2, _ = oracle.permute_bwd(dP_copy, None, idx, m)
     np.testing.assert_array_equal(dx2, _bits((w.dy.float() * k).to(torch.bfloat16)))
+    # crafted: slots (in column order, not expert order) carry 2^24, 1, -2^24.
+    # In slot order the fp32 sum is (2^24 + 1 -> 2^24, ties to even) - 2^24 = 0;
+    # summed backwards or by expert it is 1.
+    idx3 = np.array([[2, 0, 1]], np.int32)
+    m3, _ = oracle.row_id_map(idx3, 3)
+    d3 = np.zeros((3, 1), np.uint16)
+    for j, v in enumerate((0x4B80, 0x3F80, 0xCB80)):
+        d3[m3[idx3[0, j], 0], 0] = v
+    dx3, _ = oracle.permute_bwd(d3, None, idx3, m3)
+    assert int(dx3[0, 0]) == 0x0000
 
 
 # ------------------------------------- (3) chunk sort-and-pad / restore ----
@@ -790,6 +800,10 @@ def test_topk_softmax_bf16_weights_round_to_nearest():
     ([1.0, 1.0, -3.0], 2, [0x3F00, 0x3F00]),                 # tie: 1/2 each
     ([0.0, 0.0, 0.0, 0.0, -1.0], 4, [0x3E80] * 4),           # four equal: 1/4
     ([0.0, float(np.log(3.0)), -5.0], 2, [0x3F40, 0x3E80]),  # 3/4 and 1/4
+    # exp of the logits themselves would overflow (first) or underflow (second):
+    # only the differences from the largest give these weights
+    ([1000.0, 1000.0, -3.0], 2, [0x3F00, 0x3F00]),
+    ([-1000.0, -1000.0 + float(np.log(3.0)), -2000.0], 2, [0x3F40, 0x3E80]),
 ])
 def test_topk_softmax_bf16_closed_forms(logits, k, expect):
     _, w = oracle.topk_softmax(np.array([logits], np.float32), k, prob_bytes=2)
