@@ -166,6 +166,22 @@ MUTATIONS = [
      "        for (int j = 0; j < k; j++) sum += exp(lv[j]);\n"
      "        for (int j = 0; j < k; j++) {\n"
      "            double w = exp(lv[j]) / sum;"),
+    ("ep_ranks_interleaved",
+     "if (topk_idx[(int64_t)t * k + j] / per_rank != rank) continue;",
+     "if (topk_idx[(int64_t)t * k + j] % ep_size != rank) continue;"),
+    ("prob_grad_dot_on_slot_index_row",
+     "double a = (double)bf16_to_f32(fwd_in[r * H + h]);",
+     "double a = (double)bf16_to_f32(fwd_in[((int64_t)t * k + j) * H + h]);"),
+    ("prob_grad_dot_in_fp32",
+     "                        dot += a * b;\n"
+     "                    }\n"
+     "                    d_probs[(int64_t)t * k + j] = (float)dot;",
+     "                        dot = (float)(dot + (float)(a * b));\n"
+     "                    }\n"
+     "                    d_probs[(int64_t)t * k + j] = (float)dot;"),
+    ("mask_prob_grad_dot_in_fp32",
+     "dot += (double)bf16_to_f32(fwd_in[(int64_t)row * H + h]) * (double)g;",
+     "dot = (float)(dot + (float)((double)bf16_to_f32(fwd_in[(int64_t)row * H + h]) * (double)g));"),
     ("bf16_widening_drops_sign",
      "uint32_t u = ((uint32_t)b) << 16;",
      "uint32_t u = ((uint32_t)(b & 0x7FFFu)) << 16;"),

@@ -327,7 +327,17 @@ def test_unpermute_bwd_act_grad_and_prob_grad():
     g = _bf16_to_f32(dy).astype(np.float64)
     ref = np.einsum("tjh,th->tj", fi[rows], g)
     scale = np.einsum("tjh,th->tj", np.abs(fi[rows]), np.abs(g))
-    assert np.all(np.abs(d_p.astype(np.float64) - ref) <= 1e-6 * scale + 1e-30)
+    # an fp64 sum rounded once to fp32: within half an fp32 ulp of the numpy
+    # value, up to the fp64 rounding of either sum (far below 1e-12 of S)
+    assert np.all(np.abs(d_p.astype(np.float64) - ref) <= 2.0 ** -24 * np.abs(ref) + 1e-12 * scale)
+    # crafted: the row (2^24, 1, -2^24) against (1, 1, 1) dots to exactly 1; a
+    # sum kept in fp32 gives 0 (2^24 + 1 rounds back to 2^24)
+    idx1 = np.array([[0]], np.int32)
+    m1, _ = oracle.row_id_map(idx1, 1)
+    _, p1 = oracle.unpermute_bwd(np.array([[0x3F80] * 3], np.uint16),
+                                 np.array([[0x4B80, 0x3F80, 0xCB80]], np.uint16),
+                                 np.ones((1, 1), np.float32), idx1, m1)
+    assert float(p1[0, 0]) == 1.0
     # without probs the scatter is a bitwise copy
     d_in0, d_p0 = oracle.unpermute_bwd(dy, None, None, idx, m)
     exp0 = np.empty_like(exp)
